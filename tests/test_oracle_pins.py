@@ -1,0 +1,416 @@
+"""Pins of the CPU oracle against facts fixed outside it.
+
+Each test compares the oracle with something it does not contain: torch's own
+float8/bfloat16 casts, closed forms of the OCP formats, hand-worked fixtures
+under tests/golden/, numpy float64 matmuls, invariants of the gather, and the
+naive dense-masked algorithm the gather replaced.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_block_scaled_topk_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------
+# formats
+# ----------------------------------------------------------------------------
+
+def test_e4m3_all_bytes_match_torch(oracle_lib):
+    """PIN: all 256 E4M3FN bytes decode as torch.float8_e4m3fn does."""
+    b = torch.arange(256, dtype=torch.uint8)
+    ref = b.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.e4m3(i) for i in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert nan.sum() == 2  # 0x7F and 0xFF
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def _e2m1_from_bits(code):
+    """E2M1 from its bit fields: sign | 2-bit exponent (bias 1) | 1-bit mantissa."""
+    s = (code >> 3) & 1
+    e = (code >> 1) & 3
+    m = code & 1
+    mag = (m / 2.0) * 2.0 ** (1 - 1) if e == 0 else (1 + m / 2.0) * 2.0 ** (e - 1)
+    return -mag if s else mag
+
+
+def test_e2m1_table_matches_bit_fields(oracle_lib):
+    """PIN: the oracle's e2m1 table equals the E2M1 bit-field definition, the
+    magnitudes of codes 0..7 rise strictly, max is 6 and code 8 is -0."""
+    got = [oracle.e2m1(c) for c in range(16)]
+    assert got == [_e2m1_from_bits(c) for c in range(16)]
+    mags = got[:8]
+    assert all(a < b for a, b in zip(mags, mags[1:]))
+    assert mags[-1] == 6.0
+    assert got[8] == 0.0 and np.signbit(got[8])
+
+
+def test_every_e2m1_times_e4m3_is_exact_in_bf16(oracle_lib):
+    """PIN (gllm #91, "bf16 NVFP4 GEMM (CUDA)"): an e2m1 code times an e4m3 block
+    scale has at most 6 significant bits, so it is exact in bf16.  Checked over
+    all 16 x 254 finite products with torch's own float64 -> bfloat16 cast."""
+    prods = []
+    for c in range(16):
+        for s in range(256):
+            sv = oracle.e4m3(s)
+            if np.isnan(sv):
+                continue
+            prods.append(oracle.e2m1(c) * sv)
+    p = np.array(prods)
+    assert p.size == 16 * 254
+    rt = torch.from_numpy(p).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(rt, p)
+    nz = p[p != 0]
+    mant, _ = np.frexp(np.abs(nz))
+    sig = mant * 2.0 ** 6
+    assert np.all(sig == np.round(sig))  # at most 6 significant bits
+
+
+def test_round_bf16_matches_torch(oracle_lib):
+    """PIN: the oracle's round-to-bf16 equals torch's float32 -> bfloat16 cast on
+    float32-representable values, including exact ties."""
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal(2000).astype(np.float32) * np.float32(30)
+    bits = v.view(np.uint32)
+    ties = ((bits & 0xFFFF0000) | 0x8000).view(np.float32)   # halfway cases
+    vals = np.concatenate([v, ties, np.float32([0, -0.0, 1e-30, 3e38])])
+    ref = torch.from_numpy(vals).to(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.round_bf16(float(x)) for x in vals])
+    assert np.array_equal(got, ref)
+
+
+def _read_golden(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as fh:
+        lines = [ln.strip() for ln in fh if ln.strip() and not ln.startswith("#")]
+    return lines
+
+
+def test_dequant_hand_fixture(oracle_lib):
+    """PIN: hand-encoded NVFP4 rows (tests/golden/nvfp4_hand.txt)."""
+    lines = _read_golden("nvfp4_hand.txt")
+    g = float(lines[0].split()[1])
+    codes = np.zeros((2, 16), dtype=np.uint8)
+    scales = np.zeros((2, 2), dtype=np.uint8)
+    values = np.zeros((2, 32))
+    for ln in lines[1:]:
+        tok = ln.split()
+        r = int(tok[1])
+        if tok[0] == "codes":
+            codes[r] = [int(t, 16) for t in tok[2:]]
+        elif tok[0] == "scales":
+            scales[r] = [int(t, 16) for t in tok[2:]]
+        elif tok[0] == "values":
+            values[r] = [float(t) for t in tok[2:]]
+    got = oracle.dequant(codes, scales, g)
+    assert np.array_equal(got, values)
+    # negative zeros are where the fixture says
+    assert np.array_equal(np.signbit(got), np.signbit(values))
+    # dropping the global halves every value (global = 0.5)
+    assert np.array_equal(oracle.dequant(codes, scales, g, with_global=False), values / g)
+
+
+def test_dequant_matches_torch_decoders_and_nibble_order(oracle_lib):
+    """PIN: random bytes decoded by the oracle equal a decode written from torch's
+    float8_e4m3fn cast, the E2M1 bit fields and the low-nibble-first order."""
+    t = synth.random_bytes_nvfp4(11, 1, 24, 96)
+    c, s, g = t.codes[0], t.scales[0], float(t.globals_[0])
+    lo = (c & 15).astype(np.int64)
+    hi = (c >> 4).astype(np.int64)
+    code = np.empty((24, 96), dtype=np.int64)
+    code[:, 0::2] = lo
+    code[:, 1::2] = hi
+    e2 = np.vectorize(_e2m1_from_bits)(code).astype(np.float64)
+    sc = torch.from_numpy(s.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ref = np.float64(np.float32(g)) * np.repeat(sc, 16, axis=1) * e2
+    got = oracle.dequant(c, s, g)
+    assert np.array_equal(got, ref)
+
+
+def test_quantized_weights_decode_close_to_source(oracle_lib):
+    """PIN: weights encoded by the input generator and decoded by the oracle stay
+    within the format's rounding bound of the float32 source: per element, half
+    the local e2m1 gap times the block's scale and global (plus the scale's own
+    rounding, absorbed by a 2x margin).  A wrong nibble order, a transposed scale
+    or a dropped global breaks it by orders of magnitude."""
+    rng = np.random.default_rng(3)
+    w = rng.standard_normal((40, 128), dtype=np.float32) * np.float32(0.02)
+    codes, scales, g = synth.quantize_nvfp4(w)
+    deq = oracle.dequant(codes, scales, float(g))
+    block_scale = np.repeat(np.array([[oracle.e4m3(b) for b in row] for row in scales]), 16, axis=1)
+    step = block_scale * float(g)  # value of e2m1 1.0 in this block
+    err = np.abs(deq - w.astype(np.float64))
+    # the largest e2m1 gap is 2 (between 4 and 6): |err| <= 1 * step at worst
+    assert np.all(err <= 1.0 * step + 1e-12)
+    rel = np.linalg.norm(deq - w) / np.linalg.norm(w)
+    assert rel < 0.12
+
+
+# ----------------------------------------------------------------------------
+# WeightedRowSum
+# ----------------------------------------------------------------------------
+
+def _golden_wrs():
+    lines = _read_golden("weighted_row_sum_hand.txt")
+    data = {}
+    i = 0
+    while i < len(lines):
+        name, r, c = lines[i].split()
+        r, c = int(r), int(c)
+        data[name] = np.array([[float(v) for v in lines[i + 1 + k].split()] for k in range(r)])
+        i += 1 + r
+    return data
+
+
+def test_weighted_row_sum_hand_values(oracle_lib):
+    """PIN (gllm #91, "What changes" / "Testing"): hand-computed WeightedRowSum with
+    repeated source rows and a pre-filled dst."""
+    g = _golden_wrs()
+    out = oracle.weighted_row_sum(g["dst"], g["src"], g["rows"].astype(np.int32), g["weights"])
+    assert np.array_equal(out, g["expected"])
+
+
+def test_weighted_row_sum_special_cases(oracle_lib):
+    """PIN: K = 1 with w = 1 is a row add; w = 0 leaves dst unchanged; an
+    out-of-range row is rejected (bounds are checked)."""
+    rng = np.random.default_rng(5)
+    src = rng.standard_normal((7, 5))
+    dst = rng.standard_normal((4, 5))
+    rows = np.array([[3], [0], [6], [3]], dtype=np.int32)
+    out = oracle.weighted_row_sum(dst, src, rows, np.ones((4, 1)))
+    assert np.array_equal(out, dst + src[[3, 0, 6, 3]])
+    rows2 = rng.integers(0, 7, size=(4, 3)).astype(np.int32)
+    assert np.array_equal(oracle.weighted_row_sum(dst, src, rows2, np.zeros((4, 3))), dst)
+    with pytest.raises(oracle.OracleError):
+        oracle.weighted_row_sum(dst, src, np.array([[7], [0], [0], [0]], dtype=np.int32), np.ones((4, 1)))
+    with pytest.raises(oracle.OracleError):
+        oracle.weighted_row_sum(dst, src, np.array([[-1], [0], [0], [0]], dtype=np.int32), np.ones((4, 1)))
+
+
+# ----------------------------------------------------------------------------
+# routing
+# ----------------------------------------------------------------------------
+
+def test_route_matches_torch_topk_softmax(oracle_lib):
+    """PIN: on tie-free logits, ids equal torch.topk (descending) and the weights
+    equal torch.softmax of the picked logits in float64."""
+    for name in ("tiny16", "decode32_zipf", "gated2"):
+        cfg = synth.WORKLOADS[name]
+        logits = synth.draw_logits(name)
+        ids, w = oracle.route_topk(logits, cfg["K"])
+        tl = torch.from_numpy(logits)
+        vals, idx = torch.topk(tl, cfg["K"], dim=1, largest=True, sorted=True)
+        assert np.array_equal(ids, idx.numpy().astype(np.int32))
+        ref = torch.softmax(vals.to(torch.float64), dim=1).numpy()
+        assert np.max(np.abs(w - ref)) < 1e-15
+        assert np.max(np.abs(w.sum(1) - 1)) < 1e-15
+
+
+def test_route_full_softmax_and_ties(oracle_lib):
+    """PIN: K = E is a full softmax in descending order; all-equal logits pick
+    experts 0..K-1 with weight 1/K (ties go to the lower index)."""
+    rng = np.random.default_rng(9)
+    logits = rng.standard_normal((5, 6)).astype(np.float32)
+    ids, w = oracle.route_topk(logits, 6)
+    order = np.argsort(-logits.astype(np.float64), axis=1, kind="stable")
+    assert np.array_equal(ids, order.astype(np.int32))
+    full = torch.softmax(torch.from_numpy(logits).to(torch.float64), 1).numpy()
+    assert np.max(np.abs(np.take_along_axis(full, order, 1) - w)) < 1e-15
+    eq = np.zeros((3, 10), dtype=np.float32)
+    ids, w = oracle.route_topk(eq, 4)
+    assert np.array_equal(ids, np.tile(np.arange(4, dtype=np.int32), (3, 1)))
+    assert np.array_equal(w, np.full((3, 4), 0.25))
+    # partial ties: the tied pair keeps index order
+    lg = np.array([[0.5, 2.0, 0.5, 2.0, -1.0]], dtype=np.float32)
+    ids, _ = oracle.route_topk(lg, 4)
+    assert ids.tolist() == [[1, 3, 0, 2]]
+
+
+# ----------------------------------------------------------------------------
+# gather
+# ----------------------------------------------------------------------------
+
+def _check_gather_invariants(ids, E, offsets, row_token, rows):
+    n, K = ids.shape
+    R = n * K
+    assert offsets[0] == 0 and offsets[E] == R
+    assert np.array_equal(np.diff(offsets), np.bincount(ids.ravel(), minlength=E))
+    assert np.array_equal(np.sort(rows.ravel()), np.arange(R))
+    for t in range(n):
+        for j in range(K):
+            r = rows[t, j]
+            assert row_token[r] == t
+            assert offsets[ids[t, j]] <= r < offsets[ids[t, j] + 1]
+    for e in range(E):
+        seg = row_token[offsets[e]:offsets[e + 1]]
+        assert np.all(np.diff(seg) > 0)  # ascending tokens inside an expert
+
+
+def test_gather_invariants(oracle_lib):
+    """PIN: offsets are the exclusive scan of the expert counts, rows is a
+    permutation of 0..R-1, row_token[rows[t,j]] = t, rows of an expert are in
+    ascending token order, and xg[rows[t,j]] == x[t] bit for bit."""
+    for name in ("tiny16", "decode32_zipf", "gated2"):
+        cfg = synth.WORKLOADS[name]
+        ids, _ = oracle.route_topk(synth.draw_logits(name), cfg["K"])
+        offsets, row_token, rows = oracle.gather_layout(ids, cfg["E"])
+        _check_gather_invariants(ids, cfg["E"], offsets, row_token, rows)
+        x = synth.draw_activations(name)
+        xg = oracle.gather_copy(x, row_token)
+        for t in range(cfg["n"]):
+            for j in range(cfg["K"]):
+                assert np.array_equal(xg[rows[t, j]].view(np.uint8), x[t].view(np.uint8))
+
+
+def test_gather_prefill_row_counts(oracle_lib):
+    """PIN (gllm #91, "What the profile showed"): at 4314 tokens with 128 experts
+    and topK 6 the gather packs 4314 * 6 = 25,884 rows where the dense-masked
+    loop ran 4314 * 128 = 552,192; nearly all experts are picked."""
+    cfg = synth.WORKLOADS["prefill4314"]
+    ids, _ = oracle.route_topk(synth.draw_logits("prefill4314"), cfg["K"])
+    offsets, row_token, rows = oracle.gather_layout(ids, cfg["E"])
+    assert offsets[-1] == 25884
+    assert cfg["n"] * cfg["E"] == 552192
+    assert np.count_nonzero(np.diff(offsets)) >= 120
+    _check_gather_invariants(ids[:64], cfg["E"], *oracle.gather_layout(ids[:64], cfg["E"]))
+
+
+def test_gather_rejects_bad_expert_id(oracle_lib):
+    with pytest.raises(oracle.OracleError):
+        oracle.gather_layout(np.array([[0, 8]], dtype=np.int32), 8)
+
+
+# ----------------------------------------------------------------------------
+# expert FFN and the layer
+# ----------------------------------------------------------------------------
+
+def _np_dequant(t, e):
+    """Independent decode for the tests: torch's e4m3 cast + E2M1 bit fields."""
+    c = t.codes[e]
+    code = np.empty((c.shape[0], c.shape[1] * 2), dtype=np.int64)
+    code[:, 0::2] = c & 15
+    code[:, 1::2] = c >> 4
+    e2 = np.vectorize(_e2m1_from_bits)(code).astype(np.float64)
+    sc = torch.from_numpy(t.scales[e].copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return float(t.globals_[e]) * np.repeat(sc, 16, axis=1) * e2
+
+
+def _np_ffn(x, wu, wd, act, f):
+    u = x @ wu.T
+    if act == "swiglu":
+        a, b = u[:, :f], u[:, f:]
+        h = a / (1 + np.exp(-a)) * b
+    else:
+        h = np.maximum(u, 0) ** 2
+    return h @ wd.T
+
+
+@pytest.mark.parametrize("act", ["relu2", "swiglu"])
+def test_expert_ffn_matches_numpy_matmul(oracle_lib, act):
+    """PIN: the oracle FFN over grouped rows equals numpy float64 matmuls on
+    independently decoded weights, expert by expert (normwise 1e-13)."""
+    E, d, f, n = 5, 64, 48, 23
+    up_rows = 2 * f if act == "swiglu" else f
+    up = synth.random_nvfp4(21, E, up_rows, d)
+    dn = synth.random_nvfp4(22, E, d, f)
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((n, d))
+    counts = np.array([4, 0, 11, 1, 7])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    got = oracle.expert_ffn(x, offsets, up, dn, f, act)
+    ref = np.zeros_like(got)
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 > r0:
+            ref[r0:r1] = _np_ffn(x[r0:r1], _np_dequant(up, e), _np_dequant(dn, e), act, f)
+    assert np.max(np.abs(got - ref)) <= 1e-13 * np.max(np.abs(ref))
+
+
+def test_linear_matches_numpy(oracle_lib):
+    """PIN: one grouped NVFP4 projection equals numpy a @ W^T per expert."""
+    w = synth.random_bytes_nvfp4(31, 3, 40, 64)
+    rng = np.random.default_rng(32)
+    a = rng.standard_normal((9, 64))
+    offsets = np.array([0, 2, 2, 9], dtype=np.int32)
+    got = oracle.linear(a, offsets, w)
+    ref = np.zeros_like(got)
+    for e in range(3):
+        ref[offsets[e]:offsets[e + 1]] = a[offsets[e]:offsets[e + 1]] @ _np_dequant(w, e).T
+    assert np.max(np.abs(got - ref)) <= 1e-13 * np.max(np.abs(ref))
+
+
+def test_ffn_thread_count_invariance(oracle_lib):
+    """Each output element comes from one thread in one order: 1 vs 7 threads
+    give identical bits."""
+    up = synth.random_nvfp4(41, 3, 64, 64)
+    dn = synth.random_nvfp4(42, 3, 64, 64)
+    x = np.random.default_rng(43).standard_normal((30, 64))
+    off = np.array([0, 10, 25, 30], dtype=np.int32)
+    a = oracle.expert_ffn(x, off, up, dn, 64, "relu2", threads=1)
+    b = oracle.expert_ffn(x, off, up, dn, 64, "relu2", threads=7)
+    assert np.array_equal(a, b)
+
+
+def test_layer_equals_naive_dense_loop(oracle_lib):
+    """PIN (gllm #91, "What the profile showed" / "What changes"): gather +
+    per-expert FFN + WeightedRowSum equals running every expert over every token
+    with weight zero where the token did not pick it."""
+    for name in ("tiny16", "gated2"):
+        inp = synth.make_layer(name)
+        r = oracle.layer(inp)
+        nv = oracle.naive_layer(inp)
+        assert np.max(np.abs(r["out"] - nv)) <= 1e-13 * np.max(np.abs(nv))
+
+
+def test_layer_equals_naive_loop_bitwise_on_dyadic_inputs(oracle_lib):
+    """PIN: on inputs whose every product and sum is exact in float64 (small
+    dyadic activations, dyadic routing weights), the gather path and the naive
+    loop agree bit for bit."""
+    inp = synth.make_layer("tiny16")
+    rng = np.random.default_rng(51)
+    inp.x = (rng.integers(-4, 5, size=inp.x.shape) / 4.0).astype(np.float32)
+    ids, _ = oracle.route_topk(inp.logits, inp.K)
+    w = np.tile(np.array([0.75, 0.25]), (inp.n, 1))
+    r = oracle.layer(inp, routing=(ids, w))
+    nv = oracle.naive_layer(inp, routing=(ids, w))
+    assert np.array_equal(r["out"], nv)
+
+
+def test_single_expert_layer_is_a_dense_ffn(oracle_lib):
+    """PIN: E = 1, K = 1 (weight 1) reduces to relu(x W_u^T)^2 W_d^T plus the
+    shared expert's FFN, checked with numpy float64."""
+    inp = synth.make_layer("tiny16", E=1, K=1)
+    r = oracle.layer(inp)
+    assert np.all(r["weights"] == 1.0)
+    x = inp.x.astype(np.float64)
+    ref = _np_ffn(x, _np_dequant(inp.up, 0), _np_dequant(inp.down, 0), "relu2", inp.f)
+    ref += _np_ffn(x, _np_dequant(inp.shared_up, 0), _np_dequant(inp.shared_down, 0), "relu2", inp.fs)
+    assert np.max(np.abs(r["out"] - ref)) <= 1e-13 * np.max(np.abs(ref))
+
+
+def test_bf16_mode_rounds_activations(oracle_lib):
+    """The bf16-activation mode equals numpy matmuls on bf16-rounded x with h
+    rounded to bf16 (the rounding itself is pinned to torch above)."""
+    E, d, f, n = 2, 32, 32, 6
+    up = synth.random_nvfp4(61, E, f, d)
+    dn = synth.random_nvfp4(62, E, d, f)
+    x = np.random.default_rng(63).standard_normal((n, d))
+    off = np.array([0, 2, 6], dtype=np.int32)
+    got = oracle.expert_ffn(x, off, up, dn, f, "relu2", bf16_act=True)
+
+    ref = np.zeros_like(got)
+    for e in range(E):
+        r0, r1 = off[e], off[e + 1]
+        xb = np.array([[oracle.round_bf16(v) for v in row] for row in x[r0:r1]])
+        u = xb @ _np_dequant(up, e).T
+        h = np.array([[oracle.round_bf16(v) for v in row] for row in np.maximum(u, 0) ** 2])
+        ref[r0:r1] = h @ _np_dequant(dn, e).T
+    assert np.max(np.abs(got - ref)) <= 1e-13 * np.max(np.abs(ref))
