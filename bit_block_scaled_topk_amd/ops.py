@@ -1,0 +1,312 @@
+"""Python binding of libmoe_nvfp4.so (argument marshalling only).
+
+Each function has the name of the C entry point it calls and passes torch
+tensors' device pointers and the current HIP stream.  Every step of the layer
+runs in the library's HIP kernels; there is no fallback: importing this module
+raises if the library is not built, and every call raises on a non-OK status.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_nvfp4.so")
+
+MOE_OK, MOE_INVALID_ARG, MOE_UNSUPPORTED, MOE_HIP_ERROR, MOE_WORKSPACE_TOO_SMALL = 0, 1, 2, 3, 4
+MOE_F32, MOE_BF16 = 0, 1
+MOE_RELU2, MOE_SWIGLU = 0, 1
+MAX_GEMV_ROWS = 32
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built: run bit_block_scaled_topk_amd/build.py "
+                      "(or __graft_entry__.build()) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = _lib.moe_status_string(status).decode()
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+class NVFP4Weights(ctypes.Structure):
+    """moe_nvfp4_weights: device pointers of one projection for E experts."""
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("global_", ctypes.c_void_p),
+                ("rows", ctypes.c_int), ("cols", ctypes.c_int)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+_lib.moe_status_string.argtypes = [_I]
+_lib.moe_status_string.restype = ctypes.c_char_p
+_lib.moe_route_topk.argtypes = [_P, _I, _I, _I, _P, _P, _P]
+_lib.moe_route_topk.restype = _I
+_lib.moe_gather_workspace_size.argtypes = [_I, _I]
+_lib.moe_gather_workspace_size.restype = _SZ
+_lib.moe_gather_rows.argtypes = [_P, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.moe_gather_rows.restype = _I
+_lib.nvfp4_expert_ffn_workspace_size.argtypes = [_I, _I, _I, _I]
+_lib.nvfp4_expert_ffn_workspace_size.restype = _SZ
+_lib.nvfp4_grouped_linear_workspace_size.argtypes = [_I, _I, _I]
+_lib.nvfp4_grouped_linear_workspace_size.restype = _SZ
+_lib.nvfp4_expert_ffn.argtypes = [_P, _I, _I, _I, _P, _I, ctypes.POINTER(NVFP4Weights),
+                                  ctypes.POINTER(NVFP4Weights), _I, _I, _P, _SZ, _P, _P]
+_lib.nvfp4_expert_ffn.restype = _I
+_lib.moe_weighted_row_sum.argtypes = [_P, _P, _I, _P, _P, _I, _I, _I, _P]
+_lib.moe_weighted_row_sum.restype = _I
+_lib.moe_weighted_row_sum_into.argtypes = [_P, _P, _I, _P, _P, _I, _I, _I, _P]
+_lib.moe_weighted_row_sum_into.restype = _I
+_lib.nvfp4_unpack_bf16.argtypes = [_P, _P, _I, _I, _P, _P]
+_lib.nvfp4_unpack_bf16.restype = _I
+_lib.nvfp4_grouped_linear.argtypes = [_P, _I, _I, _I, _P, _I, ctypes.POINTER(NVFP4Weights), _I, _P, _SZ,
+                                      _P, _P]
+_lib.nvfp4_grouped_linear.restype = _I
+
+EXPORTED = ("moe_route_topk", "moe_gather_workspace_size", "moe_gather_rows",
+            "nvfp4_expert_ffn_workspace_size", "nvfp4_grouped_linear_workspace_size",
+            "nvfp4_expert_ffn", "moe_weighted_row_sum", "moe_weighted_row_sum_into", "nvfp4_unpack_bf16",
+            "nvfp4_grouped_linear", "moe_status_string")
+
+
+def _check(fn: str, st: int):
+    if st != MOE_OK:
+        raise MoeError(fn, st)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype in (torch.bfloat16, torch.uint16, torch.int16):
+        return MOE_BF16
+    raise TypeError(f"unsupported activation dtype {t.dtype}")
+
+
+@dataclass
+class DeviceNVFP4:
+    """One NVFP4 projection for E experts resident on the device."""
+    codes: torch.Tensor    # uint8 [E, rows, cols/2]
+    scales: torch.Tensor   # uint8 [E, rows, cols/16]
+    globals_: torch.Tensor  # float32 [E]
+    rows: int
+    cols: int
+
+    @classmethod
+    def from_host(cls, t, device="cuda") -> "DeviceNVFP4":
+        return cls(torch.from_numpy(t.codes).to(device), torch.from_numpy(t.scales).to(device),
+                   torch.from_numpy(t.globals_).to(device), int(t.rows), int(t.cols))
+
+    def struct(self) -> NVFP4Weights:
+        return NVFP4Weights(self.codes.data_ptr(), self.scales.data_ptr(), self.globals_.data_ptr(),
+                            self.rows, self.cols)
+
+    @property
+    def n_experts(self) -> int:
+        return int(self.codes.shape[0])
+
+
+# ----------------------------------------------------------------------------
+# the C entry points, one to one
+# ----------------------------------------------------------------------------
+
+def moe_route_topk(logits: torch.Tensor, top_k: int, ids: Optional[torch.Tensor] = None,
+                   weights: Optional[torch.Tensor] = None, stream=None):
+    n, E = logits.shape
+    if ids is None:
+        ids = torch.empty((n, top_k), dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty((n, top_k), dtype=torch.float32, device=logits.device)
+    _check("moe_route_topk", _lib.moe_route_topk(_ptr(logits), n, E, top_k, _ptr(ids), _ptr(weights),
+                                                 _stream(stream)))
+    return ids, weights
+
+
+def moe_gather_workspace_size(n_tokens: int, n_experts: int) -> int:
+    return int(_lib.moe_gather_workspace_size(n_tokens, n_experts))
+
+
+def moe_gather_rows(x: torch.Tensor, topk_ids: torch.Tensor, n_experts: int, workspace: torch.Tensor,
+                    xg=None, offsets=None, row_token=None, rows=None, stream=None):
+    n, d = x.shape
+    K = topk_ids.shape[1]
+    dev = x.device
+    if xg is None:
+        xg = torch.empty((n * K, d), dtype=x.dtype, device=dev)
+    if offsets is None:
+        offsets = torch.empty((n_experts + 1,), dtype=torch.int32, device=dev)
+    if row_token is None:
+        row_token = torch.empty((n * K,), dtype=torch.int32, device=dev)
+    if rows is None:
+        rows = torch.empty((n, K), dtype=torch.int32, device=dev)
+    _check("moe_gather_rows", _lib.moe_gather_rows(
+        _ptr(x), _dtype_code(x), n, d, _ptr(topk_ids), K, n_experts, _ptr(xg), _ptr(offsets),
+        _ptr(row_token), _ptr(rows), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return xg, offsets, row_token, rows
+
+
+def nvfp4_expert_ffn_workspace_size(n_rows: int, d_model: int, d_ff: int, act_dtype: int) -> int:
+    return int(_lib.nvfp4_expert_ffn_workspace_size(n_rows, d_model, d_ff, act_dtype))
+
+
+def nvfp4_grouped_linear_workspace_size(n_rows: int, k: int, a_dtype: int) -> int:
+    return int(_lib.nvfp4_grouped_linear_workspace_size(n_rows, k, a_dtype))
+
+
+def nvfp4_expert_ffn(xg: torch.Tensor, offsets: torch.Tensor, up: DeviceNVFP4, down: DeviceNVFP4,
+                     act: int, max_rows_per_expert: int, workspace: torch.Tensor, out: torch.Tensor,
+                     gemv_max_rows: int = MAX_GEMV_ROWS, stream=None) -> torch.Tensor:
+    n_rows = xg.shape[0]
+    u, dn = up.struct(), down.struct()
+    _check("nvfp4_expert_ffn", _lib.nvfp4_expert_ffn(
+        _ptr(xg), _dtype_code(xg), n_rows, max_rows_per_expert, _ptr(offsets), up.n_experts,
+        ctypes.byref(u), ctypes.byref(dn), act, gemv_max_rows, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_weighted_row_sum(dst: torch.Tensor, src: torch.Tensor, rows: torch.Tensor, weights: torch.Tensor,
+                         stream=None) -> torch.Tensor:
+    n, K = rows.shape
+    _check("moe_weighted_row_sum", _lib.moe_weighted_row_sum(
+        _ptr(dst), _ptr(src), src.shape[0], _ptr(rows), _ptr(weights), n, K, dst.shape[1], _stream(stream)))
+    return dst
+
+
+def moe_weighted_row_sum_into(dst: torch.Tensor, src: torch.Tensor, rows: torch.Tensor, weights: torch.Tensor,
+                              stream=None) -> torch.Tensor:
+    n, K = rows.shape
+    _check("moe_weighted_row_sum_into", _lib.moe_weighted_row_sum_into(
+        _ptr(dst), _ptr(src), src.shape[0], _ptr(rows), _ptr(weights), n, K, dst.shape[1], _stream(stream)))
+    return dst
+
+
+def nvfp4_unpack_bf16(codes: torch.Tensor, scales: torch.Tensor, rows: int, cols: int,
+                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.int16, device=codes.device)
+    _check("nvfp4_unpack_bf16", _lib.nvfp4_unpack_bf16(_ptr(codes), _ptr(scales), rows, cols, _ptr(out),
+                                                       _stream(stream)))
+    return out
+
+
+def nvfp4_grouped_linear(a: torch.Tensor, offsets: torch.Tensor, w: DeviceNVFP4, max_rows_per_expert: int,
+                         out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                         gemv_max_rows: int = MAX_GEMV_ROWS, stream=None) -> torch.Tensor:
+    n_rows = a.shape[0]
+    if out is None:
+        out = torch.empty((n_rows, w.rows), dtype=torch.float32, device=a.device)
+    need = nvfp4_grouped_linear_workspace_size(n_rows, w.cols, _dtype_code(a))
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=a.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws = w.struct()
+    _check("nvfp4_grouped_linear", _lib.nvfp4_grouped_linear(
+        _ptr(a), _dtype_code(a), n_rows, max_rows_per_expert, _ptr(offsets), w.n_experts, ctypes.byref(ws),
+        gemv_max_rows, _ptr(workspace), ws_bytes, _ptr(out), _stream(stream)))
+    return out
+
+
+def status_string(status: int) -> str:
+    return _lib.moe_status_string(status).decode()
+
+
+# ----------------------------------------------------------------------------
+# the layer: the four calls composed on one stream
+# ----------------------------------------------------------------------------
+
+class MoELayer:
+    """Device-resident weights and preallocated buffers of one NVFP4 MoE layer.
+
+    ``forward(x, logits)`` runs route -> gather -> shared expert -> routed
+    experts -> WeightedRowSum on the current stream and returns the [n, d]
+    float32 output (gllm PR #91, "What changes").  Buffers are allocated once
+    at construction for n_tokens tokens, so a forward pass allocates nothing.
+    """
+
+    def __init__(self, inp, device="cuda", gemv_max_rows: int = MAX_GEMV_ROWS, n_tokens: Optional[int] = None):
+        self.n = int(n_tokens if n_tokens is not None else inp.n)
+        self.d, self.E, self.K, self.f, self.fs = inp.d, inp.E, inp.K, inp.f, inp.fs
+        self.act = MOE_SWIGLU if inp.act == "swiglu" else MOE_RELU2
+        self.x_dtype = MOE_F32 if inp.x_dtype == "f32" else MOE_BF16
+        self.gemv_max_rows = gemv_max_rows
+        self.up = DeviceNVFP4.from_host(inp.up, device)
+        self.down = DeviceNVFP4.from_host(inp.down, device)
+        self.shared_up = DeviceNVFP4.from_host(inp.shared_up, device) if inp.fs > 0 else None
+        self.shared_down = DeviceNVFP4.from_host(inp.shared_down, device) if inp.fs > 0 else None
+        self.device = device
+        self._alloc(self.n)
+
+    def _alloc(self, n):
+        dev, K, d = self.device, self.K, self.d
+        xdt = torch.float32 if self.x_dtype == MOE_F32 else torch.int16
+        R = n * K
+        self.ids = torch.empty((n, K), dtype=torch.int32, device=dev)
+        self.w = torch.empty((n, K), dtype=torch.float32, device=dev)
+        self.xg = torch.empty((R, d), dtype=xdt, device=dev)
+        self.offsets = torch.empty((self.E + 1,), dtype=torch.int32, device=dev)
+        self.shared_offsets = torch.tensor([0, n], dtype=torch.int32, device=dev)
+        self.row_token = torch.empty((R,), dtype=torch.int32, device=dev)
+        self.rows = torch.empty((n, K), dtype=torch.int32, device=dev)
+        self.yg = torch.empty((R, d), dtype=torch.float32, device=dev)
+        self.out = torch.empty((n, d), dtype=torch.float32, device=dev)
+        ws = max(moe_gather_workspace_size(n, self.E),
+                 nvfp4_expert_ffn_workspace_size(R, d, self.f, self.x_dtype),
+                 nvfp4_expert_ffn_workspace_size(n, d, max(self.fs, 32), self.x_dtype))
+        self.workspace = torch.empty((ws,), dtype=torch.uint8, device=dev)
+
+    def weights(self):
+        return (self.up, self.down, self.shared_up, self.shared_down)
+
+    def forward(self, x: torch.Tensor, logits: torch.Tensor, stream=None, weights=None,
+                timing: Optional[dict] = None) -> torch.Tensor:
+        """x [n, d] (float32 or bf16 bits as int16), logits [n, E] float32.
+        ``weights`` optionally overrides the projections: (up, down, shared_up,
+        shared_down) DeviceNVFP4 tuples, e.g. another layer's copy.  ``timing``
+        (a dict of step name -> list) collects (start, end) HIP events recorded
+        on the stream around each call."""
+        up, down, sup, sdn = weights if weights is not None else self.weights()
+        n = x.shape[0]
+
+        def mark(name, fn):
+            if timing is None:
+                return fn()
+            s = torch.cuda.current_stream() if stream is None else stream
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            r = fn()
+            b.record(s)
+            timing.setdefault(name, []).append((a, b))
+            return r
+
+        mark("route", lambda: moe_route_topk(logits, self.K, self.ids, self.w, stream=stream))
+        mark("gather", lambda: moe_gather_rows(x, self.ids, self.E, self.workspace, self.xg, self.offsets,
+                                               self.row_token, self.rows, stream=stream))
+        if self.fs > 0:
+            mark("shared_ffn", lambda: nvfp4_expert_ffn(x, self.shared_offsets, sup, sdn, MOE_RELU2, n,
+                                                        self.workspace, self.out, self.gemv_max_rows,
+                                                        stream=stream))
+        mark("routed_ffn", lambda: nvfp4_expert_ffn(self.xg, self.offsets, up, down, self.act, n,
+                                                    self.workspace, self.yg, self.gemv_max_rows, stream=stream))
+        if self.fs > 0:
+            mark("combine", lambda: moe_weighted_row_sum(self.out, self.yg, self.rows, self.w, stream=stream))
+        else:
+            mark("combine", lambda: moe_weighted_row_sum_into(self.out, self.yg, self.rows, self.w,
+                                                              stream=stream))
+        return self.out

@@ -1,0 +1,219 @@
+/*
+ * moe_nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 MoE expert-FFN library.
+ *
+ * One quantised mixture-of-experts layer, as profiled and rebuilt in the gllm
+ * pull request "perf: gather tokens per MoE expert, run large NVFP4 GEMMs on bf16
+ * tensor cores #91" (sections "What changes" and "bf16 NVFP4 GEMM (CUDA)"):
+ *
+ *   moe_route_topk        topK routing, softmax over the picked logits
+ *   moe_gather_rows       each (token, picked expert) pair -> one row of packed
+ *                         n*topK-row buffers grouped by expert, plus the row copy
+ *   nvfp4_expert_ffn      each expert's up -> relu^2 (or SwiGLU) -> down over its
+ *                         own contiguous rows only (NVFP4 weights)
+ *   moe_weighted_row_sum  dst[i] += sum_j w[i,j] * src[rows[i,j]], fixed j order
+ *
+ * plus two single-step entry points used on their own and by the tests:
+ *   nvfp4_unpack_bf16     exact NVFP4 -> bf16 unpack that drops the global
+ *   nvfp4_grouped_linear  one grouped NVFP4 projection, y = global * a . W^T
+ *
+ * Conventions for every entry point
+ *   - Pointers named as device pointers are HIP device memory owned by the
+ *     caller; the library never allocates, frees or synchronises, and never
+ *     reads device memory on the host.  All work is enqueued on `stream`.
+ *   - Arguments are checked on the host before anything is launched.  On
+ *     MOE_INVALID_ARG, MOE_UNSUPPORTED and MOE_WORKSPACE_TOO_SMALL nothing was
+ *     enqueued and no output was touched; MOE_HIP_ERROR (a failed launch) may
+ *     leave earlier kernels of the same call enqueued.
+ *   - Entry points are stateless and may be called from several host threads.
+ *   - Results are deterministic: the same inputs give the same output bits,
+ *     whatever else runs on the GPU (no floating-point atomics anywhere).
+ *
+ * NVFP4 tensor layout (one projection of n_experts experts):
+ *   codes   uint8 [n_experts][rows][cols/2]: e2m1 codes (OCP MX E2M1: sign bit 3,
+ *           magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6), element 2i of a row in the
+ *           low nibble of byte i, element 2i+1 in the high nibble;
+ *   scales  uint8 [n_experts][rows][cols/16]: one OCP E4M3FN scale per 16
+ *           consecutive elements of a row (bias 7, max 448, 0x7F/0xFF = NaN);
+ *   global  float [n_experts]: the per-tensor fp32 global of each expert;
+ *   value(r, k) = global * e4m3(scale[r][k/16]) * e2m1(code(r, k)).
+ *   rows = out_features, cols = in_features; cols must be a multiple of 32.
+ */
+#ifndef MOE_NVFP4_H
+#define MOE_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int moe_status;
+#define MOE_OK 0
+#define MOE_INVALID_ARG 1          /* a null pointer, a negative or inconsistent size */
+#define MOE_UNSUPPORTED 2          /* a size or mode outside the limits stated below */
+#define MOE_HIP_ERROR 3            /* a kernel launch failed (hipGetLastError) */
+#define MOE_WORKSPACE_TOO_SMALL 4  /* ws_bytes below the size query's answer */
+
+typedef int moe_dtype;
+#define MOE_F32 0   /* IEEE binary32 */
+#define MOE_BF16 1  /* bfloat16, stored as uint16 bit patterns */
+
+typedef int moe_act;
+#define MOE_RELU2 0   /* h = max(u, 0)^2 */
+#define MOE_SWIGLU 1  /* up rows [0, f) = gate a, rows [f, 2f) = b; h = a/(1+e^-a) * b */
+
+/* Limits checked by every entry point. */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 32
+#define MOE_MAX_GEMV_ROWS 32
+
+/* One NVFP4 projection for n_experts experts; all three pointers are device
+ * pointers laid out as described in the file header. */
+typedef struct {
+  const uint8_t *codes;
+  const uint8_t *scales;
+  const float *global;
+  int rows; /* out_features */
+  int cols; /* in_features, a multiple of 32 */
+} moe_nvfp4_weights;
+
+/* moe_route_topk -- per token, the top_k experts by router logit and their
+ * weights, a softmax over the top_k picked logits only.
+ *   logits        device float [n_tokens][n_experts], finite or -inf (no NaN)
+ *   topk_ids      device int32 [n_tokens][top_k]: slot j holds the j-th largest
+ *                 logit's expert; equal logits go to the lower expert index
+ *   topk_weights  device float [n_tokens][top_k]:
+ *                 w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), i = 0..top_k-1
+ * Limits: 1 <= n_experts <= 1024, 1 <= top_k <= min(n_experts, 32),
+ * n_tokens >= 0 (0 launches nothing).
+ * Source: topK routing of the MoE layer (gllm #91 "What the profile showed":
+ * 128 experts, topK 6); the weights are the per-pick weights WeightedRowSum
+ * consumes ("What changes"). */
+moe_status moe_route_topk(const float *logits, int n_tokens, int n_experts, int top_k,
+                          int32_t *topk_ids, float *topk_weights, hipStream_t stream);
+
+/* Workspace bytes moe_gather_rows needs for n_tokens tokens and n_experts
+ * experts (0 for invalid arguments). */
+size_t moe_gather_workspace_size(int n_tokens, int n_experts);
+
+/* moe_gather_rows -- the MoE gather (gllm #91 "What changes": each (token,
+ * picked expert) pair gets a row in packed buffers of n x topK rows, grouped by
+ * expert; one Embedding gathers the inputs).
+ *   x               device [n_tokens][d_model] of x_dtype (F32 or BF16)
+ *   topk_ids        device int32 [n_tokens][top_k], expert ids (each token
+ *                   should pick an expert at most once)
+ *   xg              device [n_tokens*top_k][d_model] of x_dtype (out):
+ *                   xg[r] = x[row_token[r]], a bit copy; must not alias x
+ *   expert_offsets  device int32 [n_experts+1] (out): exclusive scan of the
+ *                   per-expert pick counts; rows of expert e are
+ *                   [expert_offsets[e], expert_offsets[e+1])
+ *   row_token       device int32 [n_tokens*top_k] (out): token of each row
+ *   rows            device int32 [n_tokens][top_k] (out): row of pick (t, j)
+ *   workspace       device scratch of ws_bytes >= moe_gather_workspace_size()
+ * Rows inside an expert's group are in ascending token order, so the layout is
+ * unique.  A pick whose id is outside [0, n_experts) is dropped: its rows[t][j]
+ * is -1, it is not counted, and the unused tail rows (from
+ * expert_offsets[n_experts] on) get row_token -1 and are not written in xg.
+ * Limits: n_tokens*top_k < 2^31, d_model a multiple of 16, x and xg 16-byte
+ * aligned. */
+moe_status moe_gather_rows(const void *x, moe_dtype x_dtype, int n_tokens, int d_model,
+                           const int32_t *topk_ids, int top_k, int n_experts, void *xg,
+                           int32_t *expert_offsets, int32_t *row_token, int32_t *rows,
+                           void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes nvfp4_expert_ffn needs for n_rows packed rows of d_model
+ * activations of act_dtype and an intermediate h of width d_ff (up->rows is
+ * d_ff, or 2*d_ff for SwiGLU); 0 for invalid arguments.  It holds h as three
+ * bf16 planes (hi + mid + lo) and, for fp32 activations, the activations split
+ * the same way. */
+size_t nvfp4_expert_ffn_workspace_size(int n_rows, int d_model, int d_ff, moe_dtype act_dtype);
+
+/* Workspace bytes nvfp4_grouped_linear needs (fp32 activations only; 0 for bf16). */
+size_t nvfp4_grouped_linear_workspace_size(int n_rows, int k, moe_dtype a_dtype);
+
+/* nvfp4_expert_ffn -- each expert's FFN over its own rows (gllm #91 "What
+ * changes": up -> relu^2 -> down over only its own rows; Glq v0.2.13 "v3b":
+ * relu^2 for non-gated NemotronH; the gated experts' fused gate-up projection
+ * of TensorFold issue #2265 "What ncu shows").
+ *   xg              device [n_rows][up->cols] activations of act_dtype
+ *   expert_offsets  device int32 [n_experts+1], non-decreasing, [0] = 0,
+ *                   [n_experts] <= n_rows; rows past it are left untouched
+ *   max_rows_per_expert  a host-side bound on every expert's row count (for
+ *                   routed experts n_tokens, since a token picks an expert once)
+ *   up, down        host structs of device pointers: up is [n_experts][f or 2f][d],
+ *                   down is [n_experts][d][f]; up->cols == down->rows == d,
+ *                   down->cols == f
+ *   gemv_max_rows   experts with at most this many rows (1..32, normally 32)
+ *                   take the decode path (fused dequant + matrix-core GEMV,
+ *                   activations and h carried at fp32 accuracy); experts with
+ *                   more rows take the prefill path (exact NVFP4 -> bf16 unpack
+ *                   into a bf16 MFMA GEMM, global as alpha, activation rounded
+ *                   to bf16 as gllm #91 "bf16 NVFP4 GEMM (CUDA)" does).  0 sends
+ *                   every expert to the prefill path.  When max_rows_per_expert
+ *                   <= gemv_max_rows the prefill kernels are not launched.
+ *   out             device float [n_rows][down->rows]
+ *   workspace       device scratch >= nvfp4_expert_ffn_workspace_size()
+ * Alignment: xg, codes and the workspace 16-byte aligned, scales 2-byte.
+ * The shared expert is this call with n_experts = 1 and offsets {0, n}. */
+moe_status nvfp4_expert_ffn(const void *xg, moe_dtype act_dtype, int n_rows,
+                            int max_rows_per_expert, const int32_t *expert_offsets,
+                            int n_experts, const moe_nvfp4_weights *up,
+                            const moe_nvfp4_weights *down, moe_act act, int gemv_max_rows,
+                            void *workspace, size_t ws_bytes, float *out, hipStream_t stream);
+
+/* moe_weighted_row_sum -- WeightedRowSum (gllm #91 "What changes"):
+ *   dst[i][c] += sum_{j=0..top_k-1} weights[i][j] * src[rows[i][j]][c]
+ * with the j-sum taken in order from 0 by fused multiply-adds into a zero
+ * accumulator and then added to dst once; one thread per output element, no
+ * atomics, so the result is deterministic.
+ *   dst      device float [n_tokens][d_model], read and written; no alias of src
+ *   src      device float [n_src_rows][d_model]
+ *   rows     device int32 [n_tokens][top_k]; an entry outside [0, n_src_rows)
+ *            contributes nothing (it is skipped, never read out of bounds)
+ *   weights  device float [n_tokens][top_k] */
+moe_status moe_weighted_row_sum(float *dst, const float *src, int n_src_rows,
+                                const int32_t *rows, const float *weights, int n_tokens,
+                                int top_k, int d_model, hipStream_t stream);
+
+/* moe_weighted_row_sum_into -- the same sum written onto a zero destination,
+ *   dst[i][c] = sum_{j=0..top_k-1} weights[i][j] * src[rows[i][j]][c]
+ * (same order and rounding as moe_weighted_row_sum with dst = 0), for layers
+ * without a shared expert. */
+moe_status moe_weighted_row_sum_into(float *dst, const float *src, int n_src_rows,
+                                     const int32_t *rows, const float *weights, int n_tokens,
+                                     int top_k, int d_model, hipStream_t stream);
+
+/* nvfp4_unpack_bf16 -- exact unpack of NVFP4 codes and scales to bf16 without
+ * the per-tensor global (gllm #91 "bf16 NVFP4 GEMM (CUDA)": an e2m1 code times
+ * an e4m3 block scale has at most 6 significant bits, so it is exact in bf16).
+ *   codes   device uint8 [rows][cols/2]; scales device uint8 [rows][cols/16]
+ *   out     device uint16 (bf16 bits) [rows][cols] = e4m3(scale) * e2m1(code)
+ * A NaN scale byte gives bf16 NaN for its 16 elements. */
+moe_status nvfp4_unpack_bf16(const uint8_t *codes, const uint8_t *scales, int rows, int cols,
+                             uint16_t *out, hipStream_t stream);
+
+/* nvfp4_grouped_linear -- one NVFP4 projection per expert group:
+ *   out[r][n] = global[e] * sum_k a[r][k] * e4m3 * e2m1 (W_e[n][k])  for r in expert e
+ * Path choice as in nvfp4_expert_ffn (decode path: fp32-accurate; prefill path:
+ * a rounded to bf16, exact bf16 weights, fp32 accumulation, global as alpha).
+ * This is the single NVFP4 matmul that gllm #91 "Testing" holds to the f32
+ * tolerance when fed bf16-exact activations.
+ *   a    device [n_rows][w->cols] of a_dtype; out device float [n_rows][w->rows]
+ *   workspace  device scratch >= nvfp4_grouped_linear_workspace_size() */
+moe_status nvfp4_grouped_linear(const void *a, moe_dtype a_dtype, int n_rows,
+                                int max_rows_per_expert, const int32_t *expert_offsets,
+                                int n_experts, const moe_nvfp4_weights *w, int gemv_max_rows,
+                                void *workspace, size_t ws_bytes, float *out,
+                                hipStream_t stream);
+
+/* A short English description of a status code (a static string). */
+const char *moe_status_string(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_NVFP4_H */

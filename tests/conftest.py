@@ -25,3 +25,15 @@ def oracle_lib():
     import oracle
     oracle.lib()
     return oracle
+
+
+_LAYER_CACHE = {}
+
+
+def cached_layer(name: str, **overrides):
+    """Seeded workload inputs, drawn once per test session."""
+    key = (name, tuple(sorted(overrides.items())))
+    if key not in _LAYER_CACHE:
+        from bit_block_scaled_topk_amd import synth
+        _LAYER_CACHE[key] = synth.make_layer(name, **overrides)
+    return _LAYER_CACHE[key]

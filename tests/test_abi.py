@@ -1,0 +1,151 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad
+arguments on the host before any HIP call (no GPU needed for any of these)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_nvfp4.h")
+LIB = os.path.join(ROOT, "bit_block_scaled_topk_amd", "libmoe_nvfp4.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from bit_block_scaled_topk_amd import build
+        build.build()
+    L = ctypes.CDLL(LIB)
+    return L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:moe_status|size_t|const char \*)\s*\**\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_layer_calls():
+    names = declared_functions()
+    for n in ("moe_route_topk", "moe_gather_rows", "nvfp4_expert_ffn", "moe_weighted_row_sum"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), f"{n} is declared in include/moe_nvfp4.h but not exported"
+
+
+def test_binding_names_match_header():
+    from bit_block_scaled_topk_amd import ops
+    assert sorted(ops.EXPORTED) == declared_functions()
+    for n in ops.EXPORTED:
+        if not n.endswith("status_string"):
+            assert hasattr(ops, n)
+
+
+class W(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("global_", ctypes.c_void_p),
+                ("rows", ctypes.c_int), ("cols", ctypes.c_int)]
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # an aligned non-null address: never dereferenced on the host
+
+
+def _setup(lib):
+    P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.moe_route_topk.argtypes = [P, I, I, I, P, P, P]
+    lib.moe_gather_rows.argtypes = [P, I, I, I, P, I, I, P, P, P, P, P, SZ, P]
+    lib.moe_gather_workspace_size.argtypes = [I, I]
+    lib.moe_gather_workspace_size.restype = SZ
+    lib.nvfp4_expert_ffn_workspace_size.argtypes = [I, I, I, I]
+    lib.nvfp4_expert_ffn_workspace_size.restype = SZ
+    lib.nvfp4_expert_ffn.argtypes = [P, I, I, I, P, I, ctypes.POINTER(W), ctypes.POINTER(W), I, I, P, SZ, P, P]
+    lib.moe_weighted_row_sum.argtypes = [P, P, I, P, P, I, I, I, P]
+    lib.moe_weighted_row_sum_into.argtypes = [P, P, I, P, P, I, I, I, P]
+    lib.nvfp4_unpack_bf16.argtypes = [P, P, I, I, P, P]
+    lib.nvfp4_grouped_linear.argtypes = [P, I, I, I, P, I, ctypes.POINTER(W), I, P, SZ, P, P]
+    lib.moe_status_string.argtypes = [I]
+    lib.moe_status_string.restype = ctypes.c_char_p
+
+
+def test_status_strings(lib):
+    _setup(lib)
+    assert lib.moe_status_string(0) == b"ok"
+    for s in (1, 2, 3, 4):
+        assert lib.moe_status_string(s) not in (b"ok", b"unknown status")
+    assert lib.moe_status_string(99) == b"unknown status"
+
+
+def test_route_argument_errors(lib):
+    _setup(lib)
+    assert lib.moe_route_topk(FAKE, 4, 8, 9, FAKE, FAKE, None) == 1       # top_k > E
+    assert lib.moe_route_topk(FAKE, 4, 8, 0, FAKE, FAKE, None) == 1       # top_k < 1
+    assert lib.moe_route_topk(FAKE, -1, 8, 2, FAKE, FAKE, None) == 1
+    assert lib.moe_route_topk(FAKE, 4, 2048, 2, FAKE, FAKE, None) == 2    # too many experts
+    assert lib.moe_route_topk(FAKE, 4, 64, 33, FAKE, FAKE, None) == 2     # top_k above 32
+    assert lib.moe_route_topk(None, 4, 8, 2, FAKE, FAKE, None) == 1       # null logits
+    assert lib.moe_route_topk(None, 0, 8, 2, None, None, None) == 0       # empty: nothing launched
+
+
+def test_gather_argument_errors(lib):
+    _setup(lib)
+    ws = lib.moe_gather_workspace_size(16, 8)
+    assert ws > 0 and ws % 256 == 0
+    assert lib.moe_gather_workspace_size(16, 0) == 0
+    assert lib.moe_gather_rows(FAKE, 1, 16, 24, FAKE, 2, 8, ctypes.c_void_p(2 << 20), FAKE, FAKE, FAKE, FAKE,
+                               ws, None) == 2   # d_model % 16
+    assert lib.moe_gather_rows(FAKE, 1, 16, 64, FAKE, 2, 8, ctypes.c_void_p(2 << 20), FAKE, FAKE, FAKE, FAKE,
+                               ws - 1, None) == 4  # workspace too small
+    assert lib.moe_gather_rows(FAKE, 1, 16, 64, FAKE, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == 1  # xg == x
+    assert lib.moe_gather_rows(FAKE, 7, 16, 64, FAKE, 2, 8, ctypes.c_void_p(2 << 20), FAKE, FAKE, FAKE, FAKE,
+                               ws, None) == 1   # bad dtype
+    assert lib.moe_gather_rows(ctypes.c_void_p((1 << 20) + 8), 1, 16, 64, FAKE, 2, 8, ctypes.c_void_p(2 << 20),
+                               FAKE, FAKE, FAKE, FAKE, ws, None) == 1  # misaligned x
+
+
+def _w(rows, cols, codes=FAKE):
+    return W(codes, FAKE, FAKE, rows, cols)
+
+
+def test_ffn_argument_errors(lib):
+    _setup(lib)
+    up, dn = _w(128, 64), _w(64, 128)
+    ws = lib.nvfp4_expert_ffn_workspace_size(32, 64, 128, 0)
+    assert ws >= 3 * 32 * 128 * 2 + 3 * 32 * 64 * 2
+    assert lib.nvfp4_expert_ffn_workspace_size(32, 64, 128, 1) < ws
+    args = lambda **k: dict(dict(xg=FAKE, dt=0, n=32, mx=16, off=FAKE, E=8, up=up, dn=dn, act=0, gm=32,
+                                 ws=FAKE, wsb=ws, out=FAKE), **k)
+
+    def call(a):
+        return lib.nvfp4_expert_ffn(a["xg"], a["dt"], a["n"], a["mx"], a["off"], a["E"], ctypes.byref(a["up"]),
+                                    ctypes.byref(a["dn"]), a["act"], a["gm"], a["ws"], a["wsb"], a["out"], None)
+
+    assert call(args(gm=33)) == 2                      # gemv_max_rows above 32
+    assert call(args(gm=-1)) == 2
+    assert call(args(wsb=ws - 1)) == 4                 # workspace too small
+    assert call(args(act=5)) == 1                      # unknown activation
+    assert call(args(act=1)) == 1                      # swiglu needs up rows = 2 f
+    assert call(args(up=_w(128, 48), dn=_w(48, 128))) == 2   # cols not a multiple of 32
+    assert call(args(up=_w(128, 64, codes=ctypes.c_void_p((1 << 20) + 4)))) == 1  # misaligned codes
+    assert call(args(E=2000)) == 2
+    assert call(args(xg=None)) == 1
+    assert call(args(n=0, xg=None, off=None, out=None, ws=None)) == 0   # empty: nothing launched
+
+
+def test_wrs_and_unpack_and_linear_argument_errors(lib):
+    _setup(lib)
+    assert lib.moe_weighted_row_sum(FAKE, FAKE, 4, FAKE, FAKE, 2, 2, 8, None) == 1      # dst aliases src
+    assert lib.moe_weighted_row_sum(FAKE, ctypes.c_void_p(2 << 20), 4, FAKE, FAKE, 2, 0, 8, None) == 1
+    assert lib.moe_weighted_row_sum_into(None, FAKE, 4, FAKE, FAKE, 2, 2, 8, None) == 1
+    assert lib.moe_weighted_row_sum(None, None, 0, None, None, 0, 2, 8, None) == 0    # empty
+    assert lib.nvfp4_unpack_bf16(FAKE, FAKE, 4, 48, FAKE, None) == 2                    # cols % 32
+    assert lib.nvfp4_unpack_bf16(FAKE, FAKE, -1, 64, FAKE, None) == 1
+    assert lib.nvfp4_unpack_bf16(ctypes.c_void_p((1 << 20) + 1), FAKE, 4, 64, FAKE, None) == 1
+    w = _w(64, 64)
+    assert lib.nvfp4_grouped_linear(FAKE, 0, 8, 8, FAKE, 2, ctypes.byref(w), 32, None, 0, FAKE, None) == 1
+    assert lib.nvfp4_grouped_linear(FAKE, 1, 8, 8, FAKE, 2, ctypes.byref(w), 40, None, 0, FAKE, None) == 2

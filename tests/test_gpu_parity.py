@@ -1,0 +1,369 @@
+"""Parity of every HIP entry point with the CPU oracle, on seeded inputs.
+
+Bars: bit-exact for routing ids, gather layouts and the unpacked weights;
+normwise relative max-error max|gpu - ref| / max|ref| <= 1e-5 for the decode
+(fp32-accurate) path and <= 2e-2 for the prefill (bf16-activation MFMA) path;
+WeightedRowSum within its rigorous fp32 rounding bound.  All inputs come from
+bit_block_scaled_topk_amd.synth; every expected value comes from oracle/.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_block_scaled_topk_amd import synth
+from conftest import cached_layer
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+TOL_DECODE = 1e-5
+TOL_PREFILL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from bit_block_scaled_topk_amd import ops as _ops
+    return _ops
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def normwise(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+
+
+def bf16_bits_to_f64(b):
+    return oracle.bf16_bits_to_f64(np.asarray(b).view(np.uint16))
+
+
+# ----------------------------------------------------------------------------
+# unpack
+# ----------------------------------------------------------------------------
+
+def test_unpack_every_code_with_every_scale(ops):
+    """Every (e2m1 code, e4m3 scale byte) pair, NaN scales included, unpacks
+    bit-exactly to the oracle's value (which PIN tests tie to torch's casts)."""
+    rows, cols = 256, 32
+    codes = np.tile(np.array([0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE], dtype=np.uint8), (rows, 2))
+    scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 2, axis=1)
+    out = ops.nvfp4_unpack_bf16(dev(codes), dev(scales), rows, cols)
+    got = bf16_bits_to_f64(host(out))
+    ref = oracle.dequant(codes, scales, 1.0, with_global=False)
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 * 32
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_unpack_random_multi_expert(ops):
+    t = synth.random_bytes_nvfp4(101, 3, 96, 224)
+    rows = 3 * 96
+    out = ops.nvfp4_unpack_bf16(dev(t.codes.reshape(rows, -1)), dev(t.scales.reshape(rows, -1)), rows, 224)
+    got = bf16_bits_to_f64(host(out))
+    ref = oracle.dequant(t.codes.reshape(rows, -1), t.scales.reshape(rows, -1), 1.0, with_global=False)
+    assert np.array_equal(got, ref)
+
+
+# ----------------------------------------------------------------------------
+# routing
+# ----------------------------------------------------------------------------
+
+def _route_case(ops, logits, K):
+    ids, w = ops.moe_route_topk(dev(logits), K)
+    rids, rw = oracle.route_topk(logits, K)
+    assert np.array_equal(host(ids), rids)
+    assert np.max(np.abs(host(w).astype(np.float64) - rw)) <= 4e-7
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_route_workloads(ops, name):
+    cfg = synth.WORKLOADS[name]
+    _route_case(ops, synth.draw_logits(name), cfg["K"])
+
+
+def test_route_edge_cases(ops):
+    rng = np.random.default_rng(3)
+    _route_case(ops, np.zeros((5, 10), dtype=np.float32), 4)                        # all tied
+    _route_case(ops, rng.standard_normal((7, 6)).astype(np.float32), 6)             # K = E
+    _route_case(ops, rng.standard_normal((3, 1)).astype(np.float32), 1)             # E = 1
+    lg = rng.standard_normal((9, 1024)).astype(np.float32)
+    _route_case(ops, lg, 32)                                                        # max E, max K
+    lg = np.round(rng.standard_normal((33, 200)) * 2).astype(np.float32)            # many ties
+    _route_case(ops, lg, 8)
+    lg = rng.standard_normal((4, 77)).astype(np.float32)
+    lg[:, ::3] = -np.inf                                                            # masked experts
+    _route_case(ops, lg, 5)
+    ids, w = ops.moe_route_topk(torch.empty((0, 8), device=DEV), 2)                 # no tokens
+    assert ids.shape == (0, 2)
+
+
+# ----------------------------------------------------------------------------
+# gather
+# ----------------------------------------------------------------------------
+
+def _gather_case(ops, x, ids, E):
+    n, K = ids.shape
+    ws = torch.empty((ops.moe_gather_workspace_size(n, E),), dtype=torch.uint8, device=DEV)
+    xg, off, row_token, rows = ops.moe_gather_rows(dev(x), dev(ids), E, ws)
+    r_off, r_rt, r_rows = oracle.gather_layout(ids, E)
+    assert np.array_equal(host(off), r_off)
+    assert np.array_equal(host(rows), r_rows)
+    assert np.array_equal(host(row_token), r_rt)
+    r_xg = oracle.gather_copy(x, r_rt)
+    assert np.array_equal(host(xg).view(np.uint8), r_xg.view(np.uint8))
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_gather_workloads(ops, name):
+    cfg = synth.WORKLOADS[name]
+    ids, _ = oracle.route_topk(synth.draw_logits(name), cfg["K"])
+    _gather_case(ops, synth.draw_activations(name), ids, cfg["E"])
+
+
+def test_gather_edge_cases(ops):
+    rng = np.random.default_rng(5)
+    # one expert takes every token; ragged token count; fp32 rows
+    ids = np.zeros((45, 1), dtype=np.int32)
+    _gather_case(ops, rng.standard_normal((45, 32)).astype(np.float32), ids, 3)
+    # many tokens, large E (global-memory bitmap path), bf16 rows
+    E, n, K = 256, 3001, 8
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(n)]).astype(np.int32)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((n, 64)).astype(np.float32))
+    _gather_case(ops, x, ids, E)
+
+
+def test_gather_drops_invalid_ids(ops):
+    """Out-of-range ids are dropped: rows -1, not counted, tail rows untouched."""
+    rng = np.random.default_rng(6)
+    n, K, E, d = 10, 3, 5, 16
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(n)]).astype(np.int32)
+    ids[2, 1] = 5
+    ids[7, 0] = -3
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    ws = torch.empty((ops.moe_gather_workspace_size(n, E),), dtype=torch.uint8, device=DEV)
+    canary = torch.full((n * K, d), float("nan"), device=DEV)
+    xg, off, row_token, rows = ops.moe_gather_rows(dev(x), dev(ids), E, ws, xg=canary)
+    valid = (ids >= 0) & (ids < E)
+    got_rows = host(rows)
+    assert np.all(got_rows[~valid] == -1)
+    got_off = host(off)
+    assert got_off[-1] == valid.sum()
+    assert np.array_equal(np.diff(got_off), np.bincount(ids[valid], minlength=E))
+    rt = host(row_token)
+    assert np.all(rt[valid.sum():] == -1)
+    xgh = host(xg)
+    for t in range(n):
+        for j in range(K):
+            if valid[t, j]:
+                assert rt[got_rows[t, j]] == t
+                assert np.array_equal(xgh[got_rows[t, j]], x[t])
+    assert np.all(np.isnan(xgh[valid.sum():]))
+
+
+# ----------------------------------------------------------------------------
+# WeightedRowSum
+# ----------------------------------------------------------------------------
+
+def _wrs_bound(dst, src, rows, w):
+    """|fl(dst + sum_j w*src) - exact| <= (K+1) * 2^-24 * (|dst| + sum_j |w*src|):
+    K fused multiply-adds and one add, each rounding once."""
+    K = rows.shape[1]
+    mag = np.abs(dst).astype(np.float64)
+    for j in range(K):
+        r = rows[:, j]
+        ok = (r >= 0) & (r < src.shape[0])
+        mag += np.where(ok[:, None], np.abs(w[:, j:j + 1] * src[np.clip(r, 0, src.shape[0] - 1)]), 0)
+    return (K + 1) * 2.0 ** -24 * mag
+
+
+@pytest.mark.parametrize("d", [100, 33])
+def test_weighted_row_sum(ops, d):
+    rng = np.random.default_rng(d)
+    n, K, ns = 37, 6, 50
+    src = rng.standard_normal((ns, d)).astype(np.float32)
+    rows = rng.integers(0, ns, size=(n, K)).astype(np.int32)
+    rows[0] = rows[0, 0]                       # repeated source rows
+    w = rng.standard_normal((n, K)).astype(np.float32)
+    dst = rng.standard_normal((n, d)).astype(np.float32) * 10   # pre-filled dst
+    out = ops.moe_weighted_row_sum(dev(dst), dev(src), dev(rows), dev(w))
+    got = host(out).astype(np.float64)
+    ref = oracle.weighted_row_sum(dst, src, rows, w)
+    assert np.all(np.abs(got - ref) <= _wrs_bound(dst, src, rows, w))
+    out2 = ops.moe_weighted_row_sum(dev(dst), dev(src), dev(rows), dev(w))
+    assert np.array_equal(host(out2), host(out))   # deterministic
+    into = ops.moe_weighted_row_sum_into(torch.full((n, d), 7.0, device=DEV), dev(src), dev(rows), dev(w))
+    zero = np.zeros_like(dst)
+    assert np.all(np.abs(host(into) - oracle.weighted_row_sum(zero, src, rows, w)) <=
+                  _wrs_bound(zero, src, rows, w))
+
+
+def test_weighted_row_sum_skips_out_of_range_rows(ops):
+    rng = np.random.default_rng(8)
+    n, K, ns, d = 6, 3, 4, 8
+    src = rng.standard_normal((ns, d)).astype(np.float32)
+    rows = rng.integers(0, ns, size=(n, K)).astype(np.int32)
+    rows[1, 2], rows[4, 0] = 4, -1
+    w = rng.standard_normal((n, K)).astype(np.float32)
+    dst = rng.standard_normal((n, d)).astype(np.float32)
+    got = host(ops.moe_weighted_row_sum(dev(dst), dev(src), dev(rows), dev(w))).astype(np.float64)
+    w0 = w.copy()
+    w0[1, 2] = w0[4, 0] = 0
+    rows0 = np.clip(rows, 0, ns - 1)
+    ref = oracle.weighted_row_sum(dst, src, rows0, w0)
+    assert np.all(np.abs(got - ref) <= _wrs_bound(dst, src, rows, w) + 1e-30)
+
+
+# ----------------------------------------------------------------------------
+# one grouped projection
+# ----------------------------------------------------------------------------
+
+def _offsets(counts):
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("a_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+def test_grouped_linear(ops, a_dtype, path):
+    """The prefill case is gllm #91's NVFP4Exact test: bf16-exact activations on
+    the bf16 MFMA path are held to the fp32 tolerance (a lossy unpack, or a
+    missing or doubled global, fails it)."""
+    rng = np.random.default_rng(11)
+    if path == "decode":
+        counts = [3, 0, 32, 1, 17, 16, 5]
+        gmax = 32
+    else:
+        counts = [33, 0, 130, 1, 257, 64]
+        gmax = 0
+    k, n_out = 96, 200
+    w = synth.random_bytes_nvfp4(12, len(counts), n_out, k)
+    n_rows = int(sum(counts))
+    a32 = rng.standard_normal((n_rows, k)).astype(np.float32)
+    if a_dtype == "bf16":
+        a = synth.f32_to_bf16_bits(a32)
+        a64 = oracle.bf16_bits_to_f64(a)
+    else:
+        a = a32
+        a64 = a32.astype(np.float64)
+    off = _offsets(counts)
+    dw = ops.DeviceNVFP4.from_host(w)
+    out = ops.nvfp4_grouped_linear(dev(a), dev(off), dw, max(counts), gemv_max_rows=gmax)
+    got = host(out)
+    if path == "prefill" and a_dtype == "f32":
+        # the prefill path rounds fp32 activations to bf16
+        a64 = np.vectorize(oracle.round_bf16)(a64)
+    ref = oracle.linear(a64, off, w)
+    assert normwise(got, ref) <= TOL_DECODE
+
+
+def test_grouped_linear_mixed_paths(ops):
+    """Experts on both sides of the 32-row threshold in one call."""
+    rng = np.random.default_rng(13)
+    counts = [32, 33, 1, 0, 70, 31]
+    k, n_out = 128, 64
+    w = synth.random_nvfp4(14, len(counts), n_out, k)
+    a = synth.f32_to_bf16_bits(rng.standard_normal((sum(counts), k)).astype(np.float32))
+    off = _offsets(counts)
+    got = host(ops.nvfp4_grouped_linear(dev(a), dev(off), ops.DeviceNVFP4.from_host(w), max(counts)))
+    ref = oracle.linear(oracle.bf16_bits_to_f64(a), off, w)
+    assert normwise(got, ref) <= TOL_DECODE
+
+
+# ----------------------------------------------------------------------------
+# the layer
+# ----------------------------------------------------------------------------
+
+def _run_layer(ops, inp, gemv_max_rows=32, stream=None):
+    layer = ops.MoELayer(inp, gemv_max_rows=gemv_max_rows)
+    out = layer.forward(dev(inp.x), dev(inp.logits), stream=stream)
+    torch.cuda.synchronize()
+    return layer, host(out).astype(np.float64)
+
+
+@pytest.mark.parametrize("name", ["tiny16", "decode1", "decode32_zipf", "gated2"])
+def test_layer_decode_workloads(ops, name):
+    inp = cached_layer(name)
+    layer, got = _run_layer(ops, inp)
+    ref = oracle.layer(inp)
+    assert np.array_equal(host(layer.ids), ref["ids"])
+    assert np.array_equal(host(layer.offsets), ref["offsets"])
+    assert np.array_equal(host(layer.rows), ref["rows"])
+    counts = np.diff(ref["offsets"])
+    assert counts.max() <= 32   # every expert on the decode path
+    assert normwise(got, ref["out"]) <= TOL_DECODE
+    # routed expert outputs row by row (the packed yg buffer)
+    R = inp.n * inp.K
+    assert normwise(host(layer.yg)[:R], ref["yg"]) <= TOL_DECODE
+
+
+def test_layer_tiny_forced_onto_prefill_path(ops):
+    inp = cached_layer("tiny16")
+    _, got = _run_layer(ops, inp, gemv_max_rows=0)
+    assert normwise(got, oracle.layer(inp)["out"]) <= TOL_PREFILL
+    # against the oracle's bf16-activation mode the only differences are
+    # accumulation order and rare bf16 rounding flips of h
+    assert normwise(got, oracle.layer(inp, bf16_act=True)["out"]) <= 2e-3
+
+
+def test_layer_prefill_4314_tokens(ops):
+    inp = cached_layer("prefill4314")
+    layer, got = _run_layer(ops, inp)
+    ids, w = oracle.route_topk(inp.logits, inp.K)
+    assert np.array_equal(host(layer.ids), ids)
+    off, row_token, rows = oracle.gather_layout(ids, inp.E)
+    assert np.array_equal(host(layer.offsets), off)
+    assert np.array_equal(host(layer.rows), rows)
+    assert np.array_equal(host(layer.row_token), row_token)
+    assert np.diff(off).min() > 32    # every expert on the prefill path
+    tokens = [0, 1, 777, 2048, 3001, 4313]
+    ref = oracle.layer_sampled(inp, tokens, ids, w)
+    assert normwise(got[tokens], ref) <= TOL_PREFILL
+    ref_bf = oracle.layer_sampled(inp, tokens, ids, w, bf16_act_of_expert=lambda e: True)
+    assert normwise(got[tokens], ref_bf) <= 2e-3
+    assert np.all(np.isfinite(got))
+
+
+def test_layer_is_deterministic_and_stream_independent(ops):
+    inp = cached_layer("decode32_zipf")
+    layer = ops.MoELayer(inp)
+    x, lg = dev(inp.x), dev(inp.logits)
+    a = layer.forward(x, lg).clone()
+    b = layer.forward(x, lg).clone()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        c = layer.forward(x, lg, stream=s).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(a, c)
+
+
+def test_expert_ffn_writes_only_its_rows(ops):
+    """A canary-filled output: the FFN writes rows [0, offsets[E]) and nothing
+    else (gllm #91 "Testing": a MatMul into a slice lands in exactly those rows)."""
+    inp = cached_layer("tiny16")
+    counts = np.array([3, 0, 9, 1, 0, 4, 2, 1], dtype=np.int64)
+    off = _offsets(counts)
+    n_rows = int(off[-1]) + 5
+    rng = np.random.default_rng(17)
+    xg = rng.standard_normal((n_rows, inp.d)).astype(np.float32)
+    out = torch.full((n_rows, inp.d), float("nan"), device=DEV)
+    ws = torch.empty((ops.nvfp4_expert_ffn_workspace_size(n_rows, inp.d, inp.f, ops.MOE_F32),),
+                     dtype=torch.uint8, device=DEV)
+    up, dn = ops.DeviceNVFP4.from_host(inp.up), ops.DeviceNVFP4.from_host(inp.down)
+    ops.nvfp4_expert_ffn(dev(xg), dev(off), up, dn, ops.MOE_RELU2, int(counts.max()), ws, out)
+    got = host(out)
+    assert np.all(np.isnan(got[off[-1]:]))
+    ref = oracle.expert_ffn(xg[:off[-1]].astype(np.float64), off, inp.up, inp.down, inp.f, "relu2")
+    assert normwise(got[:off[-1]], ref) <= TOL_DECODE
