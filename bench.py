@@ -45,8 +45,22 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
     p.add_argument("--traffic", default=None,
-                   help="JSON file with measured HBM bytes per routed-FFN call (from rocprofv3 --pmc)")
+                   help="JSON file with the measured HBM bytes per launch of the dominant kernel "
+                        "(from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
+    p.add_argument("--copy-probe-mb", type=int, default=0,
+                   help="only run a plain device-to-device copy of this many MiB, 5 times (the "
+                        "reference for scaling FETCH_SIZE / WRITE_SIZE), then exit")
     return p.parse_args()
+
+
+def copy_probe(mb: int):
+    import torch
+    src = torch.empty((mb << 20,), dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": mb << 20, "launches": 5}))
 
 
 def weight_bytes(t) -> int:
@@ -57,23 +71,31 @@ def per_expert_bytes(t) -> int:
     return weight_bytes(t) // t.n_experts
 
 
-def routed_ffn_bytes(inp, ids) -> dict:
-    """Algorithmic bytes of one routed nvfp4_expert_ffn call: every picked
-    expert's up and down NVFP4 weights once (codes + scales + global), the
-    gathered activations read, h written and read once at fp32, y written."""
+def layer_ffn_bytes(inp, ids) -> dict:
+    """Algorithmic bytes of one step's expert FFN launches (the up and the down
+    decode GEMV, shared + routed experts): every picked expert's and the shared
+    expert's NVFP4 weights once (codes + scales + global), the activations read,
+    h written and read once at fp32, the expert outputs written at fp32."""
     import numpy as np
     distinct = len(np.unique(ids))
     R = inp.n * inp.K
     xb = 4 if inp.x_dtype == "f32" else 2
     w = distinct * (per_expert_bytes(inp.up) + per_expert_bytes(inp.down))
     act = R * inp.d * xb + 2 * R * inp.f * 4 + R * inp.d * 4
+    if inp.fs > 0:
+        w += weight_bytes(inp.shared_up) + weight_bytes(inp.shared_down)
+        act += inp.n * inp.d * xb + 2 * inp.n * inp.fs * 4 + inp.n * inp.d * 4
     return dict(weights=w, activations=act, total=w + act, distinct_experts=distinct)
 
 
-def routed_ffn_flops(inp, ids) -> int:
+def layer_ffn_flops(inp) -> int:
+    """2 flops per multiply-add over real rows (no tile padding), shared + routed."""
     R = inp.n * inp.K
     up_rows = 2 * inp.f if inp.act == "swiglu" else inp.f
-    return 2 * R * inp.d * up_rows + 2 * R * inp.f * inp.d
+    fl = 2 * R * inp.d * up_rows + 2 * R * inp.f * inp.d
+    if inp.fs > 0:
+        fl += 2 * inp.n * inp.d * inp.fs * 2
+    return fl
 
 
 def cpu_baseline(inp, budget_s: float) -> dict:
@@ -114,6 +136,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                           "(the sharded design is described, not built)"}))
         sys.exit(2)
+    if args.copy_probe_mb > 0:
+        copy_probe(args.copy_probe_mb)
+        return
     import numpy as np
     import torch
 
@@ -139,12 +164,12 @@ def main():
 
     def one_pass():
         for c in copies:
-            layer.forward(x, logits, weights=c)
+            layer.forward_fused(x, logits, weights=c)
 
     # warmup (eager) on the bench stream
     with torch.cuda.stream(stream):
         for i in range(max(1, args.warmup)):
-            layer.forward(x, logits, weights=copies[i % L])
+            layer.forward_fused(x, logits, weights=copies[i % L])
     torch.cuda.synchronize()
 
     steps = max(L, (args.steps // L) * L)
@@ -166,35 +191,45 @@ def main():
                 graph.replay()
         else:
             for i in range(steps):
-                layer.forward(x, logits, weights=copies[i % L])
+                layer.forward_fused(x, logits, weights=copies[i % L])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     tokens_per_s = inp.n * steps / elapsed
 
-    # ---- kernel timing: HIP events around each call, eager, same copies ----
-    timing = {}
+    # ---- kernel timing: HIP events recorded by the library between its launch
+    # phases (moe_layer_forward_profiled), on the launch stream, same copies ----
     k_steps = min(steps, 20 * L)
+    ev = ops.HipEvents(6 * k_steps)
     with torch.cuda.stream(stream):
         for i in range(k_steps):
-            layer.forward(x, logits, weights=copies[i % L], timing=timing)
+            layer.forward_profiled(x, logits, ev.slice(6 * i), weights=copies[i % L])
     torch.cuda.synchronize()
-    breakdown = {k: float(np.mean([a.elapsed_time(b) for a, b in v]) * 1e3) for k, v in timing.items()}
-    ids = layer.ids.cpu().numpy()
-    b = routed_ffn_bytes(inp, ids)
-    ffn_us = breakdown["routed_ffn"]
-    achieved = b["total"] / (ffn_us * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "routed nvfp4_expert_ffn (k_dq_gemv up + down)",
-                "bytes_per_call": b["total"], "us_per_call": round(ffn_us, 3)}
-    counts = np.diff(layer.offsets.cpu().numpy())
-    if counts.max() > 32:
-        flops = routed_ffn_flops(inp, ids)
+    names = ["route_gather", "split", "up", "down", "combine"]
+    phase = {nm: [ev.elapsed_ms(6 * i + j, 6 * i + j + 1) * 1e3 for i in range(k_steps)]
+             for j, nm in enumerate(names)}
+    ev.close()
+    breakdown = {k: float(np.mean(v)) for k, v in phase.items()}
+    v = layer.views()
+    ids = v["ids"].cpu().numpy()
+    counts = np.diff(v["offsets"].cpu().numpy())
+    ffn_us = breakdown["up"] + breakdown["down"]
+    if counts.max() <= 32:
+        b = layer_ffn_bytes(inp, ids)
+        achieved = b["total"] / (ffn_us * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "k_dq_gemv (decode dequant-GEMV: one up and one down launch per step, "
+                              "shared + routed experts)",
+                    "bytes_per_launch": b["total"] // 2, "us_per_launch": round(ffn_us / 2, 3),
+                    "bytes": b}
+    else:
+        flops = layer_ffn_flops(inp)
         tf = flops / (ffn_us * 1e-6) / 1e12
         roofline = {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                    "kernel": "routed nvfp4_expert_ffn (k_dq_gemm up + down)",
-                    "flops_per_call": flops, "us_per_call": round(ffn_us, 3)}
+                    "kernel": "k_dq_gemm (prefill grouped bf16 GEMM: one up and one down launch per step, "
+                              "shared + routed experts)",
+                    "flops_per_launch": flops // 2, "us_per_launch": round(ffn_us / 2, 3)}
     if args.traffic and os.path.exists(args.traffic):
         with open(args.traffic) as fh:
             roofline["traffic"] = json.load(fh).get("bytes_per_call")

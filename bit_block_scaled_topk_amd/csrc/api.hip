@@ -5,6 +5,7 @@
 // device from expert_offsets, and the host only uses bounds it already knows
 // (Glq v0.2.13, "v3a": host syncs inside the MoE loop dominated the host
 // budget; gllm PR #91, "Results": every op synchronising was what remained).
+#include <limits.h>
 #include <stdint.h>
 
 #include "launch.hpp"
@@ -23,8 +24,8 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_HIP_ERROR; }
 
 bool weights_ok(const moe_nvfp4_weights *w) {
-  return w && w->codes && w->scales && w->global && w->rows > 0 && w->cols > 0 &&
-         aligned(w->codes, 16) && aligned(w->scales, 2) && aligned(w->global, 4);
+  return w && w->codes && w->scales && w->global && w->rows > 0 && w->cols > 0 && aligned(w->codes, 16) &&
+         aligned(w->scales, 2) && aligned(w->global, 4);
 }
 
 // Planes of the fp32-activation split: three bf16 planes of n_rows*k.
@@ -32,6 +33,50 @@ size_t split_bytes(long n_rows, long k) { return align_up((size_t)3 * n_rows * k
 
 // h as three bf16 planes of n_rows*f.
 size_t h_bytes(long n_rows, long f) { return align_up((size_t)3 * n_rows * f * sizeof(uint16_t)); }
+
+// A projection problem over grouped rows (offsets on the device) or over one
+// expert whose rows are known on the host (known_rows >= 0).
+ProjProblem make_problem(const uint16_t *a, long plane, long lda, const int32_t *offsets, int n_experts,
+                         int n_rows, int known_rows, const moe_nvfp4_weights *w, int n_out, float *out_f32,
+                         uint16_t *out_h, long ldo, long h_plane) {
+  ProjProblem p{};
+  p.a = a;
+  p.plane = plane;
+  p.lda = lda;
+  p.offsets = offsets;
+  p.n_experts = n_experts;
+  p.n_rows = n_rows;
+  p.known_rows = known_rows;
+  p.min_rows = 1;
+  p.max_rows = INT_MAX;
+  p.codes = w->codes;
+  p.scales = w->scales;
+  p.global = w->global;
+  p.n_w = w->rows;
+  p.k = w->cols;
+  p.n_out = n_out;
+  p.out_f32 = out_f32;
+  p.out_h = out_h;
+  p.ldo = ldo;
+  p.h_plane = h_plane;
+  return p;
+}
+
+// Decode-path copy of a problem: experts with 1..dec_rows rows.
+ProjProblem as_decode(ProjProblem p, int dec_rows) {
+  p.min_rows = 1;
+  p.max_rows = dec_rows;
+  return p;
+}
+
+// Prefill-path copy: experts with more than gemv_max_rows rows.  h is one bf16
+// plane there (the activation rounded to bf16).
+ProjProblem as_prefill(ProjProblem p, int gemv_max_rows) {
+  p.min_rows = gemv_max_rows + 1;
+  p.max_rows = INT_MAX;
+  if (p.known_rows >= 0) p.min_rows = 1;
+  return p;
+}
 
 }  // namespace
 
@@ -74,7 +119,7 @@ moe_status moe_gather_rows(const void *x, moe_dtype x_dtype, int n_tokens, int d
   if ((long)n_tokens * top_k >= (1L << 31)) return MOE_UNSUPPORTED;
   if (!expert_offsets || !workspace) return MOE_INVALID_ARG;
   if (n_tokens > 0 && (!x || !topk_ids || !xg || !row_token || !rows)) return MOE_INVALID_ARG;
-  if (n_tokens > 0 && (!aligned(x, 16) || !aligned(xg, 16))) return MOE_INVALID_ARG;
+  if (n_tokens > 0 && (!aligned(x, 16) || !aligned(xg, 16) || !aligned(workspace, 16))) return MOE_INVALID_ARG;
   if (x && xg && x == xg) return MOE_INVALID_ARG;
   if (ws_bytes < moe_gather_workspace_size(n_tokens, n_experts)) return MOE_WORKSPACE_TOO_SMALL;
   int elem = (x_dtype == MOE_F32) ? 4 : 2;
@@ -95,8 +140,7 @@ static moe_status wrs_common(float *dst, const float *src, int n_src_rows, const
 }
 
 moe_status moe_weighted_row_sum(float *dst, const float *src, int n_src_rows, const int32_t *rows,
-                                const float *weights, int n_tokens, int top_k, int d_model,
-                                hipStream_t stream) {
+                                const float *weights, int n_tokens, int top_k, int d_model, hipStream_t stream) {
   return wrs_common(dst, src, n_src_rows, rows, weights, n_tokens, top_k, d_model, true, stream);
 }
 
@@ -161,33 +205,29 @@ moe_status nvfp4_expert_ffn(const void *xg, moe_dtype act_dtype, int n_rows, int
   const uint16_t *a = (const uint16_t *)xg;
   int nt = 1;
   long a_plane = 0;
-  hipError_t err = hipSuccess;
   if (act_dtype == MOE_F32) {
     uint16_t *planes = (uint16_t *)ws;
     a_plane = (long)n_rows * d;
-    err = launch_split3((const float *)xg, (long)n_rows * d, planes, a_plane, stream);
-    if (err != hipSuccess) return MOE_HIP_ERROR;
+    if (launch_split3((const float *)xg, (long)n_rows * d, planes, a_plane, stream) != hipSuccess)
+      return MOE_HIP_ERROR;
     a = planes;
     nt = 3;
   }
-  // up projection + activation -> h
-  err = launch_dq_gemv_planes(a, nt, a_plane, d, expert_offsets, n_experts, n_rows, dec_rows, max_active, up->codes,
-                              up->scales, up->global, up->rows, d, f, epi, nullptr, h, f, h_plane, stream);
-  if (err != hipSuccess) return MOE_HIP_ERROR;
+  ProjProblem pu = make_problem(a, a_plane, d, expert_offsets, n_experts, n_rows, -1, up, f, nullptr, h, f, h_plane);
+  ProjProblem pd = make_problem(h, h_plane, f, expert_offsets, n_experts, n_rows, -1, down, d_out, out, nullptr,
+                                d_out, 0);
+  ProjProblem q;
+  q = as_decode(pu, dec_rows);
+  if (launch_dq_gemv(&q, &max_active, 1, nt, epi, stream) != hipSuccess) return MOE_HIP_ERROR;
   if (use_gemm) {
-    err = launch_dq_gemm(a, d, expert_offsets, n_experts, gemv_max_rows + 1, n_rows, up->codes, up->scales,
-                         up->global, up->rows, d, f, epi, nullptr, h, f, stream);
-    if (err != hipSuccess) return MOE_HIP_ERROR;
+    q = as_prefill(pu, gemv_max_rows);
+    if (launch_dq_gemm(&q, 1, epi, stream) != hipSuccess) return MOE_HIP_ERROR;
   }
-  // down projection -> out
-  err = launch_dq_gemv_planes(h, 3, h_plane, f, expert_offsets, n_experts, n_rows, dec_rows, max_active, down->codes,
-                              down->scales, down->global, d_out, f, d_out, EPI_F32, out, nullptr, d_out, 0,
-                              stream);
-  if (err != hipSuccess) return MOE_HIP_ERROR;
+  q = as_decode(pd, dec_rows);
+  if (launch_dq_gemv(&q, &max_active, 1, 3, EPI_F32, stream) != hipSuccess) return MOE_HIP_ERROR;
   if (use_gemm) {
-    err = launch_dq_gemm(h, f, expert_offsets, n_experts, gemv_max_rows + 1, n_rows, down->codes, down->scales,
-                         down->global, d_out, f, d_out, EPI_F32, out, nullptr, d_out, stream);
-    if (err != hipSuccess) return MOE_HIP_ERROR;
+    q = as_prefill(pd, gemv_max_rows);
+    if (launch_dq_gemm(&q, 1, EPI_F32, stream) != hipSuccess) return MOE_HIP_ERROR;
   }
   return MOE_OK;
 }
@@ -217,23 +257,241 @@ moe_status nvfp4_grouped_linear(const void *a_in, moe_dtype a_dtype, int n_rows,
   const uint16_t *a = (const uint16_t *)a_in;
   int nt = 1;
   long a_plane = 0;
-  hipError_t err;
   if (a_dtype == MOE_F32) {
     uint16_t *planes = (uint16_t *)workspace;
     a_plane = (long)n_rows * k;
-    err = launch_split3((const float *)a_in, (long)n_rows * k, planes, a_plane, stream);
-    if (err != hipSuccess) return MOE_HIP_ERROR;
+    if (launch_split3((const float *)a_in, (long)n_rows * k, planes, a_plane, stream) != hipSuccess)
+      return MOE_HIP_ERROR;
     a = planes;
     nt = 3;
   }
-  err = launch_dq_gemv_planes(a, nt, a_plane, k, expert_offsets, n_experts, n_rows, dec_rows, max_active, w->codes,
-                              w->scales, w->global, n_out, k, n_out, EPI_F32, out, nullptr, n_out, 0, stream);
-  if (err != hipSuccess) return MOE_HIP_ERROR;
+  ProjProblem p = make_problem(a, a_plane, k, expert_offsets, n_experts, n_rows, -1, w, n_out, out, nullptr, n_out, 0);
+  ProjProblem q = as_decode(p, dec_rows);
+  if (launch_dq_gemv(&q, &max_active, 1, nt, EPI_F32, stream) != hipSuccess) return MOE_HIP_ERROR;
   if (use_gemm) {
-    err = launch_dq_gemm(a, k, expert_offsets, n_experts, gemv_max_rows + 1, n_rows, w->codes, w->scales,
-                         w->global, n_out, k, n_out, EPI_F32, out, nullptr, n_out, stream);
-    if (err != hipSuccess) return MOE_HIP_ERROR;
+    q = as_prefill(p, gemv_max_rows);
+    if (launch_dq_gemm(&q, 1, EPI_F32, stream) != hipSuccess) return MOE_HIP_ERROR;
   }
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// the whole layer
+// ---------------------------------------------------------------------------
+
+namespace {
+
+struct LayerPlan {
+  int n, d, E, K, f, fs, R;
+  bool has_shared, f32;
+  size_t off_ids, off_w, off_offsets, off_row_token, off_rows, off_xg, off_yg, off_gather, off_h, off_hs,
+      off_split, off_split_s, total;
+};
+
+bool plan_layer(const moe_layer_desc *dsc, LayerPlan *pl) {
+  if (!dsc) return false;
+  LayerPlan p{};
+  p.n = dsc->n_tokens;
+  p.d = dsc->d_model;
+  p.E = dsc->n_experts;
+  p.K = dsc->top_k;
+  if (p.n < 0 || p.d <= 0 || p.E < 1 || p.K < 1 || p.K > p.E) return false;
+  if (p.E > MOE_MAX_EXPERTS || p.K > MOE_MAX_TOPK) return false;
+  if (dsc->x_dtype != MOE_F32 && dsc->x_dtype != MOE_BF16) return false;
+  if (dsc->act != MOE_RELU2 && dsc->act != MOE_SWIGLU) return false;
+  if (dsc->gemv_max_rows < 0 || dsc->gemv_max_rows > MOE_MAX_GEMV_ROWS) return false;
+  if (!weights_ok(&dsc->up) || !weights_ok(&dsc->down)) return false;
+  p.f = dsc->down.cols;
+  if (dsc->up.cols != p.d || dsc->down.rows != p.d) return false;
+  if (dsc->up.rows != (dsc->act == MOE_SWIGLU ? 2 * p.f : p.f)) return false;
+  if (p.d % 32 || p.f % 32) return false;
+  p.has_shared = dsc->shared_up.codes != nullptr;
+  p.fs = 0;
+  if (p.has_shared) {
+    if (!weights_ok(&dsc->shared_up) || !weights_ok(&dsc->shared_down)) return false;
+    p.fs = dsc->shared_down.cols;
+    if (dsc->shared_up.cols != p.d || dsc->shared_down.rows != p.d || dsc->shared_up.rows != p.fs) return false;
+    if (p.fs % 32) return false;
+  }
+  if ((long)p.n * p.K >= (1L << 31)) return false;
+  p.R = p.n * p.K;
+  p.f32 = dsc->x_dtype == MOE_F32;
+  const size_t xb = p.f32 ? 4 : 2;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  p.off_ids = take((size_t)p.R * 4);
+  p.off_w = take((size_t)p.R * 4);
+  p.off_offsets = take((size_t)(p.E + 1) * 4);
+  p.off_row_token = take((size_t)p.R * 4);
+  p.off_rows = take((size_t)p.R * 4);
+  p.off_xg = take((size_t)p.R * p.d * xb);
+  p.off_yg = take((size_t)p.R * p.d * 4);
+  p.off_gather = take(gather_workspace_bytes(p.n, p.E));
+  p.off_h = take(h_bytes(p.R, p.f));
+  p.off_hs = take(p.has_shared ? h_bytes(p.n, p.fs) : 0);
+  p.off_split = take(p.f32 ? split_bytes(p.R, p.d) : 0);
+  p.off_split_s = take(p.f32 ? split_bytes(p.n, p.d) : 0);
+  p.total = o;
+  *pl = p;
+  return true;
+}
+
+}  // namespace
+
+size_t moe_layer_workspace_size(const moe_layer_desc *desc) {
+  LayerPlan p;
+  if (!plan_layer(desc, &p)) return 0;
+  return p.total;
+}
+
+moe_status moe_layer_get_views(const moe_layer_desc *desc, void *workspace, moe_layer_views *v) {
+  LayerPlan p;
+  if (!plan_layer(desc, &p) || !workspace || !v) return MOE_INVALID_ARG;
+  char *ws = (char *)workspace;
+  v->topk_ids = (int32_t *)(ws + p.off_ids);
+  v->topk_weights = (float *)(ws + p.off_w);
+  v->expert_offsets = (int32_t *)(ws + p.off_offsets);
+  v->row_token = (int32_t *)(ws + p.off_row_token);
+  v->rows = (int32_t *)(ws + p.off_rows);
+  v->xg = (void *)(ws + p.off_xg);
+  v->yg = (float *)(ws + p.off_yg);
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward(const moe_layer_desc *dsc, const void *x, const float *logits, float *out,
+                             void *workspace, size_t ws_bytes, hipStream_t stream) {
+  return moe_layer_forward_profiled(dsc, x, logits, out, workspace, ws_bytes, nullptr, stream);
+}
+
+moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, const float *logits, float *out,
+                                      void *workspace, size_t ws_bytes, hipEvent_t *events, hipStream_t stream) {
+  auto mark = [&](int i) { return events ? hipEventRecord(events[i], stream) : hipSuccess; };
+  LayerPlan p;
+  if (!plan_layer(dsc, &p)) return MOE_INVALID_ARG;
+  if (p.n == 0) return MOE_OK;
+  if (!x || !logits || !out || !workspace) return MOE_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(workspace, kAlign)) return MOE_INVALID_ARG;
+  if (ws_bytes < p.total) return MOE_WORKSPACE_TOO_SMALL;
+  char *ws = (char *)workspace;
+  int32_t *ids = (int32_t *)(ws + p.off_ids);
+  float *w = (float *)(ws + p.off_w);
+  int32_t *offsets = (int32_t *)(ws + p.off_offsets);
+  int32_t *row_token = (int32_t *)(ws + p.off_row_token);
+  int32_t *rows = (int32_t *)(ws + p.off_rows);
+  void *xg = ws + p.off_xg;
+  float *yg = (float *)(ws + p.off_yg);
+  uint16_t *h = (uint16_t *)(ws + p.off_h);
+  uint16_t *hs = (uint16_t *)(ws + p.off_hs);
+  const int elem = p.f32 ? 4 : 2;
+
+  if (mark(0) != hipSuccess) return MOE_HIP_ERROR;
+  // 1. routing + gather
+  if (gather_is_single_launch(p.n, p.K, p.E, elem, p.d)) {
+    if (launch_route_gather_small(logits, p.n, p.E, p.K, ids, w, x, elem, p.d, xg, offsets, row_token, rows,
+                                  stream) != hipSuccess)
+      return MOE_HIP_ERROR;
+  } else {
+    if (launch_route_topk(logits, p.n, p.E, p.K, ids, w, stream) != hipSuccess) return MOE_HIP_ERROR;
+    if (launch_gather(x, elem, p.n, p.d, ids, p.K, p.E, xg, offsets, row_token, rows, ws + p.off_gather, stream) !=
+        hipSuccess)
+      return MOE_HIP_ERROR;
+  }
+
+  if (mark(1) != hipSuccess) return MOE_HIP_ERROR;
+  // 2. activation planes
+  const uint16_t *a_r = (const uint16_t *)xg, *a_s = (const uint16_t *)x;
+  long plane_r = 0, plane_s = 0;
+  int nt = 1;
+  if (p.f32) {
+    uint16_t *sr = (uint16_t *)(ws + p.off_split), *ss = (uint16_t *)(ws + p.off_split_s);
+    plane_r = (long)p.R * p.d;
+    plane_s = (long)p.n * p.d;
+    if (launch_split3((const float *)xg, plane_r, sr, plane_r, stream) != hipSuccess) return MOE_HIP_ERROR;
+    if (p.has_shared && launch_split3((const float *)x, plane_s, ss, plane_s, stream) != hipSuccess)
+      return MOE_HIP_ERROR;
+    a_r = sr;
+    a_s = ss;
+    nt = 3;
+  }
+
+  const int gmax = dsc->gemv_max_rows;
+  const int dec_rows = gmax < p.n ? gmax : p.n;  // a routed expert has at most n rows
+  const bool routed_gemm = p.n > gmax;
+  const bool shared_gemv = p.has_shared && p.n <= gmax;
+  const bool shared_gemm = p.has_shared && p.n > gmax;
+  const int max_active = p.E < p.R ? p.E : p.R;
+  const int epi = dsc->act == MOE_SWIGLU ? EPI_SWIGLU : EPI_RELU2;
+  const long h_plane = (long)p.R * p.f, hs_plane = (long)p.n * p.fs;
+
+  ProjProblem ru = make_problem(a_r, plane_r, p.d, offsets, p.E, p.R, -1, &dsc->up, p.f, nullptr, h, p.f, h_plane);
+  ProjProblem rd = make_problem(h, h_plane, p.f, offsets, p.E, p.R, -1, &dsc->down, p.d, yg, nullptr, p.d, 0);
+  ProjProblem su{}, sd{};
+  if (p.has_shared) {
+    su = make_problem(a_s, plane_s, p.d, nullptr, 1, p.n, p.n, &dsc->shared_up, p.fs, nullptr, hs, p.fs, hs_plane);
+    sd = make_problem(hs, hs_plane, p.fs, nullptr, 1, p.n, p.n, &dsc->shared_down, p.d, out, nullptr, p.d, 0);
+  }
+
+  if (mark(2) != hipSuccess) return MOE_HIP_ERROR;
+  // 3. up projections (+ activation); the shared expert joins the routed launch
+  //    when both use the same epilogue
+  {
+    ProjProblem dec[2];
+    int act[2];
+    int c = 0;
+    const bool join = shared_gemv && epi == EPI_RELU2;
+    if (join) {
+      dec[c] = as_decode(su, gmax);
+      act[c++] = 1;
+    }
+    dec[c] = as_decode(ru, dec_rows);
+    act[c++] = max_active;
+    if (launch_dq_gemv(dec, act, c, nt, epi, stream) != hipSuccess) return MOE_HIP_ERROR;
+    if (shared_gemv && !join) {
+      ProjProblem s1 = as_decode(su, gmax);
+      int one = 1;
+      if (launch_dq_gemv(&s1, &one, 1, nt, EPI_RELU2, stream) != hipSuccess) return MOE_HIP_ERROR;
+    }
+    ProjProblem gem[2];
+    int g = 0;
+    const bool gjoin = shared_gemm && epi == EPI_RELU2;
+    if (gjoin) gem[g++] = as_prefill(su, gmax);
+    if (routed_gemm) gem[g++] = as_prefill(ru, gmax);
+    if (g > 0 && launch_dq_gemm(gem, g, epi, stream) != hipSuccess) return MOE_HIP_ERROR;
+    if (shared_gemm && !gjoin) {
+      ProjProblem s1 = as_prefill(su, gmax);
+      if (launch_dq_gemm(&s1, 1, EPI_RELU2, stream) != hipSuccess) return MOE_HIP_ERROR;
+    }
+  }
+
+  if (mark(3) != hipSuccess) return MOE_HIP_ERROR;
+  // 4. down projections: shared -> out, routed -> yg
+  {
+    ProjProblem dec[2];
+    int act[2];
+    int c = 0;
+    if (shared_gemv) {
+      dec[c] = as_decode(sd, gmax);
+      act[c++] = 1;
+    }
+    dec[c] = as_decode(rd, dec_rows);
+    act[c++] = max_active;
+    if (launch_dq_gemv(dec, act, c, 3, EPI_F32, stream) != hipSuccess) return MOE_HIP_ERROR;
+    ProjProblem gem[2];
+    int g = 0;
+    if (shared_gemm) gem[g++] = as_prefill(sd, gmax);
+    if (routed_gemm) gem[g++] = as_prefill(rd, gmax);
+    if (g > 0 && launch_dq_gemm(gem, g, EPI_F32, stream) != hipSuccess) return MOE_HIP_ERROR;
+  }
+
+  if (mark(4) != hipSuccess) return MOE_HIP_ERROR;
+  // 5. combine: out += sum_j w * yg[rows]  (onto zero without a shared expert)
+  if (launch_weighted_row_sum(out, yg, p.R, rows, w, p.n, p.K, p.d, p.has_shared, stream) != hipSuccess)
+    return MOE_HIP_ERROR;
+  if (mark(5) != hipSuccess) return MOE_HIP_ERROR;
   return MOE_OK;
 }
 

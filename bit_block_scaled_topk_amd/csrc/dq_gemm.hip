@@ -20,28 +20,15 @@ namespace {
 
 constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;  // +8 bf16 pad per LDS row
 
-struct GemmArgs {
-  const uint16_t *a;  // bf16 activations [rows][lda]
-  long lda;
-  const int32_t *offsets;
-  int n_experts;
-  int n_rows;    // rows of the activation / output buffers
-  int min_rows;  // experts with at least this many rows are handled here
-  const uint8_t *codes;
-  const uint8_t *scales;
-  const float *global;
-  int n_w;
-  int k;
-  int n_out;
-  float *out_f32;     // EPI_F32
-  uint16_t *out_h;    // EPI_RELU2 / EPI_SWIGLU: bf16 h [rows][ldo]
-  long ldo;
+struct GemmBatch {
+  ProjProblem p[2];
+  int count;
 };
 
 // Which expert and which of its 128-row tiles the m-tile index `mt` names.
 // Experts whose row range is not inside [0, n_rows) are skipped.
-__device__ __forceinline__ void find_tile(const int32_t *offsets, int E, int n_rows, int min_rows, int mt,
-                                          int lane, int *s_info) {
+__device__ __forceinline__ void find_tile(const int32_t *offsets, int E, int n_rows, int min_rows, int max_rows,
+                                          int mt, int lane, int *s_info) {
   int base = 0;
   for (int e0 = 0; e0 < E; e0 += 64) {
     int e = e0 + lane;
@@ -51,7 +38,7 @@ __device__ __forceinline__ void find_tile(const int32_t *offsets, int E, int n_r
       cnt = offsets[e + 1] - r0;
     }
     bool inside = r0 >= 0 && cnt > 0 && r0 <= n_rows - cnt;
-    int tiles = (cnt >= min_rows && inside) ? (cnt + BM - 1) / BM : 0;
+    int tiles = (cnt >= min_rows && cnt <= max_rows && inside) ? (cnt + BM - 1) / BM : 0;
     int incl = tiles;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -75,19 +62,34 @@ __device__ __forceinline__ void find_tile(const int32_t *offsets, int E, int n_r
 }
 
 template <int EPI>
-__global__ void __launch_bounds__(256) k_dq_gemm(GemmArgs p, int n_ntiles) {
+__global__ void __launch_bounds__(256) k_dq_gemm(GemmBatch batch) {
   __shared__ int s_info[3];
   __shared__ __attribute__((aligned(16))) uint16_t sA[BM * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t sB[BN * LDK];
 
+  int bid = blockIdx.x;
+  const bool second = batch.count > 1 && bid >= batch.p[0].blocks;
+  const ProjProblem p = second ? batch.p[1] : batch.p[0];
+  if (second) bid -= batch.p[0].blocks;
+  const int n_ntiles = p.n_tiles;
+
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int mt = blockIdx.x / n_ntiles;
-  const int nt = blockIdx.x - mt * n_ntiles;
-  if (wave == 0) find_tile(p.offsets, p.n_experts, p.n_rows, p.min_rows, mt, lane, s_info);
-  __syncthreads();
-  const int e = s_info[0];
-  if (e < 0) return;
-  const int r0 = s_info[1], mrows = s_info[2];
+  const int mt = bid / n_ntiles;
+  const int nt = bid - mt * n_ntiles;
+  int e, r0, mrows;
+  if (p.known_rows >= 0) {
+    e = 0;
+    r0 = mt * BM;
+    mrows = min(BM, p.known_rows - r0);
+    if (mrows <= 0) return;
+  } else {
+    if (wave == 0) find_tile(p.offsets, p.n_experts, p.n_rows, p.min_rows, p.max_rows, mt, lane, s_info);
+    __syncthreads();
+    e = s_info[0];
+    if (e < 0) return;
+    r0 = s_info[1];
+    mrows = s_info[2];
+  }
 
   // loader roles: thread -> (tile row, 32-wide half of the k step)
   const int lrow = tid >> 1, lhalf = tid & 1;
@@ -136,7 +138,8 @@ __global__ void __launch_bounds__(256) k_dq_gemm(GemmArgs p, int n_ntiles) {
     u32x4_t *da = (u32x4_t *)(sA + lrow * LDK + lhalf * 32);
 #pragma unroll
     for (int t = 0; t < 4; ++t) da[t] = ra[t];
-    const float s0 = e4m3_to_f32(rs & 0xFFu), s1 = e4m3_to_f32(rs >> 8);
+    float s0, s1;
+    e4m3x2_to_f32(rs, s0, s1);
     u32x4_t *db = (u32x4_t *)(sB + lrow * LDK + lhalf * 32);
     db[0] = dq8_bf16(rc[0], s0);
     db[1] = dq8_bf16(rc[1], s0);
@@ -200,26 +203,36 @@ __global__ void __launch_bounds__(256) k_dq_gemm(GemmArgs p, int n_ntiles) {
 
 }  // namespace
 
-hipError_t launch_dq_gemm(const uint16_t *a, long lda, const int32_t *offsets, int n_experts,
-                          int min_rows, long n_rows, const uint8_t *codes, const uint8_t *scales,
-                          const float *global, int n_w, int k, int n_out, int epi, float *out_f32,
-                          uint16_t *out_h, long ldo, hipStream_t stream) {
-  if (n_rows <= 0) return hipSuccess;
-  GemmArgs g;
-  g.a = a; g.lda = lda; g.offsets = offsets; g.n_experts = n_experts; g.n_rows = (int)n_rows;
-  g.min_rows = min_rows < 1 ? 1 : min_rows;
-  g.codes = codes; g.scales = scales; g.global = global; g.n_w = n_w; g.k = k; g.n_out = n_out;
-  g.out_f32 = out_f32; g.out_h = out_h; g.ldo = ldo;
-  // m-tiles: sum over big experts of ceil(rows/BM) <= n_rows/BM + (number of big experts)
-  long big = n_rows / g.min_rows;
-  if (big > n_experts) big = n_experts;
-  long m_tiles = (n_rows + BM - 1) / BM + big;
-  int n_ntiles = (epi == EPI_SWIGLU) ? (n_out + 63) / 64 : (n_out + BN - 1) / BN;
-  dim3 grid((unsigned)(m_tiles * n_ntiles)), block(256);
+hipError_t launch_dq_gemm(ProjProblem *probs, int count, int epi, hipStream_t stream) {
+  GemmBatch b;
+  b.count = 0;
+  long total = 0;
+  for (int i = 0; i < count; ++i) {
+    ProjProblem p = probs[i];
+    if (p.n_rows <= 0) continue;
+    long m_tiles;
+    if (p.known_rows >= 0) {
+      if (p.known_rows < p.min_rows || p.known_rows < 1) continue;
+      m_tiles = (p.known_rows + BM - 1) / BM;
+    } else {
+      // sum over big experts of ceil(rows/BM) <= n_rows/BM + (number of big experts)
+      const int min_rows = p.min_rows < 1 ? 1 : p.min_rows;
+      long big = p.n_rows / min_rows;
+      if (big > p.n_experts) big = p.n_experts;
+      m_tiles = (p.n_rows + BM - 1) / BM + big;
+    }
+    p.n_tiles = (epi == EPI_SWIGLU) ? (p.n_out + 63) / 64 : (p.n_out + BN - 1) / BN;
+    p.blocks = (int)(m_tiles * p.n_tiles);
+    total += p.blocks;
+    b.p[b.count++] = p;
+  }
+  if (b.count == 0) return hipSuccess;
+  if (b.count == 1) b.p[1] = b.p[0];
+  dim3 grid((unsigned)total), block(256);
   switch (epi) {
-    case EPI_F32: hipLaunchKernelGGL(k_dq_gemm<EPI_F32>, grid, block, 0, stream, g, n_ntiles); break;
-    case EPI_RELU2: hipLaunchKernelGGL(k_dq_gemm<EPI_RELU2>, grid, block, 0, stream, g, n_ntiles); break;
-    default: hipLaunchKernelGGL(k_dq_gemm<EPI_SWIGLU>, grid, block, 0, stream, g, n_ntiles); break;
+    case EPI_F32: hipLaunchKernelGGL(k_dq_gemm<EPI_F32>, grid, block, 0, stream, b); break;
+    case EPI_RELU2: hipLaunchKernelGGL(k_dq_gemm<EPI_RELU2>, grid, block, 0, stream, b); break;
+    default: hipLaunchKernelGGL(k_dq_gemm<EPI_SWIGLU>, grid, block, 0, stream, b); break;
   }
   return hipGetLastError();
 }

@@ -4,21 +4,29 @@
 // inputs).  Rows inside an expert's group are in ascending token order.
 //
 // Layout without order-dependent atomics: a bitmap bit[e][t] marks that token t
-// picked expert e (atomicOr: the result does not depend on the order), the
-// per-expert prefix popcounts of the bitmap give every pick its rank among the
-// expert's earlier tokens, and an exclusive scan of the counts gives the group
-// offsets.  The whole layout runs in one workgroup; for small problems the
-// bitmap lives in LDS and the row copy is done by the same workgroup.
+// picked expert e (atomicOr: the result does not depend on the order), prefix
+// popcounts of the bitmap give every pick its rank among the expert's earlier
+// tokens, and an exclusive scan of the counts gives the group offsets.
+//
+// Small problems (decode) run in ONE workgroup with the bitmap in LDS, the row
+// copy included, and optionally the top-K routing of every token in front of
+// it (one launch for route + gather).  Large problems (prefill) use three
+// launches: per-256-token chunk bitmaps and counts, then placement with the
+// offsets recomputed per workgroup from the count table, then the row copy.
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
+#include "route_device.hpp"
 
 namespace moe {
 
 namespace {
 
-constexpr int kLayoutThreads = 1024;
-constexpr int kLdsWords = 4096;             // bitmap + prefix words kept in LDS (32 KB)
-constexpr long kInlineCopyBytes = 1 << 18;  // copy inside the layout kernel below this
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallWords = 4096;  // LDS bitmap words (16 KB) for the one-workgroup path
+constexpr int kSmallPicks = 4096;
+constexpr long kSmallCopyBytes = 1L << 21;
+constexpr int kChunkTokens = 256;  // tokens per chunk on the multi-workgroup path
+constexpr int kChunkWords = kChunkTokens / 32;
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
@@ -29,8 +37,8 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-__device__ __forceinline__ void copy_rows(const void *x, int row_bytes, const int32_t *row_token,
-                                          long R, void *xg, long tid, long nthreads) {
+__device__ __forceinline__ void copy_rows(const void *x, int row_bytes, const int32_t *row_token, long R,
+                                          void *xg, long tid, long nthreads) {
   const int chunks = row_bytes / 16;
   const long total = R * chunks;
   for (long i = tid; i < total; i += nthreads) {
@@ -44,50 +52,62 @@ __device__ __forceinline__ void copy_rows(const void *x, int row_bytes, const in
   }
 }
 
-__global__ void __launch_bounds__(kLayoutThreads)
-k_gather_layout(const int32_t *__restrict__ ids, int n, int K, int E, int32_t *__restrict__ offsets,
-                int32_t *__restrict__ row_token, int32_t *__restrict__ rows, uint32_t *ws_bitmap,
-                uint32_t *ws_prefix, int use_lds, const void *x, int row_bytes, void *xg,
-                int inline_copy) {
+// One workgroup: [routing of every token ->] bitmap in LDS -> ranks -> offsets
+// -> placement -> row copy.  Only __syncthreads between phases: every phase
+// reads LDS or global memory written by this workgroup's earlier phases
+// through the same CU.
+template <bool ROUTE>
+__global__ void __launch_bounds__(kSmallThreads)
+k_gather_small(const float *__restrict__ logits, float *__restrict__ topk_w, int32_t *ids, int n, int K, int E,
+               int32_t *__restrict__ offsets, int32_t *__restrict__ row_token, int32_t *__restrict__ rows,
+               const void *x, int row_bytes, void *xg) {
+  __shared__ uint32_t s_bits[kSmallWords];
+  __shared__ int32_t s_ids[kSmallPicks];
   __shared__ int32_t s_count[MOE_MAX_EXPERTS + 1];
   __shared__ int32_t s_off[MOE_MAX_EXPERTS + 1];
-  __shared__ uint32_t s_words[kLdsWords];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
   const int W = (n + 31) >> 5;
-  const long picks = (long)n * K;
-  uint32_t *bitmap = use_lds ? s_words : ws_bitmap;
-  uint32_t *prefix = use_lds ? s_words + (size_t)E * W : ws_prefix;
+  const int picks = n * K;
+  uint32_t *bits = s_bits;
+  uint32_t *prefix = s_bits + E * W;
 
-  // phase 0: clear the bitmap
-  for (long i = tid; i < (long)E * W; i += blockDim.x) bitmap[i] = 0u;
-  __threadfence();
-  __syncthreads();
-
-  // phase 1: mark (expert, token) pairs; invalid ids are dropped
-  for (long p = tid; p < picks; p += blockDim.x) {
-    int e = ids[p];
-    int t = (int)(p / K);
-    if (e >= 0 && e < E) atomicOr(&bitmap[(size_t)e * W + (t >> 5)], 1u << (t & 31));
+  for (int i = tid; i < E * W; i += blockDim.x) bits[i] = 0u;
+  if (ROUTE) {
+    for (int t = wave; t < n; t += nwaves) {
+      int my_id;
+      float my_w;
+      route_one_token(logits + (size_t)t * E, E, K, lane, my_id, my_w);
+      if (lane < K) {
+        ids[(size_t)t * K + lane] = my_id;
+        topk_w[(size_t)t * K + lane] = my_w;
+        s_ids[t * K + lane] = my_id;
+      }
+    }
+  } else {
+    for (int p = tid; p < picks; p += blockDim.x) s_ids[p] = ids[p];
   }
-  __threadfence();
   __syncthreads();
 
-  // phase 2: per expert, exclusive prefix popcount over its bitmap words
+  for (int p = tid; p < picks; p += blockDim.x) {
+    int e = s_ids[p];
+    int t = p / K;
+    if (e >= 0 && e < E) atomicOr(&bits[e * W + (t >> 5)], 1u << (t & 31));
+  }
+  __syncthreads();
+
   for (int e = wave; e < E; e += nwaves) {
     int running = 0;
     for (int w0 = 0; w0 < W; w0 += 64) {
       int w = w0 + lane;
-      int c = (w < W) ? __popc(bitmap[(size_t)e * W + w]) : 0;
+      int c = (w < W) ? __popc(bits[e * W + w]) : 0;
       int incl = wave_incl_scan(c, lane);
-      if (w < W) prefix[(size_t)e * W + w] = running + incl - c;
+      if (w < W) prefix[e * W + w] = running + incl - c;
       running += __shfl(incl, 63, 64);
     }
     if (lane == 0) s_count[e] = running;
   }
-  __threadfence();
   __syncthreads();
 
-  // phase 3: exclusive scan of the counts -> group offsets
   if (wave == 0) {
     int running = 0;
     for (int e0 = 0; e0 < E; e0 += 64) {
@@ -102,64 +122,186 @@ k_gather_layout(const int32_t *__restrict__ ids, int n, int K, int E, int32_t *_
   __syncthreads();
   for (int e = tid; e <= E; e += blockDim.x) offsets[e] = s_off[e];
 
-  // phase 4: place every pick
-  for (long p = tid; p < picks; p += blockDim.x) {
-    int e = ids[p];
-    int t = (int)(p / K);
+  for (int p = tid; p < picks; p += blockDim.x) {
+    int e = s_ids[p];
+    int t = p / K;
     int32_t r = -1;
     if (e >= 0 && e < E) {
-      size_t wi = (size_t)e * W + (t >> 5);
-      uint32_t below = bitmap[wi] & ((1u << (t & 31)) - 1u);
-      r = s_off[e] + (int32_t)prefix[wi] + __popc(below);
+      int wi = e * W + (t >> 5);
+      r = s_off[e] + (int32_t)prefix[wi] + __popc(bits[wi] & ((1u << (t & 31)) - 1u));
       row_token[r] = t;
     }
     rows[p] = r;
   }
-  for (long r = s_off[E] + tid; r < picks; r += blockDim.x) row_token[r] = -1;
+  for (int r = s_off[E] + tid; r < picks; r += blockDim.x) row_token[r] = -1;
+  __syncthreads();  // row_token written above is read back by other threads of this workgroup
+  copy_rows(x, row_bytes, row_token, picks, xg, tid, blockDim.x);
+}
 
-  if (inline_copy) {
-    __threadfence();
-    __syncthreads();
-    copy_rows(x, row_bytes, row_token, picks, xg, tid, blockDim.x);
+// Multi-workgroup path, launch 1: chunk c covers tokens [256c, 256c+256): its
+// bitmap words for every expert and its per-expert pick counts.
+__global__ void __launch_bounds__(256)
+k_gather_bits(const int32_t *__restrict__ ids, int n, int K, int E, int W, uint32_t *__restrict__ bitmap,
+              int32_t *__restrict__ chunk_count, int n_chunks) {
+  __shared__ uint32_t s_bits[MOE_MAX_EXPERTS * kChunkWords];
+  const int c = blockIdx.x, tid = threadIdx.x;
+  const int t0 = c * kChunkTokens;
+  const int t1 = min(n, t0 + kChunkTokens);
+  for (int i = tid; i < E * kChunkWords; i += blockDim.x) s_bits[i] = 0u;
+  __syncthreads();
+  for (long p = (long)t0 * K + tid; p < (long)t1 * K; p += blockDim.x) {
+    int e = ids[p];
+    int t = (int)(p / K) - t0;
+    if (e >= 0 && e < E) atomicOr(&s_bits[e * kChunkWords + (t >> 5)], 1u << (t & 31));
+  }
+  __syncthreads();
+  const int w0 = c * kChunkWords;
+  for (int i = tid; i < E * kChunkWords; i += blockDim.x) {
+    int e = i / kChunkWords, wl = i - e * kChunkWords;
+    if (w0 + wl < W) bitmap[(size_t)e * W + w0 + wl] = s_bits[i];
+  }
+  for (int e = tid; e < E; e += blockDim.x) {
+    int cnt = 0;
+#pragma unroll
+    for (int wl = 0; wl < kChunkWords; ++wl) cnt += __popc(s_bits[e * kChunkWords + wl]);
+    chunk_count[(size_t)e * n_chunks + c] = cnt;
   }
 }
 
+// Launch 2: per chunk, offsets and the chunk's base per expert from the count
+// table (each workgroup recomputes them; workgroup 0 also writes offsets),
+// then every pick of the chunk gets its row.
 __global__ void __launch_bounds__(256)
-k_gather_copy(const void *__restrict__ x, int row_bytes, const int32_t *__restrict__ row_token,
-              long R, void *__restrict__ xg) {
+k_gather_place(const int32_t *__restrict__ ids, int n, int K, int E, int W,
+               const uint32_t *__restrict__ bitmap, const int32_t *__restrict__ chunk_count, int n_chunks,
+               int32_t *__restrict__ offsets, int32_t *__restrict__ row_token, int32_t *__restrict__ rows) {
+  __shared__ int32_t s_total[MOE_MAX_EXPERTS];
+  __shared__ int32_t s_base[MOE_MAX_EXPERTS + 1];
+  __shared__ uint32_t s_bits[MOE_MAX_EXPERTS * kChunkWords];
+  __shared__ int32_t s_wave_sum[4];
+  const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = c * kChunkTokens;
+  const int t1 = min(n, t0 + kChunkTokens);
+  for (int e = tid; e < E; e += blockDim.x) {
+    const int32_t *row = chunk_count + (size_t)e * n_chunks;
+    int pre = 0, tot = 0;
+    for (int cc = 0; cc < n_chunks; ++cc) {
+      int v = row[cc];
+      tot += v;
+      if (cc < c) pre += v;
+    }
+    s_total[e] = tot;
+    s_base[e] = pre;
+  }
+  const int w0 = c * kChunkWords;
+  for (int i = tid; i < E * kChunkWords; i += blockDim.x) {
+    int e = i / kChunkWords, wl = i - e * kChunkWords;
+    s_bits[i] = (w0 + wl < W) ? bitmap[(size_t)e * W + w0 + wl] : 0u;
+  }
+  __syncthreads();
+  // exclusive scan of s_total over experts: 4 waves x 64 lanes, E <= 1024
+  int run = 0;
+  if (tid == 0) s_base[E] = 0;
+  for (int e0 = 0; e0 < E; e0 += 256) {
+    int e = e0 + tid;
+    int v = (e < E) ? s_total[e] : 0;
+    int incl = wave_incl_scan(v, lane);
+    if (lane == 63) s_wave_sum[wave] = incl;
+    __syncthreads();
+    int before = run;
+    for (int w = 0; w < wave; ++w) before += s_wave_sum[w];
+    int excl = before + incl - v;
+    int chunk_sum = s_wave_sum[0] + s_wave_sum[1] + s_wave_sum[2] + s_wave_sum[3];
+    __syncthreads();
+    if (e < E) {
+      if (c == 0) offsets[e] = excl;
+      s_base[e] += excl;  // = offsets[e] + picks of e in earlier chunks
+    }
+    run += chunk_sum;
+  }
+  if (c == 0 && tid == 0) offsets[E] = run;
+  __syncthreads();
+  for (long p = (long)t0 * K + tid; p < (long)t1 * K; p += blockDim.x) {
+    int e = ids[p];
+    int t = (int)(p / K);
+    int32_t r = -1;
+    if (e >= 0 && e < E) {
+      int tl = t - t0;
+      int wl = tl >> 5;
+      int below = 0;
+      for (int ww = 0; ww < wl; ++ww) below += __popc(s_bits[e * kChunkWords + ww]);
+      below += __popc(s_bits[e * kChunkWords + wl] & ((1u << (tl & 31)) - 1u));
+      r = s_base[e] + below;
+      row_token[r] = t;
+    }
+    rows[p] = r;
+  }
+  // rows past the valid picks (only when ids were dropped)
+  const long picks = (long)n * K;
+  for (long r = run + (long)c * blockDim.x + tid; r < picks; r += (long)n_chunks * blockDim.x) row_token[r] = -1;
+}
+
+__global__ void __launch_bounds__(256)
+k_gather_copy(const void *__restrict__ x, int row_bytes, const int32_t *__restrict__ row_token, long R,
+              void *__restrict__ xg) {
   long tid = (long)blockIdx.x * blockDim.x + threadIdx.x;
   copy_rows(x, row_bytes, row_token, R, xg, tid, (long)gridDim.x * blockDim.x);
+}
+
+bool small_path(int n, int K, int E, long row_bytes) {
+  long W = ((long)n + 31) / 32;
+  return 2 * (long)E * W <= kSmallWords && (long)n * K <= kSmallPicks &&
+         (long)n * K * row_bytes <= kSmallCopyBytes;
 }
 
 }  // namespace
 
 size_t gather_workspace_bytes(int n_tokens, int n_experts) {
   size_t W = ((size_t)n_tokens + 31) / 32;
-  size_t words = (size_t)n_experts * W;
-  return 2 * words * sizeof(uint32_t) + 256;
+  size_t n_chunks = ((size_t)n_tokens + kChunkTokens - 1) / kChunkTokens;
+  return (size_t)n_experts * W * sizeof(uint32_t) + (size_t)n_experts * n_chunks * sizeof(int32_t) + 512;
 }
 
-hipError_t launch_gather(const void *x, int elem_bytes, int n_tokens, int d_model, const int32_t *ids,
-                         int top_k, int n_experts, void *xg, int32_t *offsets, int32_t *row_token,
-                         int32_t *rows, void *workspace, hipStream_t stream) {
-  size_t W = ((size_t)n_tokens + 31) / 32;
-  size_t words = (size_t)n_experts * W;
-  int use_lds = (2 * words <= (size_t)kLdsWords) ? 1 : 0;
+bool gather_is_single_launch(int n_tokens, int top_k, int n_experts, int elem_bytes, int d_model) {
+  return small_path(n_tokens, top_k, n_experts, (long)elem_bytes * d_model);
+}
+
+hipError_t launch_gather(const void *x, int elem_bytes, int n_tokens, int d_model, const int32_t *ids, int top_k,
+                         int n_experts, void *xg, int32_t *offsets, int32_t *row_token, int32_t *rows,
+                         void *workspace, hipStream_t stream) {
+  const int row_bytes = elem_bytes * d_model;
+  if (small_path(n_tokens, top_k, n_experts, row_bytes)) {
+    hipLaunchKernelGGL(k_gather_small<false>, dim3(1), dim3(kSmallThreads), 0, stream, nullptr, nullptr,
+                       const_cast<int32_t *>(ids), n_tokens, top_k, n_experts, offsets, row_token, rows, x,
+                       row_bytes, xg);
+    return hipGetLastError();
+  }
+  const int W = (n_tokens + 31) / 32;
+  const int n_chunks = (n_tokens + kChunkTokens - 1) / kChunkTokens;
   uint32_t *bitmap = (uint32_t *)workspace;
-  uint32_t *prefix = bitmap + words;
-  int row_bytes = elem_bytes * d_model;
-  long R = (long)n_tokens * top_k;
-  int inline_copy = (R * row_bytes <= kInlineCopyBytes) ? 1 : 0;
-  hipLaunchKernelGGL(k_gather_layout, dim3(1), dim3(kLayoutThreads), 0, stream, ids, n_tokens, top_k,
-                     n_experts, offsets, row_token, rows, bitmap, prefix, use_lds, x, row_bytes, xg,
-                     inline_copy);
+  int32_t *chunk_count = (int32_t *)(bitmap + (size_t)n_experts * W);
+  hipLaunchKernelGGL(k_gather_bits, dim3(n_chunks), dim3(256), 0, stream, ids, n_tokens, top_k, n_experts, W, bitmap,
+                     chunk_count, n_chunks);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || inline_copy) return err;
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_gather_place, dim3(n_chunks), dim3(256), 0, stream, ids, n_tokens, top_k, n_experts, W,
+                     bitmap, chunk_count, n_chunks, offsets, row_token, rows);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  long R = (long)n_tokens * top_k;
   long chunks = R * (row_bytes / 16);
   long blocks = (chunks + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(k_gather_copy, dim3((unsigned)blocks), dim3(256), 0, stream, x, row_bytes, row_token,
-                     R, xg);
+  if (blocks > 16384) blocks = 16384;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_gather_copy, dim3((unsigned)blocks), dim3(256), 0, stream, x, row_bytes, row_token, R, xg);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_gather_small(const float *logits, int n_tokens, int n_experts, int top_k, int32_t *ids,
+                                     float *weights, const void *x, int elem_bytes, int d_model, void *xg,
+                                     int32_t *offsets, int32_t *row_token, int32_t *rows, hipStream_t stream) {
+  hipLaunchKernelGGL(k_gather_small<true>, dim3(1), dim3(kSmallThreads), 0, stream, logits, weights, ids, n_tokens,
+                     top_k, n_experts, offsets, row_token, rows, x, elem_bytes * d_model, xg);
   return hipGetLastError();
 }
 

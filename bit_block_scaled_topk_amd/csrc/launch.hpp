@@ -14,8 +14,14 @@ namespace moe {
 hipError_t launch_route_topk(const float *logits, int n_tokens, int n_experts, int top_k,
                              int32_t *ids, float *weights, hipStream_t stream);
 
-// Gather: bitmap layout (one workgroup) + row copy.
+// Gather: bitmap layout + row copy (one workgroup for small problems).
 size_t gather_workspace_bytes(int n_tokens, int n_experts);
+bool gather_is_single_launch(int n_tokens, int top_k, int n_experts, int elem_bytes, int d_model);
+// Routing of every token and the whole gather in one workgroup (requires
+// gather_is_single_launch).
+hipError_t launch_route_gather_small(const float *logits, int n_tokens, int n_experts, int top_k, int32_t *ids,
+                                     float *weights, const void *x, int elem_bytes, int d_model, void *xg,
+                                     int32_t *offsets, int32_t *row_token, int32_t *rows, hipStream_t stream);
 hipError_t launch_gather(const void *x, int elem_bytes, int n_tokens, int d_model,
                          const int32_t *ids, int top_k, int n_experts, void *xg,
                          int32_t *offsets, int32_t *row_token, int32_t *rows, void *workspace,
@@ -38,20 +44,36 @@ enum Epilogue : int {
 // fp32 activations -> three bf16 planes hi, mid, lo (plane stride `plane`).
 hipError_t launch_split3(const float *a, long n_elems, uint16_t *planes, long plane, hipStream_t stream);
 
-// Decode path over experts with 1..max_rows rows (at most max_active of them):
-// activations are nt bf16 planes; EPI_F32 writes out_f32, the activation
-// epilogues write h as three bf16 planes (hi, mid, lo) with plane stride h_plane.
-hipError_t launch_dq_gemv_planes(const uint16_t *a, int nt, long plane, long lda, const int32_t *offsets,
-                                 int n_experts, int n_rows, int max_rows, int max_active, const uint8_t *codes,
-                                 const uint8_t *scales, const float *global, int n_w, int k, int n_out,
-                                 int epi, float *out_f32, uint16_t *out_h, long ldo, long h_plane,
-                                 hipStream_t stream);
+// One grouped NVFP4 projection handled by the decode or prefill kernels.
+struct ProjProblem {
+  const uint16_t *a;      // bf16 activations: nt planes of [n_rows][lda] (plane stride `plane`)
+  long plane;
+  long lda;
+  const int32_t *offsets; // [n_experts + 1] device (unused when known_rows >= 0)
+  int n_experts;
+  int n_rows;             // rows of a / out
+  int known_rows;         // >= 0: one expert, rows [0, known_rows) known on the host
+  int min_rows, max_rows; // experts with min_rows..max_rows rows are handled
+  const uint8_t *codes;   // [n_experts][n_w][k/2]
+  const uint8_t *scales;  // [n_experts][n_w][k/16]
+  const float *global;    // [n_experts]
+  int n_w, k, n_out;
+  float *out_f32;         // EPI_F32 output [n_rows][ldo]
+  uint16_t *out_h;        // activation epilogues: bf16 h (3 planes on the decode path)
+  long ldo;
+  long h_plane;
+  // filled by the launchers
+  int n_tiles;            // output-column tiles
+  int blocks;             // workgroups of this problem
+};
 
-// Prefill path over experts with at least min_rows rows: bf16 activations;
-// EPI_F32 writes out_f32, the activation epilogues write bf16 h.
-hipError_t launch_dq_gemm(const uint16_t *a, long lda, const int32_t *offsets, int n_experts,
-                          int min_rows, long n_rows, const uint8_t *codes, const uint8_t *scales,
-                          const float *global, int n_w, int k, int n_out, int epi, float *out_f32,
-                          uint16_t *out_h, long ldo, hipStream_t stream);
+// Decode path: up to two problems in one launch (e.g. the shared and the routed
+// experts).  Both use the same epilogue and activation planes nt; max_active
+// bounds the experts with 1..max_rows rows of each problem.
+hipError_t launch_dq_gemv(ProjProblem *probs, const int *max_active, int count, int nt, int epi,
+                          hipStream_t stream);
+
+// Prefill path: up to two problems in one launch; bf16 activations (plane 0).
+hipError_t launch_dq_gemm(ProjProblem *probs, int count, int epi, hipStream_t stream);
 
 }  // namespace moe

@@ -35,10 +35,18 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   return __uint_as_float(__float_as_uint(mag) | s);
 }
 
+// The two e4m3 block scales of one 32-element group (low byte = first block),
+// decoded with the OCP FP8 converter (unit scale: exact).
+__device__ __forceinline__ void e4m3x2_to_f32(uint32_t two, float &s0, float &s1) {
+  s0 = __builtin_amdgcn_cvt_scalef32_f32_fp8(two, 1.0f, 0);
+  s1 = __builtin_amdgcn_cvt_scalef32_f32_fp8(two, 1.0f, 1);
+}
+
 // Decode 8 codes (one 32-bit word, element 0 in the low nibble of byte 0) into
 // 8 bf16 values scale * e2m1, packed as 4 x (even element in the low half).
-// Every product is exact in f32 and in bf16 (<= 6 significant bits, within the
-// normal range), so taking the upper 16 bits of the f32 is the exact bf16.
+// The FP4 converter (unit scale) gives exact e2m1 values; every product with
+// the e4m3 scale is exact in f32 and in bf16 (<= 6 significant bits, inside the
+// normal range), so the upper 16 bits of the f32 are the exact bf16.
 __device__ __forceinline__ u32x4_t dq8_bf16(uint32_t w, float scale) {
   u32x4_t r;
 #pragma unroll
@@ -50,9 +58,9 @@ __device__ __forceinline__ u32x4_t dq8_bf16(uint32_t w, float scale) {
       case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); break;
       default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); break;
     }
-    uint32_t lo = __float_as_uint(v.x * scale);
-    uint32_t hi = __float_as_uint(v.y * scale);
-    r[j] = (lo >> 16) | (hi & 0xFFFF0000u);  // {hi[31:16], lo[31:16]}
+    const uint32_t lo = __float_as_uint(v.x * scale);
+    const uint32_t hi = __float_as_uint(v.y * scale);
+    r[j] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);  // {hi[31:16], lo[31:16]}
   }
   return r;
 }

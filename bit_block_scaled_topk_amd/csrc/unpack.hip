@@ -19,8 +19,8 @@ k_unpack_bf16(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ sca
   int g = (int)(gid - r * gpr);
   u32x4_t c = *(const u32x4_t *)(codes + (size_t)r * (cols / 2) + (size_t)g * 16);
   const uint8_t *sp = scales + (size_t)r * (cols / 16) + (size_t)g * 2;
-  float s0 = e4m3_to_f32(sp[0]);
-  float s1 = e4m3_to_f32(sp[1]);
+  float s0, s1;
+  e4m3x2_to_f32((uint32_t)sp[0] | ((uint32_t)sp[1] << 8), s0, s1);
   u32x4_t *o = (u32x4_t *)(out + (size_t)r * cols + (size_t)g * 32);
   o[0] = dq8_bf16(c[0], s0);
   o[1] = dq8_bf16(c[1], s0);

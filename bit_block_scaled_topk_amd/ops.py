@@ -70,10 +70,35 @@ _lib.nvfp4_grouped_linear.argtypes = [_P, _I, _I, _I, _P, _I, ctypes.POINTER(NVF
                                       _P, _P]
 _lib.nvfp4_grouped_linear.restype = _I
 
+class LayerDesc(ctypes.Structure):
+    """moe_layer_desc."""
+    _fields_ = [("n_tokens", ctypes.c_int), ("d_model", ctypes.c_int), ("n_experts", ctypes.c_int),
+                ("top_k", ctypes.c_int), ("x_dtype", ctypes.c_int), ("act", ctypes.c_int),
+                ("gemv_max_rows", ctypes.c_int), ("up", NVFP4Weights), ("down", NVFP4Weights),
+                ("shared_up", NVFP4Weights), ("shared_down", NVFP4Weights)]
+
+
+class LayerViews(ctypes.Structure):
+    """moe_layer_views."""
+    _fields_ = [("topk_ids", ctypes.c_void_p), ("topk_weights", ctypes.c_void_p),
+                ("expert_offsets", ctypes.c_void_p), ("row_token", ctypes.c_void_p), ("rows", ctypes.c_void_p),
+                ("xg", ctypes.c_void_p), ("yg", ctypes.c_void_p)]
+
+
+_lib.moe_layer_workspace_size.argtypes = [ctypes.POINTER(LayerDesc)]
+_lib.moe_layer_workspace_size.restype = _SZ
+_lib.moe_layer_get_views.argtypes = [ctypes.POINTER(LayerDesc), _P, ctypes.POINTER(LayerViews)]
+_lib.moe_layer_get_views.restype = _I
+_lib.moe_layer_forward.argtypes = [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _SZ, _P]
+_lib.moe_layer_forward.restype = _I
+_lib.moe_layer_forward_profiled.argtypes = [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _SZ, _P, _P]
+_lib.moe_layer_forward_profiled.restype = _I
+
 EXPORTED = ("moe_route_topk", "moe_gather_workspace_size", "moe_gather_rows",
             "nvfp4_expert_ffn_workspace_size", "nvfp4_grouped_linear_workspace_size",
             "nvfp4_expert_ffn", "moe_weighted_row_sum", "moe_weighted_row_sum_into", "nvfp4_unpack_bf16",
-            "nvfp4_grouped_linear", "moe_status_string")
+            "nvfp4_grouped_linear", "moe_status_string", "moe_layer_workspace_size", "moe_layer_get_views",
+            "moe_layer_forward", "moe_layer_forward_profiled")
 
 
 def _check(fn: str, st: int):
@@ -223,6 +248,66 @@ def nvfp4_grouped_linear(a: torch.Tensor, offsets: torch.Tensor, w: DeviceNVFP4,
     return out
 
 
+def moe_layer_workspace_size(desc: LayerDesc) -> int:
+    return int(_lib.moe_layer_workspace_size(ctypes.byref(desc)))
+
+
+def moe_layer_get_views(desc: LayerDesc, workspace: torch.Tensor) -> LayerViews:
+    v = LayerViews()
+    _check("moe_layer_get_views", _lib.moe_layer_get_views(ctypes.byref(desc), _ptr(workspace), ctypes.byref(v)))
+    return v
+
+
+def moe_layer_forward(desc: LayerDesc, x: torch.Tensor, logits: torch.Tensor, out: torch.Tensor,
+                      workspace: torch.Tensor, stream=None) -> torch.Tensor:
+    _check("moe_layer_forward", _lib.moe_layer_forward(
+        ctypes.byref(desc), _ptr(x), _ptr(logits), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def moe_layer_forward_profiled(desc: LayerDesc, x: torch.Tensor, logits: torch.Tensor, out: torch.Tensor,
+                               workspace: torch.Tensor, events, stream=None) -> torch.Tensor:
+    """``events``: a ctypes array of 6 hipEvent_t handles (see HipEvents)."""
+    _check("moe_layer_forward_profiled", _lib.moe_layer_forward_profiled(
+        ctypes.byref(desc), _ptr(x), _ptr(logits), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), events, _stream(stream)))
+    return out
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch already loaded (for the
+    profiled layer entry point); elapsed times in milliseconds."""
+
+    def __init__(self, count: int):
+        self._hip = ctypes.CDLL("libamdhip64.so.7", mode=ctypes.RTLD_GLOBAL)
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                  ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.handles = (ctypes.c_void_p * count)()
+        for i in range(count):
+            h = ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles[i] = h
+
+    def slice(self, start: int):
+        return ctypes.cast(ctypes.byref(self.handles, start * ctypes.sizeof(ctypes.c_void_p)),
+                           ctypes.c_void_p)
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.handles[a], self.handles[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self):
+        for h in self.handles:
+            self._hip.hipEventDestroy(h)
+        self.handles = (ctypes.c_void_p * 0)()
+
+
 def status_string(status: int) -> str:
     return _lib.moe_status_string(status).decode()
 
@@ -251,6 +336,7 @@ class MoELayer:
         self.shared_up = DeviceNVFP4.from_host(inp.shared_up, device) if inp.fs > 0 else None
         self.shared_down = DeviceNVFP4.from_host(inp.shared_down, device) if inp.fs > 0 else None
         self.device = device
+        self.layer_ws = None
         self._alloc(self.n)
 
     def _alloc(self, n):
@@ -270,9 +356,52 @@ class MoELayer:
                  nvfp4_expert_ffn_workspace_size(R, d, self.f, self.x_dtype),
                  nvfp4_expert_ffn_workspace_size(n, d, max(self.fs, 32), self.x_dtype))
         self.workspace = torch.empty((ws,), dtype=torch.uint8, device=dev)
+        self.layer_ws = torch.empty((moe_layer_workspace_size(self.desc(None, n)),), dtype=torch.uint8, device=dev)
 
     def weights(self):
         return (self.up, self.down, self.shared_up, self.shared_down)
+
+    def desc(self, weights=None, n_tokens: Optional[int] = None) -> LayerDesc:
+        up, down, sup, sdn = weights if weights is not None else self.weights()
+        empty = NVFP4Weights(None, None, None, 0, 0)
+        return LayerDesc(self.n if n_tokens is None else n_tokens, self.d, self.E, self.K, self.x_dtype, self.act,
+                         self.gemv_max_rows, up.struct(), down.struct(),
+                         sup.struct() if sup is not None else empty, sdn.struct() if sdn is not None else empty)
+
+    def forward_fused(self, x: torch.Tensor, logits: torch.Tensor, stream=None, weights=None) -> torch.Tensor:
+        """The whole layer through moe_layer_forward (the fewest launches);
+        intermediates stay in the layer workspace (see views())."""
+        d = self.desc(weights, x.shape[0])
+        need = moe_layer_workspace_size(d)
+        if self.layer_ws is None or self.layer_ws.numel() < need:
+            raise MoeError("moe_layer_forward", MOE_WORKSPACE_TOO_SMALL)
+        return moe_layer_forward(d, x, logits, self.out, self.layer_ws, stream=stream)
+
+    def forward_profiled(self, x: torch.Tensor, logits: torch.Tensor, events, stream=None,
+                         weights=None) -> torch.Tensor:
+        d = self.desc(weights, x.shape[0])
+        return moe_layer_forward_profiled(d, x, logits, self.out, self.layer_ws, events, stream=stream)
+
+    def views(self, n_tokens: Optional[int] = None) -> dict:
+        """The fused path's intermediates as tensors viewing the workspace."""
+        n = self.n if n_tokens is None else n_tokens
+        v = moe_layer_get_views(self.desc(None, n), self.layer_ws)
+        base = self.layer_ws.data_ptr()
+        R = n * self.K
+
+        def view(addr, numel, dtype):
+            off = addr - base
+            esz = torch.tensor([], dtype=dtype).element_size()
+            return self.layer_ws[off:off + numel * esz].view(dtype)
+
+        xdt = torch.float32 if self.x_dtype == MOE_F32 else torch.int16
+        return dict(ids=view(v.topk_ids, R, torch.int32).view(n, self.K),
+                    w=view(v.topk_weights, R, torch.float32).view(n, self.K),
+                    offsets=view(v.expert_offsets, self.E + 1, torch.int32),
+                    row_token=view(v.row_token, R, torch.int32),
+                    rows=view(v.rows, R, torch.int32).view(n, self.K),
+                    xg=view(v.xg, R * self.d, xdt).view(R, self.d),
+                    yg=view(v.yg, R * self.d, torch.float32).view(R, self.d))
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor, stream=None, weights=None,
                 timing: Optional[dict] = None) -> torch.Tensor:

@@ -209,6 +209,66 @@ moe_status nvfp4_grouped_linear(const void *a, moe_dtype a_dtype, int n_rows,
                                 void *workspace, size_t ws_bytes, float *out,
                                 hipStream_t stream);
 
+/* ------------------------------------------------------------------------- */
+/* The whole layer in the fewest launches                                     */
+/* ------------------------------------------------------------------------- */
+
+/* Shapes and weights of one MoE layer.  The shared expert is optional
+ * (shared_up.codes == NULL: none, so the output is the routed sum alone); it
+ * always uses relu^2, the routed experts use `act`. */
+typedef struct {
+  int n_tokens;               /* n */
+  int d_model;                /* d: columns of x, up.cols, down.rows */
+  int n_experts;              /* routed experts E */
+  int top_k;                  /* K */
+  moe_dtype x_dtype;          /* activations */
+  moe_act act;                /* routed experts' activation */
+  int gemv_max_rows;          /* 0..32, as in nvfp4_expert_ffn */
+  moe_nvfp4_weights up, down; /* routed: [E][f or 2f][d], [E][d][f] */
+  moe_nvfp4_weights shared_up, shared_down; /* [1][fs][d], [1][d][fs] */
+} moe_layer_desc;
+
+/* Device pointers into a layer workspace where moe_layer_forward leaves the
+ * intermediates of its last call (for inspection; computed on the host). */
+typedef struct {
+  int32_t *topk_ids;       /* [n][K] */
+  float *topk_weights;     /* [n][K] */
+  int32_t *expert_offsets; /* [E+1] */
+  int32_t *row_token;      /* [n*K] */
+  int32_t *rows;           /* [n][K] */
+  void *xg;                /* [n*K][d] of x_dtype */
+  float *yg;               /* [n*K][d]: each routed expert's output rows */
+} moe_layer_views;
+
+/* Workspace bytes moe_layer_forward needs (0 for an invalid description). */
+size_t moe_layer_workspace_size(const moe_layer_desc *desc);
+
+/* Fill `views` with the intermediates' addresses inside `workspace`. */
+moe_status moe_layer_get_views(const moe_layer_desc *desc, void *workspace, moe_layer_views *views);
+
+/* moe_layer_forward -- route -> gather -> experts -> WeightedRowSum for one
+ * layer (gllm #91 "What changes"), with the same results as the four calls
+ * above made in order, in fewer launches: routing and gather share one
+ * workgroup for small batches, the shared and the routed experts share each
+ * up and each down launch, and nothing synchronises or allocates (Glq v0.2.13
+ * "Remaining gap to bf16-native": fewer launches per layer).
+ *   x       device [n][d] of desc->x_dtype (16-byte aligned)
+ *   logits  device float [n][E]
+ *   out     device float [n][d] (written, not accumulated)
+ *   workspace  device scratch >= moe_layer_workspace_size(desc), 256-byte
+ *           aligned; holds every intermediate (see moe_layer_get_views) */
+moe_status moe_layer_forward(const moe_layer_desc *desc, const void *x, const float *logits, float *out,
+                             void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* moe_layer_forward with timing: events[0..5] (created by the caller, timing
+ * enabled) are recorded on `stream` before routing, after routing + gather,
+ * after the activation split, after the up projections, after the down
+ * projections and after the combine, so each phase's GPU time can be read
+ * with hipEventElapsedTime.  events == NULL records nothing. */
+moe_status moe_layer_forward_profiled(const moe_layer_desc *desc, const void *x, const float *logits,
+                                      float *out, void *workspace, size_t ws_bytes, hipEvent_t *events,
+                                      hipStream_t stream);
+
 /* A short English description of a status code (a static string). */
 const char *moe_status_string(moe_status status);
 

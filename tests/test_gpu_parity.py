@@ -367,3 +367,56 @@ def test_expert_ffn_writes_only_its_rows(ops):
     assert np.all(np.isnan(got[off[-1]:]))
     ref = oracle.expert_ffn(xg[:off[-1]].astype(np.float64), off, inp.up, inp.down, inp.f, "relu2")
     assert normwise(got[:off[-1]], ref) <= TOL_DECODE
+
+
+# ----------------------------------------------------------------------------
+# the fused layer entry point
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny16", "decode1", "decode32_zipf", "gated2", "prefill4314"])
+def test_layer_forward_fused(ops, name):
+    """moe_layer_forward matches the oracle at the path's tolerance, leaves the
+    same intermediates, and gives the same bits as the four calls in order."""
+    inp = cached_layer(name)
+    layer = ops.MoELayer(inp)
+    x, lg = dev(inp.x), dev(inp.logits)
+    fused = layer.forward_fused(x, lg).clone()
+    v = layer.views()
+    torch.cuda.synchronize()
+    ids, w = oracle.route_topk(inp.logits, inp.K)
+    off, row_token, rows = oracle.gather_layout(ids, inp.E)
+    assert np.array_equal(host(v["ids"]), ids)
+    assert np.max(np.abs(host(v["w"]).astype(np.float64) - w)) <= 4e-7
+    assert np.array_equal(host(v["offsets"]), off)
+    assert np.array_equal(host(v["rows"]), rows)
+    assert np.array_equal(host(v["row_token"]), row_token)
+    got = host(fused).astype(np.float64)
+    if name == "prefill4314":
+        tokens = [0, 5, 1234, 4313]
+        ref = oracle.layer_sampled(inp, tokens, ids, w)
+        assert normwise(got[tokens], ref) <= TOL_PREFILL
+    else:
+        ref = oracle.layer(inp)
+        assert normwise(got, ref["out"]) <= TOL_DECODE
+    unfused = layer.forward(x, lg).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(fused, unfused)
+
+
+def test_layer_forward_fused_repeat_and_graph(ops):
+    """Captured in a HIP graph and replayed, the fused layer gives the eager
+    bits on every replay (the layer neither allocates nor synchronises)."""
+    inp = cached_layer("decode32_zipf")
+    layer = ops.MoELayer(inp)
+    x, lg = dev(inp.x), dev(inp.logits)
+    eager = layer.forward_fused(x, lg).clone()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        layer.forward_fused(x, lg)
+    for _ in range(3):
+        layer.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.out, eager)
