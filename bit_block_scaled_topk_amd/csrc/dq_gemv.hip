@@ -32,7 +32,13 @@ namespace moe {
 
 namespace {
 
-constexpr int kNI = 8;  // k-group iterations whose weight loads are in flight per lane
+#ifndef MOE_GEMV_NI
+#define MOE_GEMV_NI 8
+#endif
+#ifndef MOE_GEMV_WAVES
+#define MOE_GEMV_WAVES 4
+#endif
+constexpr int kNI = MOE_GEMV_NI;  // k-group iterations whose weight loads are in flight per lane
 
 struct GemvBatch {
   ProjProblem p[2];
@@ -48,8 +54,9 @@ __device__ __forceinline__ void find_expert(const int32_t *__restrict__ offsets,
   const int q = (E + 63) >> 6;
   const int eb = lane * q;
   int off[kMaxQ + 1];
+  // unpredicated loads of clamped indices: one round trip, no branches
 #pragma unroll
-  for (int i = 0; i <= kMaxQ; ++i) off[i] = (i <= q && eb + i <= E) ? offsets[eb + i] : 0;
+  for (int i = 0; i <= kMaxQ; ++i) off[i] = (i <= q) ? offsets[min(eb + i, E)] : 0;
   int local = 0;
   unsigned valid_mask = 0;
 #pragma unroll
@@ -315,7 +322,7 @@ hipError_t launch_dq_gemv(ProjProblem *probs, const int *max_active, int count, 
   if (b.count == 0) return hipSuccess;
   if (b.count == 1) b.p[1] = b.p[0];
   dim3 grid((unsigned)total);
-  constexpr int W = 4;
+  constexpr int W = MOE_GEMV_WAVES;
   if (rows_bound <= 16) {
     if (nt == 1) return dispatch_epi<W, 1, 1>(b, epi, grid, stream);
     return dispatch_epi<W, 1, 3>(b, epi, grid, stream);

@@ -22,8 +22,8 @@ namespace moe {
 namespace {
 
 constexpr int kSmallThreads = 1024;
-constexpr int kSmallWords = 4096;  // LDS bitmap words (16 KB) for the one-workgroup path
-constexpr int kSmallPicks = 4096;
+constexpr int kSmallWords = 2048;  // LDS bitmap + prefix words (8 KB) for the one-workgroup path
+constexpr int kSmallPicks = 2048;
 constexpr long kSmallCopyBytes = 1L << 21;
 constexpr int kChunkTokens = 256;  // tokens per chunk on the multi-workgroup path
 constexpr int kChunkWords = kChunkTokens / 32;
@@ -63,6 +63,7 @@ k_gather_small(const float *__restrict__ logits, float *__restrict__ topk_w, int
                const void *x, int row_bytes, void *xg) {
   __shared__ uint32_t s_bits[kSmallWords];
   __shared__ int32_t s_ids[kSmallPicks];
+  __shared__ int32_t s_rt[kSmallPicks];
   __shared__ int32_t s_count[MOE_MAX_EXPERTS + 1];
   __shared__ int32_t s_off[MOE_MAX_EXPERTS + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
@@ -76,7 +77,7 @@ k_gather_small(const float *__restrict__ logits, float *__restrict__ topk_w, int
     for (int t = wave; t < n; t += nwaves) {
       int my_id;
       float my_w;
-      route_one_token(logits + (size_t)t * E, E, K, lane, my_id, my_w);
+      route_one_token_any(logits + (size_t)t * E, E, K, lane, my_id, my_w);
       if (lane < K) {
         ids[(size_t)t * K + lane] = my_id;
         topk_w[(size_t)t * K + lane] = my_w;
@@ -130,12 +131,25 @@ k_gather_small(const float *__restrict__ logits, float *__restrict__ topk_w, int
       int wi = e * W + (t >> 5);
       r = s_off[e] + (int32_t)prefix[wi] + __popc(bits[wi] & ((1u << (t & 31)) - 1u));
       row_token[r] = t;
+      s_rt[r] = t;
     }
     rows[p] = r;
   }
-  for (int r = s_off[E] + tid; r < picks; r += blockDim.x) row_token[r] = -1;
-  __syncthreads();  // row_token written above is read back by other threads of this workgroup
-  copy_rows(x, row_bytes, row_token, picks, xg, tid, blockDim.x);
+  for (int r = s_off[E] + tid; r < picks; r += blockDim.x) {
+    row_token[r] = -1;
+    s_rt[r] = -1;
+  }
+  __syncthreads();
+  // row copy from the LDS copy of row_token
+  const int chunks = row_bytes / 16;
+  for (int i = tid; i < picks * chunks; i += blockDim.x) {
+    const int r = i / chunks, c = i - r * chunks;
+    const int t = s_rt[r];
+    if (t < 0) continue;
+    const u32x4_t *src = (const u32x4_t *)((const char *)x + (size_t)t * row_bytes) + c;
+    u32x4_t *dst = (u32x4_t *)((char *)xg + (size_t)r * row_bytes) + c;
+    *dst = *src;
+  }
 }
 
 // Multi-workgroup path, launch 1: chunk c covers tokens [256c, 256c+256): its

@@ -15,7 +15,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe_nvfp4.so")
+# MOE_NVFP4_LIB may name another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("MOE_NVFP4_LIB", os.path.join(_HERE, "libmoe_nvfp4.so"))
 
 MOE_OK, MOE_INVALID_ARG, MOE_UNSUPPORTED, MOE_HIP_ERROR, MOE_WORKSPACE_TOO_SMALL = 0, 1, 2, 3, 4
 MOE_F32, MOE_BF16 = 0, 1
