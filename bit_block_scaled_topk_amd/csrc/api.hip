@@ -41,6 +41,7 @@ ProjProblem make_problem(const uint16_t *a, long plane, long lda, const int32_t 
                          uint16_t *out_h, long ldo, long h_plane) {
   ProjProblem p{};
   p.a = a;
+  p.row_map = nullptr;
   p.plane = plane;
   p.lda = lda;
   p.offsets = offsets;
@@ -284,8 +285,8 @@ namespace {
 struct LayerPlan {
   int n, d, E, K, f, fs, R;
   bool has_shared, f32;
-  size_t off_ids, off_w, off_offsets, off_row_token, off_rows, off_xg, off_yg, off_gather, off_h, off_hs,
-      off_split, off_split_s, total;
+  size_t off_ids, off_w, off_offsets, off_row_token, off_rows, off_yg, off_gather, off_h, off_hs, off_split,
+      total;
 };
 
 bool plan_layer(const moe_layer_desc *dsc, LayerPlan *pl) {
@@ -328,13 +329,12 @@ bool plan_layer(const moe_layer_desc *dsc, LayerPlan *pl) {
   p.off_offsets = take((size_t)(p.E + 1) * 4);
   p.off_row_token = take((size_t)p.R * 4);
   p.off_rows = take((size_t)p.R * 4);
-  p.off_xg = take((size_t)p.R * p.d * xb);
   p.off_yg = take((size_t)p.R * p.d * 4);
   p.off_gather = take(gather_workspace_bytes(p.n, p.E));
   p.off_h = take(h_bytes(p.R, p.f));
   p.off_hs = take(p.has_shared ? h_bytes(p.n, p.fs) : 0);
-  p.off_split = take(p.f32 ? split_bytes(p.R, p.d) : 0);
-  p.off_split_s = take(p.f32 ? split_bytes(p.n, p.d) : 0);
+  p.off_split = take(p.f32 ? split_bytes(p.n, p.d) : 0);
+  (void)xb;
   p.total = o;
   *pl = p;
   return true;
@@ -357,7 +357,6 @@ moe_status moe_layer_get_views(const moe_layer_desc *desc, void *workspace, moe_
   v->expert_offsets = (int32_t *)(ws + p.off_offsets);
   v->row_token = (int32_t *)(ws + p.off_row_token);
   v->rows = (int32_t *)(ws + p.off_rows);
-  v->xg = (void *)(ws + p.off_xg);
   v->yg = (float *)(ws + p.off_yg);
   return MOE_OK;
 }
@@ -382,39 +381,35 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, 
   int32_t *offsets = (int32_t *)(ws + p.off_offsets);
   int32_t *row_token = (int32_t *)(ws + p.off_row_token);
   int32_t *rows = (int32_t *)(ws + p.off_rows);
-  void *xg = ws + p.off_xg;
   float *yg = (float *)(ws + p.off_yg);
   uint16_t *h = (uint16_t *)(ws + p.off_h);
   uint16_t *hs = (uint16_t *)(ws + p.off_hs);
   const int elem = p.f32 ? 4 : 2;
 
   if (mark(0) != hipSuccess) return MOE_HIP_ERROR;
-  // 1. routing + gather
+  // 1. routing + gather layout.  The packed activation rows are not
+  //    materialised: the routed up projection reads x through row_token.
   if (gather_is_single_launch(p.n, p.K, p.E, elem, p.d)) {
-    if (launch_route_gather_small(logits, p.n, p.E, p.K, ids, w, x, elem, p.d, xg, offsets, row_token, rows,
+    if (launch_route_gather_small(logits, p.n, p.E, p.K, ids, w, x, elem, p.d, nullptr, offsets, row_token, rows,
                                   stream) != hipSuccess)
       return MOE_HIP_ERROR;
   } else {
     if (launch_route_topk(logits, p.n, p.E, p.K, ids, w, stream) != hipSuccess) return MOE_HIP_ERROR;
-    if (launch_gather(x, elem, p.n, p.d, ids, p.K, p.E, xg, offsets, row_token, rows, ws + p.off_gather, stream) !=
-        hipSuccess)
+    if (launch_gather(x, elem, p.n, p.d, ids, p.K, p.E, nullptr, offsets, row_token, rows, ws + p.off_gather,
+                      stream) != hipSuccess)
       return MOE_HIP_ERROR;
   }
 
   if (mark(1) != hipSuccess) return MOE_HIP_ERROR;
-  // 2. activation planes
-  const uint16_t *a_r = (const uint16_t *)xg, *a_s = (const uint16_t *)x;
-  long plane_r = 0, plane_s = 0;
+  // 2. activation planes (fp32 x only: three bf16 planes of the n token rows)
+  const uint16_t *a_x = (const uint16_t *)x;
+  long plane_x = 0;
   int nt = 1;
   if (p.f32) {
-    uint16_t *sr = (uint16_t *)(ws + p.off_split), *ss = (uint16_t *)(ws + p.off_split_s);
-    plane_r = (long)p.R * p.d;
-    plane_s = (long)p.n * p.d;
-    if (launch_split3((const float *)xg, plane_r, sr, plane_r, stream) != hipSuccess) return MOE_HIP_ERROR;
-    if (p.has_shared && launch_split3((const float *)x, plane_s, ss, plane_s, stream) != hipSuccess)
-      return MOE_HIP_ERROR;
-    a_r = sr;
-    a_s = ss;
+    uint16_t *sx = (uint16_t *)(ws + p.off_split);
+    plane_x = (long)p.n * p.d;
+    if (launch_split3((const float *)x, plane_x, sx, plane_x, stream) != hipSuccess) return MOE_HIP_ERROR;
+    a_x = sx;
     nt = 3;
   }
 
@@ -427,11 +422,12 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, 
   const int epi = dsc->act == MOE_SWIGLU ? EPI_SWIGLU : EPI_RELU2;
   const long h_plane = (long)p.R * p.f, hs_plane = (long)p.n * p.fs;
 
-  ProjProblem ru = make_problem(a_r, plane_r, p.d, offsets, p.E, p.R, -1, &dsc->up, p.f, nullptr, h, p.f, h_plane);
+  ProjProblem ru = make_problem(a_x, plane_x, p.d, offsets, p.E, p.R, -1, &dsc->up, p.f, nullptr, h, p.f, h_plane);
+  ru.row_map = row_token;  // gather on load
   ProjProblem rd = make_problem(h, h_plane, p.f, offsets, p.E, p.R, -1, &dsc->down, p.d, yg, nullptr, p.d, 0);
   ProjProblem su{}, sd{};
   if (p.has_shared) {
-    su = make_problem(a_s, plane_s, p.d, nullptr, 1, p.n, p.n, &dsc->shared_up, p.fs, nullptr, hs, p.fs, hs_plane);
+    su = make_problem(a_x, plane_x, p.d, nullptr, 1, p.n, p.n, &dsc->shared_up, p.fs, nullptr, hs, p.fs, hs_plane);
     sd = make_problem(hs, hs_plane, p.fs, nullptr, 1, p.n, p.n, &dsc->shared_down, p.d, out, nullptr, p.d, 0);
   }
 

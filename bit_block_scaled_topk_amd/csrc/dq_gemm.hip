@@ -94,7 +94,8 @@ __global__ void __launch_bounds__(256) k_dq_gemm(GemmBatch batch) {
   // loader roles: thread -> (tile row, 32-wide half of the k step)
   const int lrow = tid >> 1, lhalf = tid & 1;
   const bool a_ok = lrow < mrows;
-  const uint16_t *a_ptr = p.a + (size_t)(r0 + (a_ok ? lrow : 0)) * p.lda + lhalf * 32;
+  const int a_row = p.row_map ? max(p.row_map[r0 + (a_ok ? lrow : 0)], 0) : r0 + (a_ok ? lrow : 0);
+  const uint16_t *a_ptr = p.a + (size_t)a_row * p.lda + lhalf * 32;
 
   int hcol, wrow_idx;
   if (EPI == EPI_SWIGLU) {

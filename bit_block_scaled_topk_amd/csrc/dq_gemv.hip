@@ -147,7 +147,8 @@ __global__ void __launch_bounds__(64 * WAVES) k_dq_gemv(GemvBatch batch) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = min(mt * 16 + nl, rows - 1);
-    arow[mt] = p.a + (size_t)(r0 + m) * p.lda;
+    const int ar = p.row_map ? max(p.row_map[r0 + m], 0) : r0 + m;
+    arow[mt] = p.a + (size_t)ar * p.lda;
   }
 
   f32x4_t acc[MT][NB];

@@ -52,10 +52,85 @@ __device__ __forceinline__ void copy_rows(const void *x, int row_bytes, const in
   }
 }
 
+// Inclusive prefix sum over a wavefront: DPP row shifts inside each 16-lane
+// row, then the totals of the earlier rows read with readlane.
+__device__ __forceinline__ int wave_scan_incl(int v, int lane) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  return v + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
+}
+
+// Top-K of every token by ranks, with the whole workgroup: logits staged in LDS,
+// each (token, expert, part) thread counts how many experts of its part beat
+// the expert (larger logit, or equal logit and lower index: a strict total
+// order, so ranks are unique), the parts are summed with LDS atomics, and the
+// expert of rank j < K becomes slot j.  Softmax over the picks per token, the
+// sum in slot order.  Requires n*E <= kRankPairs.
+constexpr int kRankPairs = 8192;
+
+__device__ void route_by_rank(const float *__restrict__ logits, int n, int E, int K, float *s_logit, int *s_rank,
+                              int *s_sel, int32_t *ids, float *topk_w, int32_t *s_ids) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int pairs = n * E;
+  for (int i = tid; i < pairs; i += nthr) {
+    s_logit[i] = logits[i];
+    s_rank[i] = 0;
+  }
+  for (int i = tid; i < n * K; i += nthr) s_sel[i] = -1;
+  __syncthreads();
+  const int parts = pairs >= nthr ? 1 : nthr / pairs;
+  const int span = (E + parts - 1) / parts;
+  for (int i = tid; i < pairs * parts; i += nthr) {
+    const int pair = i / parts, part = i - pair * parts;
+    const int t = pair / E, a = pair - t * E;
+    const float *row = s_logit + t * E;
+    const float va = row[a];
+    const int b0 = part * span, b1 = min(E, b0 + span);
+    int cnt = 0;
+    for (int b = b0; b < b1; ++b) {
+      const float vb = row[b];
+      cnt += (vb > va || (vb == va && b < a)) ? 1 : 0;
+    }
+    if (parts == 1)
+      s_rank[pair] = cnt;
+    else if (cnt)
+      atomicAdd(&s_rank[pair], cnt);
+  }
+  __syncthreads();
+  for (int i = tid; i < pairs; i += nthr) {
+    const int r = s_rank[i];
+    if (r < K) {
+      const int t = i / E;
+      s_sel[t * K + r] = i - t * E;
+    }
+  }
+  __syncthreads();
+  for (int t = tid; t < n; t += nthr) {
+    const float *row = s_logit + t * E;
+    const int e0 = s_sel[t * K];
+    const float l0 = e0 >= 0 ? row[e0] : 0.0f;
+    float sum = 0.0f;
+    for (int j = 0; j < K; ++j) {
+      const int e = s_sel[t * K + j];
+      sum += e >= 0 ? expf(row[e] - l0) : 0.0f;
+    }
+    for (int j = 0; j < K; ++j) {
+      const int e = s_sel[t * K + j];
+      ids[(size_t)t * K + j] = e;
+      topk_w[(size_t)t * K + j] = e >= 0 ? expf(row[e] - l0) / sum : 0.0f;
+      s_ids[t * K + j] = e;
+    }
+  }
+}
+
 // One workgroup: [routing of every token ->] bitmap in LDS -> ranks -> offsets
-// -> placement -> row copy.  Only __syncthreads between phases: every phase
-// reads LDS or global memory written by this workgroup's earlier phases
-// through the same CU.
+// -> placement [-> row copy when xg is given].  Only __syncthreads between
+// phases: every phase reads LDS, or global memory this workgroup wrote.
 template <bool ROUTE>
 __global__ void __launch_bounds__(kSmallThreads)
 k_gather_small(const float *__restrict__ logits, float *__restrict__ topk_w, int32_t *ids, int n, int K, int E,
@@ -66,6 +141,10 @@ k_gather_small(const float *__restrict__ logits, float *__restrict__ topk_w, int
   __shared__ int32_t s_rt[kSmallPicks];
   __shared__ int32_t s_count[MOE_MAX_EXPERTS + 1];
   __shared__ int32_t s_off[MOE_MAX_EXPERTS + 1];
+  __shared__ int32_t s_wave[kSmallThreads / 64];
+  __shared__ float s_logit[ROUTE ? kRankPairs : 1];
+  __shared__ int32_t s_rank[ROUTE ? kRankPairs : 1];
+  __shared__ int32_t s_sel[ROUTE ? kSmallPicks : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
   const int W = (n + 31) >> 5;
   const int picks = n * K;
@@ -74,14 +153,18 @@ k_gather_small(const float *__restrict__ logits, float *__restrict__ topk_w, int
 
   for (int i = tid; i < E * W; i += blockDim.x) bits[i] = 0u;
   if (ROUTE) {
-    for (int t = wave; t < n; t += nwaves) {
-      int my_id;
-      float my_w;
-      route_one_token_any(logits + (size_t)t * E, E, K, lane, my_id, my_w);
-      if (lane < K) {
-        ids[(size_t)t * K + lane] = my_id;
-        topk_w[(size_t)t * K + lane] = my_w;
-        s_ids[t * K + lane] = my_id;
+    if (n * E <= kRankPairs) {
+      route_by_rank(logits, n, E, K, s_logit, s_rank, s_sel, ids, topk_w, s_ids);
+    } else {
+      for (int t = wave; t < n; t += nwaves) {
+        int my_id;
+        float my_w;
+        route_one_token_any(logits + (size_t)t * E, E, K, lane, my_id, my_w);
+        if (lane < K) {
+          ids[(size_t)t * K + lane] = my_id;
+          topk_w[(size_t)t * K + lane] = my_w;
+          s_ids[t * K + lane] = my_id;
+        }
       }
     }
   } else {
@@ -90,45 +173,43 @@ k_gather_small(const float *__restrict__ logits, float *__restrict__ topk_w, int
   __syncthreads();
 
   for (int p = tid; p < picks; p += blockDim.x) {
-    int e = s_ids[p];
-    int t = p / K;
+    const int e = s_ids[p];
+    const int t = p / K;
     if (e >= 0 && e < E) atomicOr(&bits[e * W + (t >> 5)], 1u << (t & 31));
   }
   __syncthreads();
 
-  for (int e = wave; e < E; e += nwaves) {
+  // per expert: exclusive prefix popcount over its (few) words, and its count
+  for (int e = tid; e < E; e += blockDim.x) {
     int running = 0;
-    for (int w0 = 0; w0 < W; w0 += 64) {
-      int w = w0 + lane;
-      int c = (w < W) ? __popc(bits[e * W + w]) : 0;
-      int incl = wave_incl_scan(c, lane);
-      if (w < W) prefix[e * W + w] = running + incl - c;
-      running += __shfl(incl, 63, 64);
+    for (int w = 0; w < W; ++w) {
+      prefix[e * W + w] = running;
+      running += __popc(bits[e * W + w]);
     }
-    if (lane == 0) s_count[e] = running;
+    s_count[e] = running;
   }
   __syncthreads();
 
-  if (wave == 0) {
-    int running = 0;
-    for (int e0 = 0; e0 < E; e0 += 64) {
-      int e = e0 + lane;
-      int c = (e < E) ? s_count[e] : 0;
-      int incl = wave_incl_scan(c, lane);
-      if (e < E) s_off[e] = running + incl - c;
-      running += __shfl(incl, 63, 64);
-    }
-    if (lane == 0) s_off[E] = running;
+  // exclusive scan of the counts -> group offsets (E <= blockDim)
+  {
+    const int c = (tid < E) ? s_count[tid] : 0;
+    const int incl = wave_scan_incl(c, lane);
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += s_wave[w];
+    if (tid < E) s_off[tid] = base + incl - c;
+    if (tid == blockDim.x - 1) s_off[E] = base + incl;
   }
   __syncthreads();
   for (int e = tid; e <= E; e += blockDim.x) offsets[e] = s_off[e];
 
   for (int p = tid; p < picks; p += blockDim.x) {
-    int e = s_ids[p];
-    int t = p / K;
+    const int e = s_ids[p];
+    const int t = p / K;
     int32_t r = -1;
     if (e >= 0 && e < E) {
-      int wi = e * W + (t >> 5);
+      const int wi = e * W + (t >> 5);
       r = s_off[e] + (int32_t)prefix[wi] + __popc(bits[wi] & ((1u << (t & 31)) - 1u));
       row_token[r] = t;
       s_rt[r] = t;
@@ -139,16 +220,34 @@ k_gather_small(const float *__restrict__ logits, float *__restrict__ topk_w, int
     row_token[r] = -1;
     s_rt[r] = -1;
   }
+  if (xg == nullptr) return;
   __syncthreads();
-  // row copy from the LDS copy of row_token
+  // row copy from the LDS copy of row_token, 4 chunks in flight per thread
   const int chunks = row_bytes / 16;
-  for (int i = tid; i < picks * chunks; i += blockDim.x) {
-    const int r = i / chunks, c = i - r * chunks;
-    const int t = s_rt[r];
-    if (t < 0) continue;
-    const u32x4_t *src = (const u32x4_t *)((const char *)x + (size_t)t * row_bytes) + c;
-    u32x4_t *dst = (u32x4_t *)((char *)xg + (size_t)r * row_bytes) + c;
-    *dst = *src;
+  const int total = picks * chunks;
+  for (int i0 = tid; i0 < total; i0 += 4 * blockDim.x) {
+    u32x4_t v[4];
+    int dst[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * blockDim.x;
+      dst[u] = -1;
+      if (i < total) {
+        const int r = i / chunks, c = i - r * chunks;
+        const int t = s_rt[r];
+        if (t >= 0) {
+          v[u] = *((const u32x4_t *)((const char *)x + (size_t)t * row_bytes) + c);
+          dst[u] = i;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (dst[u] >= 0) {
+        const int r = dst[u] / chunks, c = dst[u] - r * chunks;
+        *((u32x4_t *)((char *)xg + (size_t)r * row_bytes) + c) = v[u];
+      }
+    }
   }
 }
 
@@ -307,6 +406,7 @@ hipError_t launch_gather(const void *x, int elem_bytes, int n_tokens, int d_mode
   long blocks = (chunks + 255) / 256;
   if (blocks > 16384) blocks = 16384;
   if (blocks < 1) blocks = 1;
+  if (xg == nullptr) return hipSuccess;  // the caller reads x through row_token instead
   hipLaunchKernelGGL(k_gather_copy, dim3((unsigned)blocks), dim3(256), 0, stream, x, row_bytes, row_token, R, xg);
   return hipGetLastError();
 }

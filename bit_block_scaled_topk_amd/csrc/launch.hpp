@@ -46,7 +46,8 @@ hipError_t launch_split3(const float *a, long n_elems, uint16_t *planes, long pl
 
 // One grouped NVFP4 projection handled by the decode or prefill kernels.
 struct ProjProblem {
-  const uint16_t *a;      // bf16 activations: nt planes of [n_rows][lda] (plane stride `plane`)
+  const uint16_t *a;      // bf16 activations: nt planes of [rows][lda] (plane stride `plane`)
+  const int32_t *row_map; // optional: packed row r reads activation row row_map[r] (gather on load)
   long plane;
   long lda;
   const int32_t *offsets; // [n_experts + 1] device (unused when known_rows >= 0)

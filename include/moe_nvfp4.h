@@ -236,9 +236,10 @@ typedef struct {
   int32_t *expert_offsets; /* [E+1] */
   int32_t *row_token;      /* [n*K] */
   int32_t *rows;           /* [n][K] */
-  void *xg;                /* [n*K][d] of x_dtype */
   float *yg;               /* [n*K][d]: each routed expert's output rows */
 } moe_layer_views;
+/* (moe_layer_forward does not materialise the packed activation rows: the
+ * routed up projection reads x[row_token[r]] directly.) */
 
 /* Workspace bytes moe_layer_forward needs (0 for an invalid description). */
 size_t moe_layer_workspace_size(const moe_layer_desc *desc);
