@@ -286,7 +286,8 @@ struct LayerPlan {
   int n, d, E, K, f, fs, R;
   bool has_shared, f32;
   size_t off_ids, off_w, off_offsets, off_row_token, off_rows, off_yg, off_gather, off_h, off_hs, off_split,
-      total;
+      off_sync, total;
+  int sync_words;
 };
 
 bool plan_layer(const moe_layer_desc *dsc, LayerPlan *pl) {
@@ -334,6 +335,8 @@ bool plan_layer(const moe_layer_desc *dsc, LayerPlan *pl) {
   p.off_h = take(h_bytes(p.R, p.f));
   p.off_hs = take(p.has_shared ? h_bytes(p.n, p.fs) : 0);
   p.off_split = take(p.f32 ? split_bytes(p.n, p.d) : 0);
+  p.sync_words = (int)decode_layer_sync_words(p.E < p.R ? p.E : p.R, p.d);
+  p.off_sync = take((size_t)p.sync_words * 4);
   (void)xb;
   p.total = o;
   *pl = p;
@@ -358,6 +361,8 @@ moe_status moe_layer_get_views(const moe_layer_desc *desc, void *workspace, moe_
   v->row_token = (int32_t *)(ws + p.off_row_token);
   v->rows = (int32_t *)(ws + p.off_rows);
   v->yg = (float *)(ws + p.off_yg);
+  v->wait_error = (int32_t *)(ws + p.off_sync);
+  v->decode_launch = (int32_t *)(ws + p.off_sync) + 1;
   return MOE_OK;
 }
 
@@ -386,12 +391,15 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, 
   uint16_t *hs = (uint16_t *)(ws + p.off_hs);
   const int elem = p.f32 ? 4 : 2;
 
+  int32_t *sync = (int32_t *)(ws + p.off_sync);
+
   if (mark(0) != hipSuccess) return MOE_HIP_ERROR;
   // 1. routing + gather layout.  The packed activation rows are not
   //    materialised: the routed up projection reads x through row_token.
-  if (gather_is_single_launch(p.n, p.K, p.E, elem, p.d)) {
+  const bool single = gather_is_single_launch(p.n, p.K, p.E, elem, p.d);
+  if (single) {
     if (launch_route_gather_small(logits, p.n, p.E, p.K, ids, w, x, elem, p.d, nullptr, offsets, row_token, rows,
-                                  stream) != hipSuccess)
+                                  sync, p.sync_words, stream) != hipSuccess)
       return MOE_HIP_ERROR;
   } else {
     if (launch_route_topk(logits, p.n, p.E, p.K, ids, w, stream) != hipSuccess) return MOE_HIP_ERROR;
@@ -401,6 +409,49 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, 
   }
 
   if (mark(1) != hipSuccess) return MOE_HIP_ERROR;
+  const int gmax = dsc->gemv_max_rows;
+  const int max_active = p.E < p.R ? p.E : p.R;
+  const int epi = dsc->act == MOE_SWIGLU ? EPI_SWIGLU : EPI_RELU2;
+  // 2-5 in one persistent launch for a decode step (every expert on the decode
+  //     path, at most two tokens) once step 1 has cleared the counters
+  if (single && p.n <= gmax && decode_layer_takes(p.n)) {
+    DecodeLayerProblem lp{};
+    ProjProblem ru = make_problem(nullptr, 0, p.d, offsets, p.E, p.R, -1, &dsc->up, p.f, nullptr, nullptr, 0, 0);
+    ru.row_map = row_token;
+    lp.up[1] = as_decode(ru, p.n);
+    lp.down[1] = make_problem(nullptr, 0, p.f, offsets, p.E, p.R, -1, &dsc->down, p.d, nullptr, nullptr, 0, 0);
+    if (p.has_shared) {
+      lp.up[0] = make_problem(nullptr, 0, p.d, nullptr, 1, p.n, p.n, &dsc->shared_up, p.fs, nullptr, nullptr, 0, 0);
+      lp.down[0] =
+          make_problem(nullptr, 0, p.fs, nullptr, 1, p.n, p.n, &dsc->shared_down, p.d, nullptr, nullptr, 0, 0);
+    }
+    lp.has_shared = p.has_shared;
+    lp.max_slots = max_active;
+    lp.act = epi;
+    lp.x = x;
+    lp.x_f32 = p.f32;
+    lp.h[0] = (float *)hs;
+    lp.h[1] = (float *)h;
+    lp.out = out;
+    lp.yg = yg;
+    lp.rows = rows;
+    lp.w = w;
+    lp.n_tokens = p.n;
+    lp.top_k = p.K;
+    lp.d = p.d;
+    lp.f = p.f;
+    lp.fs = p.fs;
+    lp.n_rows = p.R;
+    lp.sync = sync;
+    const hipError_t e = launch_decode_layer(lp, stream);
+    if (e == hipSuccess) {
+      for (int i = 2; i <= 5; ++i)
+        if (mark(i) != hipSuccess) return MOE_HIP_ERROR;
+      return MOE_OK;
+    }
+    if (e != hipErrorNotSupported) return MOE_HIP_ERROR;
+  }
+
   // 2. activation planes (fp32 x only: three bf16 planes of the n token rows)
   const uint16_t *a_x = (const uint16_t *)x;
   long plane_x = 0;
@@ -413,13 +464,10 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, 
     nt = 3;
   }
 
-  const int gmax = dsc->gemv_max_rows;
   const int dec_rows = gmax < p.n ? gmax : p.n;  // a routed expert has at most n rows
   const bool routed_gemm = p.n > gmax;
   const bool shared_gemv = p.has_shared && p.n <= gmax;
   const bool shared_gemm = p.has_shared && p.n > gmax;
-  const int max_active = p.E < p.R ? p.E : p.R;
-  const int epi = dsc->act == MOE_SWIGLU ? EPI_SWIGLU : EPI_RELU2;
   const long h_plane = (long)p.R * p.f, hs_plane = (long)p.n * p.fs;
 
   ProjProblem ru = make_problem(a_x, plane_x, p.d, offsets, p.E, p.R, -1, &dsc->up, p.f, nullptr, h, p.f, h_plane);

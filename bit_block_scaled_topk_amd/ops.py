@@ -83,7 +83,8 @@ class LayerViews(ctypes.Structure):
     """moe_layer_views."""
     _fields_ = [("topk_ids", ctypes.c_void_p), ("topk_weights", ctypes.c_void_p),
                 ("expert_offsets", ctypes.c_void_p), ("row_token", ctypes.c_void_p), ("rows", ctypes.c_void_p),
-                ("yg", ctypes.c_void_p)]
+                ("yg", ctypes.c_void_p), ("wait_error", ctypes.c_void_p),
+                ("decode_launch", ctypes.c_void_p)]
 
 
 _lib.moe_layer_workspace_size.argtypes = [ctypes.POINTER(LayerDesc)]
@@ -401,7 +402,9 @@ class MoELayer:
                     offsets=view(v.expert_offsets, self.E + 1, torch.int32),
                     row_token=view(v.row_token, R, torch.int32),
                     rows=view(v.rows, R, torch.int32).view(n, self.K),
-                    yg=view(v.yg, R * self.d, torch.float32).view(R, self.d))
+                    yg=view(v.yg, R * self.d, torch.float32).view(R, self.d),
+                    wait_error=view(v.wait_error, 1, torch.int32),
+                    decode_launch=view(v.decode_launch, 1, torch.int32))
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor, stream=None, weights=None,
                 timing: Optional[dict] = None) -> torch.Tensor:

@@ -398,15 +398,71 @@ def test_layer_forward_fused(ops, name):
     else:
         ref = oracle.layer(inp)
         assert normwise(got, ref["out"]) <= TOL_DECODE
+    assert int(host(v["wait_error"])[0]) == 0
+    single = inp.n <= 2
+    if inp.n <= 64:  # routing and gather share one launch, which clears the word
+        assert int(host(v["decode_launch"])[0]) == (1 if single else 0)
     unfused = layer.forward(x, lg).clone()
     torch.cuda.synchronize()
-    assert torch.equal(fused, unfused)
+    if single:  # fp32 dot products on the vector ALUs: equal to fp32 rounding
+        assert normwise(host(fused).astype(np.float64), host(unfused).astype(np.float64)) <= 2e-6
+    else:
+        assert torch.equal(fused, unfused)
 
 
-def test_layer_forward_fused_repeat_and_graph(ops):
+# Decode steps the single-launch layer takes (one or two tokens): tiny shapes
+# (fp32 x) with every expert holding both rows, one expert, k-slices that leave
+# wavefronts empty; realistic shapes with a skewed router, without a shared
+# expert and with the gated FFN (bf16 x).  The last case (seven tokens) falls
+# back to the per-step launches.
+SINGLE_LAUNCH_CASES = [
+    ("tiny16", dict(n=1, seed=11), True),
+    ("tiny16", dict(n=2, E=4, K=4, seed=12), True),
+    ("tiny16", dict(n=1, E=1, K=1, seed=13), True),
+    ("tiny16", dict(n=2, d=96, f=160, fs=224, seed=14), True),
+    ("decode1", dict(n=2, K=2, E=32, fs=1856, logits="zipf", seed=15), True),
+    ("decode1", dict(n=1, E=32, fs=0, seed=16), True),
+    ("gated2", dict(n=1, seed=17), True),
+    ("decode1", dict(n=7, E=32, fs=0, seed=18), False),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SINGLE_LAUNCH_CASES)))
+def test_layer_single_launch_decode(ops, case):
+    """Back-to-back fused calls with different routings: each matches the
+    oracle, leaves no expired wait, agrees with the four-call path (bit for bit
+    where the per-step launches run) and repeats bit for bit."""
+    name, ov, single = SINGLE_LAUNCH_CASES[case]
+    inp = cached_layer(name, **ov)
+    print(f"single-launch case {name} {ov}", flush=True)
+    layer = ops.MoELayer(inp)
+    x = dev(inp.x)
+    logit_sets = [inp.logits, np.ascontiguousarray(np.roll(inp.logits, 1, axis=1))]
+    lgs = [dev(l) for l in logit_sets]
+    outs = [layer.forward_fused(x, lg).clone() for lg in lgs + lgs[:1]]
+    v = layer.views()
+    errs = host(v["wait_error"]).copy()
+    ran = host(v["decode_launch"]).copy()
+    torch.cuda.synchronize()
+    assert int(errs[0]) == 0
+    assert int(ran[0]) == (1 if single else 0)
+    assert torch.equal(outs[0], outs[2])
+    for lg_host, lg, got in zip(logit_sets, lgs, outs):
+        ref = oracle.layer(inp, routing=oracle.route_topk(lg_host, inp.K))
+        assert normwise(host(got).astype(np.float64), ref["out"]) <= TOL_DECODE
+        unfused = layer.forward(x, lg).clone()
+        torch.cuda.synchronize()
+        if single:
+            assert normwise(host(got).astype(np.float64), host(unfused).astype(np.float64)) <= 2e-6
+        else:
+            assert torch.equal(got, unfused)
+
+
+@pytest.mark.parametrize("name", ["decode1", "decode32_zipf"])
+def test_layer_forward_fused_repeat_and_graph(ops, name):
     """Captured in a HIP graph and replayed, the fused layer gives the eager
     bits on every replay (the layer neither allocates nor synchronises)."""
-    inp = cached_layer("decode32_zipf")
+    inp = cached_layer(name)
     layer = ops.MoELayer(inp)
     x, lg = dev(inp.x), dev(inp.logits)
     eager = layer.forward_fused(x, lg).clone()
