@@ -325,6 +325,10 @@ bool plan_layer(const moe_layer_desc *dsc, LayerPlan *pl) {
     o += align_up(bytes);
     return at;
   };
+  // the decode layer's flags and counters first: the same place for every
+  // description, so a workspace initialised once serves calls of any size
+  p.sync_words = (int)decode_layer_sync_words();
+  p.off_sync = take((size_t)p.sync_words * 4);
   p.off_ids = take((size_t)p.R * 4);
   p.off_w = take((size_t)p.R * 4);
   p.off_offsets = take((size_t)(p.E + 1) * 4);
@@ -335,8 +339,6 @@ bool plan_layer(const moe_layer_desc *dsc, LayerPlan *pl) {
   p.off_h = take(h_bytes(p.R, p.f));
   p.off_hs = take(p.has_shared ? h_bytes(p.n, p.fs) : 0);
   p.off_split = take(p.f32 ? split_bytes(p.n, p.d) : 0);
-  p.sync_words = (int)decode_layer_sync_words(p.E < p.R ? p.E : p.R, p.d);
-  p.off_sync = take((size_t)p.sync_words * 4);
   (void)xb;
   p.total = o;
   *pl = p;
@@ -363,6 +365,15 @@ moe_status moe_layer_get_views(const moe_layer_desc *desc, void *workspace, moe_
   v->yg = (float *)(ws + p.off_yg);
   v->wait_error = (int32_t *)(ws + p.off_sync);
   v->decode_launch = (int32_t *)(ws + p.off_sync) + 1;
+  return MOE_OK;
+}
+
+moe_status moe_layer_workspace_init(const moe_layer_desc *desc, void *workspace, size_t ws_bytes,
+                                    hipStream_t stream) {
+  LayerPlan p;
+  if (!plan_layer(desc, &p) || !workspace || !aligned(workspace, kAlign)) return MOE_INVALID_ARG;
+  if (ws_bytes < p.total) return MOE_WORKSPACE_TOO_SMALL;
+  if (decode_layer_init((int32_t *)((char *)workspace + p.off_sync), stream) != hipSuccess) return MOE_HIP_ERROR;
   return MOE_OK;
 }
 
@@ -394,32 +405,15 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, 
   int32_t *sync = (int32_t *)(ws + p.off_sync);
 
   if (mark(0) != hipSuccess) return MOE_HIP_ERROR;
-  // 1. routing + gather layout.  The packed activation rows are not
-  //    materialised: the routed up projection reads x through row_token.
-  const bool single = gather_is_single_launch(p.n, p.K, p.E, elem, p.d);
-  if (single) {
-    if (launch_route_gather_small(logits, p.n, p.E, p.K, ids, w, x, elem, p.d, nullptr, offsets, row_token, rows,
-                                  sync, p.sync_words, stream) != hipSuccess)
-      return MOE_HIP_ERROR;
-  } else {
-    if (launch_route_topk(logits, p.n, p.E, p.K, ids, w, stream) != hipSuccess) return MOE_HIP_ERROR;
-    if (launch_gather(x, elem, p.n, p.d, ids, p.K, p.E, nullptr, offsets, row_token, rows, ws + p.off_gather,
-                      stream) != hipSuccess)
-      return MOE_HIP_ERROR;
-  }
-
-  if (mark(1) != hipSuccess) return MOE_HIP_ERROR;
   const int gmax = dsc->gemv_max_rows;
   const int max_active = p.E < p.R ? p.E : p.R;
   const int epi = dsc->act == MOE_SWIGLU ? EPI_SWIGLU : EPI_RELU2;
-  // 2-5 in one persistent launch for a decode step (every expert on the decode
-  //     path, at most two tokens) once step 1 has cleared the counters
-  if (single && p.n <= gmax && decode_layer_takes(p.n)) {
+  // 1-5 in one persistent launch for a decode step (at most two tokens, every
+  //     expert on the decode path)
+  if (p.n <= gmax && decode_layer_takes(p.n, p.K, p.d)) {
     DecodeLayerProblem lp{};
-    ProjProblem ru = make_problem(nullptr, 0, p.d, offsets, p.E, p.R, -1, &dsc->up, p.f, nullptr, nullptr, 0, 0);
-    ru.row_map = row_token;
-    lp.up[1] = as_decode(ru, p.n);
-    lp.down[1] = make_problem(nullptr, 0, p.f, offsets, p.E, p.R, -1, &dsc->down, p.d, nullptr, nullptr, 0, 0);
+    lp.up[1] = make_problem(nullptr, 0, p.d, nullptr, p.E, p.R, -1, &dsc->up, p.f, nullptr, nullptr, 0, 0);
+    lp.down[1] = make_problem(nullptr, 0, p.f, nullptr, p.E, p.R, -1, &dsc->down, p.d, nullptr, nullptr, 0, 0);
     if (p.has_shared) {
       lp.up[0] = make_problem(nullptr, 0, p.d, nullptr, 1, p.n, p.n, &dsc->shared_up, p.fs, nullptr, nullptr, 0, 0);
       lp.down[0] =
@@ -430,13 +424,18 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, 
     lp.act = epi;
     lp.x = x;
     lp.x_f32 = p.f32;
+    lp.logits = logits;
     lp.h[0] = (float *)hs;
     lp.h[1] = (float *)h;
     lp.out = out;
     lp.yg = yg;
+    lp.ids = ids;
+    lp.topk_w = w;
+    lp.offsets = offsets;
+    lp.row_token = row_token;
     lp.rows = rows;
-    lp.w = w;
     lp.n_tokens = p.n;
+    lp.n_experts = p.E;
     lp.top_k = p.K;
     lp.d = p.d;
     lp.f = p.f;
@@ -445,12 +444,26 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, 
     lp.sync = sync;
     const hipError_t e = launch_decode_layer(lp, stream);
     if (e == hipSuccess) {
-      for (int i = 2; i <= 5; ++i)
+      for (int i = 1; i <= 5; ++i)
         if (mark(i) != hipSuccess) return MOE_HIP_ERROR;
       return MOE_OK;
     }
     if (e != hipErrorNotSupported) return MOE_HIP_ERROR;
   }
+
+  // 1. routing + gather layout.  The packed activation rows are not
+  //    materialised: the routed up projection reads x through row_token.
+  if (gather_is_single_launch(p.n, p.K, p.E, elem, p.d)) {
+    if (launch_route_gather_small(logits, p.n, p.E, p.K, ids, w, x, elem, p.d, nullptr, offsets, row_token, rows,
+                                  stream) != hipSuccess)
+      return MOE_HIP_ERROR;
+  } else {
+    if (launch_route_topk(logits, p.n, p.E, p.K, ids, w, stream) != hipSuccess) return MOE_HIP_ERROR;
+    if (launch_gather(x, elem, p.n, p.d, ids, p.K, p.E, nullptr, offsets, row_token, rows, ws + p.off_gather,
+                      stream) != hipSuccess)
+      return MOE_HIP_ERROR;
+  }
+  if (mark(1) != hipSuccess) return MOE_HIP_ERROR;
 
   // 2. activation planes (fp32 x only: three bf16 planes of the n token rows)
   const uint16_t *a_x = (const uint16_t *)x;

@@ -36,24 +36,34 @@
 // whole L2: an agent-scope fence costs tens of nanoseconds, serialised per
 // XCD, per call.
 //
-// Flags and counters live in the caller's workspace and are zero at launch
-// (the routing + gather launch before this one clears them): after an error
-// word and a word that workgroup 0 sets to 1 (this launch ran),
-//   up_flag[w]  1 once workgroup w's up tiles are stored; a down tile of an
-//               expert waits for the flags of the workgroups that own that
-//               expert's up tiles (plain flags, one per workgroup: counters
-//               that hundreds of workgroups increment serialise on one
-//               address).
+// Routing comes first and is done by every workgroup for itself (one or two
+// tokens: a wavefront per token, top-K then softmax over the picks), followed
+// by the packed-row layout of the gather (expert ascending, token ascending
+// within an expert), kept in LDS; workgroup 0 also stores the routing and
+// layout views.  So a step is this one launch.
+//
+// Flags and counters live at the start of the caller's workspace; they are
+// zeroed once (decode_layer_init) and each launch leaves them ready for the
+// next, so no launch has to clear them:
+//   up_flag[w]  workgroup w's launch count: w reads its own flag e at start
+//               (every flag holds the same count between launches) and stores
+//               e + 1 once its up tiles are stored; a down tile of an expert
+//               waits until the flags of the workgroups that own that
+//               expert's up tiles read e + 1 (plain flags, one per workgroup:
+//               counters that hundreds of workgroups increment serialise on
+//               one address).
 //   ct_done[c]  down tiles finished for output column block c (one counter per
-//               64 bytes); the workgroup
-//               that finishes the last of them computes out = shared +
-//               sum_j w_j * y_j for those 16 columns, j in order.
+//               64 bytes); the workgroup that finishes the last of them resets
+//               it to zero and computes out = shared + sum_j w_j * y_j for
+//               those 16 columns, j in order.
 // Every wait is bounded (kSpinLimit sleeps); on expiry the error word is set
-// and the workgroup goes on, so the kernel always finishes.  No workgroup waits
-// before it has published all of its up tiles, so every wait ends once the
-// whole grid is resident (the host checks that with the occupancy query).
+// (it stays set) and the workgroup goes on, so the kernel always finishes and
+// every flag and counter still ends as described.  No workgroup waits before
+// it has published all of its up tiles, so every wait ends once the whole grid
+// is resident (the host checks that with the occupancy query).
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
+#include "route_device.hpp"
 
 namespace moe {
 
@@ -74,6 +84,9 @@ constexpr int kBatch = 4;              // one-token tiles whose sums are reduced
 constexpr int kMaxGrid = 1024;         // workgroups (one per CU)
 constexpr int kCtStride = 16;          // words between column counters: one counter per 64 bytes (atomics
                                        // to one cache line serialise)
+constexpr int kMaxCt = 1024;           // column blocks: d <= 16384
+constexpr int kMaxPicks = kMaxRows * MOE_MAX_TOPK;  // routed rows of a step (<= 64: one wavefront)
+constexpr int kSyncWords = 2 + kMaxGrid + kMaxCt * kCtStride;
 
 struct LayerArgs {
   DecodeLayerProblem lp;
@@ -91,17 +104,6 @@ struct Tile {
   int slot;
   int tile;
 };
-
-__device__ __forceinline__ int wave_scan_incl(int v, int lane) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);
-  const int r0 = __builtin_amdgcn_readlane(v, 15);
-  const int r1 = __builtin_amdgcn_readlane(v, 31);
-  const int r2 = __builtin_amdgcn_readlane(v, 47);
-  return v + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
-}
 
 // i-th tile of the up list: the shared expert's tiles, then slot by slot.
 __device__ __forceinline__ Tile up_tile(const LayerArgs &a, int i) {
@@ -549,13 +551,14 @@ __device__ __forceinline__ int up_owner(int i, int n_up, int grid) {
   return w;
 }
 
-// Wavefront-wide wait until flags[w_lo .. w_hi] are all set (lane l polls
-// w_lo + l, + 64, ...).  Bounded: on expiry the error word is set.
-__device__ __forceinline__ void wait_flags(const int32_t *flags, int w_lo, int w_hi, int lane, int32_t *err) {
+// Wavefront-wide wait until flags[w_lo .. w_hi] all read `target` (lane l
+// polls w_lo + l, + 64, ...).  Bounded: on expiry the error word is set.
+__device__ __forceinline__ void wait_flags(const int32_t *flags, int w_lo, int w_hi, int32_t target, int lane,
+                                           int32_t *err) {
   for (int base = w_lo; base <= w_hi; base += 64) {
     const int w = base + lane;
     int spins = 0;
-    while (!__all(w > w_hi || __hip_atomic_load(flags + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)) {
+    while (!__all(w > w_hi || __hip_atomic_load(flags + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == target)) {
       if (++spins > kSpinLimit) {
         if (lane == 0) __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
@@ -573,8 +576,11 @@ __device__ __forceinline__ void wait_flags(const int32_t *flags, int w_lo, int w
 template <int NB, int KU, int EPI_UP, bool X_F32, bool XREG>
 __global__ void __launch_bounds__(kThreads) k_decode_layer(LayerArgs a) {
   extern __shared__ u32x4_t s_dyn[];  // x [n][d] f32 | h [rows][k] f32 | down weights
-  __shared__ int s_e[MOE_MAX_EXPERTS], s_r0[MOE_MAX_EXPERTS], s_rows[MOE_MAX_EXPERTS];
-  __shared__ int s_wave[kWaves];
+  __shared__ int s_e[kMaxPicks], s_r0[kMaxPicks], s_rows[kMaxPicks];  // per slot: expert, first row, rows
+  __shared__ int s_id[kMaxPicks], s_prow[kMaxPicks], s_both[kMaxPicks];   // per pick t*K+j: expert, packed row
+  __shared__ float s_pw[kMaxPicks];                                        // ... and routing weight
+  __shared__ int s_rt[kMaxPicks];                                          // token of each packed row
+  __shared__ int s_nact;
   __shared__ float s_dgl[kMaxDown];  // globals of this workgroup's down tiles
   __shared__ int s_last[kMaxDown];   // 1: this workgroup combines that tile's 16 columns
   __shared__ float s_red[XREG ? kBatch * NB * kWaves * 64 : kWaves * kMaxRows * NB * 16];
@@ -618,45 +624,52 @@ __global__ void __launch_bounds__(kThreads) k_decode_layer(LayerArgs a) {
     }
   }
 
-  // active routed experts in ascending id -> slots (every workgroup, in LDS)
-  const ProjProblem &ru = lp.up[1];
-  const int E = ru.n_experts;
-  const int per = (E + kThreads - 1) / kThreads;  // <= 2
-  const int eb = tid * per;
-  int flags = 0, cnt_local = 0;
-  int offs[3];
-#pragma unroll
-  for (int i = 0; i < 3; ++i) offs[i] = (i <= per) ? ru.offsets[min(eb + i, E)] : 0;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    if (i < per && eb + i < E) {
-      const int r0 = offs[i], c = offs[i + 1] - offs[i];
-      if (c >= 1 && c <= ru.max_rows && r0 >= 0 && r0 <= ru.n_rows - c) {
-        flags |= 1 << i;
-        ++cnt_local;
-      }
-    }
-  }
-  const int incl = wave_scan_incl(cnt_local, lane);
-  if (lane == 63) s_wave[wave] = incl;
-  __syncthreads();
-  int base = 0, n_active = 0;
-  for (int w = 0; w < kWaves; ++w) {
-    base += w < wave ? s_wave[w] : 0;
-    n_active += s_wave[w];
-  }
-  int slot = base + incl - cnt_local;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    if ((flags >> i) & 1) {
-      s_e[slot] = eb + i;
-      s_r0[slot] = offs[i];
-      s_rows[slot] = offs[i + 1] - offs[i];
-      ++slot;
+  // this launch's count: the value every flag holds until its owner finishes
+  // its up tiles (read early, used late)
+  const int32_t epoch = __hip_atomic_load(&up_flag[blockIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // routing: wavefront t picks token t's top-K experts and their weights
+  const int E = lp.n_experts, K = lp.top_k, P = n * K;
+  if (wave < n) {
+    int my_id;
+    float my_w;
+    route_one_token_any(lp.logits + (size_t)wave * E, E, K, lane, my_id, my_w);
+    if (lane < K) {
+      s_id[wave * K + lane] = my_id;
+      s_pw[wave * K + lane] = my_w;
     }
   }
   __syncthreads();
-  if (blockIdx.x == 0 && tid == 0) __hip_atomic_store(lp.sync + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // gather layout (picks in wavefront 0, P <= 64): rows grouped by expert in
+  // ascending id, tokens ascending within an expert; a slot per distinct
+  // expert, in ascending id.  s_both[p]: token 0's pick p is also token 1's.
+  if (tid < P) {
+    const int e = s_id[tid], t = tid >= K;
+    int other = 0;
+    for (int q = t ? 0 : K; q < (t ? K : P); ++q) other |= s_id[q] == e;
+    s_both[tid] = t == 0 && other;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the flags are written
+    __builtin_amdgcn_wave_barrier();
+    int below = 0, dup_below = 0, n_dup = 0;
+    for (int q = 0; q < P; ++q) {
+      const int eq = s_id[q], bq = q < K ? s_both[q] : 0;
+      below += eq < e;
+      dup_below += bq && eq < e;
+      n_dup += bq;
+    }
+    const int r = below + (t == 1 && other);
+    s_prow[tid] = r;
+    s_rt[r] = t;
+    if (t == 0 || !other) {
+      const int slot = below - dup_below;
+      s_e[slot] = e;
+      s_r0[slot] = below;
+      s_rows[slot] = 1 + (t == 0 && other);
+    }
+    if (tid == 0) s_nact = P - n_dup;
+  }
+  __syncthreads();
+  const int n_active = s_nact;
 
   // the four projections, read once
   const ProbView U0 = view_of(lp.up[0], lp.h[0], lp.fs), U1 = view_of(lp.up[1], lp.h[1], lp.f);
@@ -683,7 +696,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_layer(LayerArgs a) {
   //  issued before it.
   WRegs<NB, KU> RU[kMaxUp];
   float ugl[kMaxUp];
-  int utok[kMaxUp][kMaxRows];  // raw row_token entries, resolved where used
+  int utok[kMaxUp][kMaxRows];  // token of each row of the tile's expert
   bool uok[kMaxUp];
 #pragma unroll
   for (int u = 0; u < kMaxUp; ++u) {
@@ -696,7 +709,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_layer(LayerArgs a) {
     issue_weights<NB, KU>(p, e, uok[u] ? t.tile : 0, lane, wave, RU[u]);
     ugl[u] = p.global[e];
 #pragma unroll
-    for (int r = 0; r < kMaxRows; ++r) utok[u][r] = U1.row_map[min(r0 + r, lp.n_rows - 1)];
+    for (int r = 0; r < kMaxRows; ++r) utok[u][r] = s_rt[min(r0 + r, P - 1)];
   }
   float dgl = 0.f;  // thread i: global of down tile d_first + i
   {
@@ -714,6 +727,21 @@ __global__ void __launch_bounds__(kThreads) k_decode_layer(LayerArgs a) {
       off += round_kb(cb) + round_kb(sb);
       if (tid == i - d_first) dgl = p.global[e];
     }
+  }
+  // workgroup 0: the routing and layout views, while the weights stream in
+  if (blockIdx.x == 0) {
+    if (tid < P) {
+      lp.ids[tid] = s_id[tid];
+      lp.topk_w[tid] = s_pw[tid];
+      lp.rows[tid] = s_prow[tid];
+      lp.row_token[tid] = s_rt[tid];
+    }
+    for (int e = tid; e <= E; e += kThreads) {
+      int below = 0;
+      for (int q = 0; q < P; ++q) below += s_id[q] < e;
+      lp.offsets[e] = below;
+    }
+    if (tid == 0) __hip_atomic_fetch_add(lp.sync + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   memory_done();
   if (tid < d_last - d_first) s_dgl[tid] = dgl;
@@ -780,7 +808,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_layer(LayerArgs a) {
     }
   }
   memory_done();
-  if (tid == 0) __hip_atomic_store(&up_flag[blockIdx.x], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(&up_flag[blockIdx.x], epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- 3. down tiles, each once its expert's h is complete
   long off = 0;
@@ -812,7 +840,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_layer(LayerArgs a) {
         const int ups = lp.has_shared ? a.up_tiles[0] : 0;
         const int u0 = t.prob == 0 ? 0 : ups + t.slot * a.up_tiles[1];
         const int u1 = u0 + a.up_tiles[t.prob] - 1;
-        wait_flags(up_flag, up_owner(u0, a.n_up, a.grid), up_owner(u1, a.n_up, a.grid), lane, err);
+        wait_flags(up_flag, up_owner(u0, a.n_up, a.grid), up_owner(u1, a.n_up, a.grid), epoch + 1, lane, err);
       }
       __syncthreads();
       const long ldh = p.ldh;
@@ -867,9 +895,10 @@ __global__ void __launch_bounds__(kThreads) k_decode_layer(LayerArgs a) {
     const Tile t = down_tile(a, d_first + i);
     int last = 0;
     if (t.prob == 0 || t.slot < n_active) {
-      const int old =
-          __hip_atomic_fetch_add(&ct_done[t.tile * kCtStride], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int32_t *ct = &ct_done[t.tile * kCtStride];
+      const int old = __hip_atomic_fetch_add(ct, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       last = old == lp.has_shared + n_active - 1;
+      if (last) __hip_atomic_store(ct, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next launch
     }
     s_last[i] = last;
   }
@@ -884,24 +913,29 @@ __global__ void __launch_bounds__(kThreads) k_decode_layer(LayerArgs a) {
       const float sh = lp.has_shared ? __hip_atomic_load(o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
       float accw = 0.f;
       // the routed outputs in groups of eight: their loads in flight together
-      for (int j0 = 0; j0 < lp.top_k; j0 += 8) {
+      for (int j0 = 0; j0 < K; j0 += 8) {
         float y[8];
         int ok[8];
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
           const int j = j0 + jj;
-          const int r = j < lp.top_k ? lp.rows[(size_t)tok * lp.top_k + j] : -1;
-          ok[jj] = r >= 0 && r < lp.n_rows;
-          y[jj] = ok[jj] ? __hip_atomic_load(lp.yg + (size_t)r * lp.d + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+          ok[jj] = j < K;
+          y[jj] = ok[jj] ? __hip_atomic_load(lp.yg + (size_t)s_prow[tok * K + j] * lp.d + c, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT)
                          : 0.f;
         }
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj)
-          if (ok[jj]) accw = fmaf(lp.w[(size_t)tok * lp.top_k + j0 + jj], y[jj], accw);
+          if (ok[jj]) accw = fmaf(s_pw[tok * K + j0 + jj], y[jj], accw);
       }
       *o = lp.has_shared ? sh + accw : accw;
     }
   }
+}
+
+__global__ void k_zero_words(int32_t *w, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) w[i] = 0;
 }
 
 template <int NB, int KU, int EPI, bool XF, bool XR>
@@ -942,12 +976,17 @@ hipError_t launch_x(LayerArgs &a, bool xreg, size_t lds, hipStream_t stream) {
 
 }  // namespace
 
-size_t decode_layer_sync_words(int max_slots, int d) {
-  (void)max_slots;
-  return (size_t)(2 + kMaxGrid + (d + 15) / 16 * kCtStride);
+size_t decode_layer_sync_words() { return (size_t)kSyncWords; }
+
+bool decode_layer_takes(int n_tokens, int top_k, int d_model) {
+  return n_tokens >= 1 && n_tokens <= kMaxRows && top_k >= 1 && n_tokens * top_k <= kMaxPicks &&
+         d_model >= 16 && (d_model + 15) / 16 <= kMaxCt;
 }
 
-bool decode_layer_takes(int n_tokens) { return n_tokens >= 1 && n_tokens <= kMaxRows; }
+hipError_t decode_layer_init(int32_t *sync, hipStream_t stream) {
+  hipLaunchKernelGGL(k_zero_words, dim3((kSyncWords + 255) / 256), dim3(256), 0, stream, sync, kSyncWords);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_layer(const DecodeLayerProblem &lp, hipStream_t stream) {
   LayerArgs a;
@@ -960,7 +999,10 @@ hipError_t launch_decode_layer(const DecodeLayerProblem &lp, hipStream_t stream)
   a.n_down = (lp.has_shared ? a.down_tiles : 0) + lp.max_slots * a.down_tiles;
   const bool swiglu = lp.act == EPI_SWIGLU;
   // the shared expert is relu^2: with a gated routed FFN it keeps its own launches
-  if (!decode_layer_takes(n) || (swiglu && lp.has_shared) || d % 32 != 0) return hipErrorNotSupported;
+  if (!decode_layer_takes(n, lp.top_k, d) || (swiglu && lp.has_shared) || d % 32 != 0) return hipErrorNotSupported;
+  if (lp.n_experts < lp.top_k || lp.n_experts > MOE_MAX_EXPERTS || lp.n_rows != n * lp.top_k)
+    return hipErrorNotSupported;
+  if (lp.max_slots != (lp.n_experts < lp.n_rows ? lp.n_experts : lp.n_rows)) return hipErrorNotSupported;
   if ((long)n * d * (lp.x_f32 ? 4 : 2) > 16L * kThreads * kXChunks) return hipErrorNotSupported;
   // k-group iterations of an up tile per lane
   const int ku = ((d / 32 + kWaves - 1) / kWaves + 3) / 4;

@@ -135,7 +135,7 @@ template <bool ROUTE>
 __global__ void __launch_bounds__(kSmallThreads)
 k_gather_small(const float *__restrict__ logits, float *__restrict__ topk_w, int32_t *ids, int n, int K, int E,
                int32_t *__restrict__ offsets, int32_t *__restrict__ row_token, int32_t *__restrict__ rows,
-               const void *x, int row_bytes, void *xg, int32_t *zero_words, int n_zero) {
+               const void *x, int row_bytes, void *xg) {
   __shared__ uint32_t s_bits[kSmallWords];
   __shared__ int32_t s_ids[kSmallPicks];
   __shared__ int32_t s_rt[kSmallPicks];
@@ -152,7 +152,6 @@ k_gather_small(const float *__restrict__ logits, float *__restrict__ topk_w, int
   uint32_t *prefix = s_bits + E * W;
 
   for (int i = tid; i < E * W; i += blockDim.x) bits[i] = 0u;
-  for (int i = tid; i < n_zero; i += blockDim.x) zero_words[i] = 0;
   if (ROUTE) {
     if (n * E <= kRankPairs) {
       route_by_rank(logits, n, E, K, s_logit, s_rank, s_sel, ids, topk_w, s_ids);
@@ -387,7 +386,7 @@ hipError_t launch_gather(const void *x, int elem_bytes, int n_tokens, int d_mode
   if (small_path(n_tokens, top_k, n_experts, row_bytes)) {
     hipLaunchKernelGGL(k_gather_small<false>, dim3(1), dim3(kSmallThreads), 0, stream, nullptr, nullptr,
                        const_cast<int32_t *>(ids), n_tokens, top_k, n_experts, offsets, row_token, rows, x,
-                       row_bytes, xg, nullptr, 0);
+                       row_bytes, xg);
     return hipGetLastError();
   }
   const int W = (n_tokens + 31) / 32;
@@ -414,10 +413,9 @@ hipError_t launch_gather(const void *x, int elem_bytes, int n_tokens, int d_mode
 
 hipError_t launch_route_gather_small(const float *logits, int n_tokens, int n_experts, int top_k, int32_t *ids,
                                      float *weights, const void *x, int elem_bytes, int d_model, void *xg,
-                                     int32_t *offsets, int32_t *row_token, int32_t *rows, int32_t *zero_words,
-                                     int n_zero, hipStream_t stream) {
+                                     int32_t *offsets, int32_t *row_token, int32_t *rows, hipStream_t stream) {
   hipLaunchKernelGGL(k_gather_small<true>, dim3(1), dim3(kSmallThreads), 0, stream, logits, weights, ids, n_tokens,
-                     top_k, n_experts, offsets, row_token, rows, x, elem_bytes * d_model, xg, zero_words, n_zero);
+                     top_k, n_experts, offsets, row_token, rows, x, elem_bytes * d_model, xg);
   return hipGetLastError();
 }
 

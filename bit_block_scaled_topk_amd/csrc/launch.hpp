@@ -18,12 +18,10 @@ hipError_t launch_route_topk(const float *logits, int n_tokens, int n_experts, i
 size_t gather_workspace_bytes(int n_tokens, int n_experts);
 bool gather_is_single_launch(int n_tokens, int top_k, int n_experts, int elem_bytes, int d_model);
 // Routing of every token and the whole gather in one workgroup (requires
-// gather_is_single_launch).  It also zeroes zero_words[0, n_zero) (the
-// counters of the persistent decode layer launched after it).
+// gather_is_single_launch).
 hipError_t launch_route_gather_small(const float *logits, int n_tokens, int n_experts, int top_k, int32_t *ids,
                                      float *weights, const void *x, int elem_bytes, int d_model, void *xg,
-                                     int32_t *offsets, int32_t *row_token, int32_t *rows, int32_t *zero_words,
-                                     int n_zero, hipStream_t stream);
+                                     int32_t *offsets, int32_t *row_token, int32_t *rows, hipStream_t stream);
 hipError_t launch_gather(const void *x, int elem_bytes, int n_tokens, int d_model,
                          const int32_t *ids, int top_k, int n_experts, void *xg,
                          int32_t *offsets, int32_t *row_token, int32_t *rows, void *workspace,
@@ -79,15 +77,17 @@ hipError_t launch_dq_gemv(ProjProblem *probs, const int *max_active, int count, 
 // Prefill path: up to two problems in one launch; bf16 activations (plane 0).
 hipError_t launch_dq_gemm(ProjProblem *probs, int count, int epi, hipStream_t stream);
 
-// The expert FFN of a decode step (n_tokens <= 2) in one persistent launch:
-// up[0]/down[0] the shared expert (ignored unless has_shared), up[1]/down[1]
-// the routed experts (up[1] carries expert_offsets, n_experts, n_rows,
-// max_rows and row_map = row_token); weights only are read from the problems.
-// h[0] ([n][fs]) and h[1] ([n_rows][f]) are fp32 scratch; out gets
-// (shared ? shared : 0) + sum_j w[t][j] * yg[rows[t][j]].  sync holds
-// decode_layer_sync_words() int32 words, zero at launch.  Returns
-// hipErrorNotSupported for shapes it does not take (the caller then uses the
-// per-step launches).
+// A whole decode step (n_tokens <= 2) in one persistent launch: routing, the
+// gather layout, the shared expert (up[0]/down[0], ignored unless has_shared)
+// and the routed experts (up[1]/down[1]; only their weights and shapes are
+// read), and the combine.  h[0] ([n][fs]) and h[1] ([n*K][f]) are fp32
+// scratch; out gets (shared ? shared : 0) + sum_j w[t][j] * yg[rows[t][j]].
+// The routing and layout views (ids, topk_w, offsets, row_token, rows) are
+// written as by the separate routing and gather launches.  sync points to
+// decode_layer_sync_words() int32 words that decode_layer_init zeroed once;
+// every launch leaves them ready for the next (sync[0]: set once a bounded
+// wait expires; sync[1]: launches so far).  Returns hipErrorNotSupported for
+// shapes it does not take (the caller then uses the per-step launches).
 struct DecodeLayerProblem {
   ProjProblem up[2], down[2];
   bool has_shared;
@@ -95,15 +95,17 @@ struct DecodeLayerProblem {
   int act;             // EPI_RELU2 or EPI_SWIGLU (routed up projection)
   const void *x;       // [n][d] activations
   bool x_f32;          // else bf16
+  const float *logits; // [n][n_experts]
   float *h[2];
   float *out, *yg;
-  const int32_t *rows;
-  const float *w;
-  int n_tokens, top_k, d, f, fs, n_rows;
+  int32_t *ids, *rows, *offsets, *row_token;
+  float *topk_w;
+  int n_tokens, n_experts, top_k, d, f, fs, n_rows;
   int32_t *sync;
 };
-size_t decode_layer_sync_words(int max_slots, int d);
-bool decode_layer_takes(int n_tokens);
+size_t decode_layer_sync_words();
+bool decode_layer_takes(int n_tokens, int top_k, int d_model);
+hipError_t decode_layer_init(int32_t *sync, hipStream_t stream);
 hipError_t launch_decode_layer(const DecodeLayerProblem &lp, hipStream_t stream);
 
 }  // namespace moe

@@ -89,6 +89,8 @@ class LayerViews(ctypes.Structure):
 
 _lib.moe_layer_workspace_size.argtypes = [ctypes.POINTER(LayerDesc)]
 _lib.moe_layer_workspace_size.restype = _SZ
+_lib.moe_layer_workspace_init.argtypes = [ctypes.POINTER(LayerDesc), _P, _SZ, _P]
+_lib.moe_layer_workspace_init.restype = _I
 _lib.moe_layer_get_views.argtypes = [ctypes.POINTER(LayerDesc), _P, ctypes.POINTER(LayerViews)]
 _lib.moe_layer_get_views.restype = _I
 _lib.moe_layer_forward.argtypes = [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _SZ, _P]
@@ -99,7 +101,8 @@ _lib.moe_layer_forward_profiled.restype = _I
 EXPORTED = ("moe_route_topk", "moe_gather_workspace_size", "moe_gather_rows",
             "nvfp4_expert_ffn_workspace_size", "nvfp4_grouped_linear_workspace_size",
             "nvfp4_expert_ffn", "moe_weighted_row_sum", "moe_weighted_row_sum_into", "nvfp4_unpack_bf16",
-            "nvfp4_grouped_linear", "moe_status_string", "moe_layer_workspace_size", "moe_layer_get_views",
+            "nvfp4_grouped_linear", "moe_status_string", "moe_layer_workspace_size",
+            "moe_layer_workspace_init", "moe_layer_get_views",
             "moe_layer_forward", "moe_layer_forward_profiled")
 
 
@@ -254,6 +257,11 @@ def moe_layer_workspace_size(desc: LayerDesc) -> int:
     return int(_lib.moe_layer_workspace_size(ctypes.byref(desc)))
 
 
+def moe_layer_workspace_init(desc: LayerDesc, workspace: torch.Tensor, stream=None) -> None:
+    _check("moe_layer_workspace_init", _lib.moe_layer_workspace_init(
+        ctypes.byref(desc), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 def moe_layer_get_views(desc: LayerDesc, workspace: torch.Tensor) -> LayerViews:
     v = LayerViews()
     _check("moe_layer_get_views", _lib.moe_layer_get_views(ctypes.byref(desc), _ptr(workspace), ctypes.byref(v)))
@@ -359,6 +367,7 @@ class MoELayer:
                  nvfp4_expert_ffn_workspace_size(n, d, max(self.fs, 32), self.x_dtype))
         self.workspace = torch.empty((ws,), dtype=torch.uint8, device=dev)
         self.layer_ws = torch.empty((moe_layer_workspace_size(self.desc(None, n)),), dtype=torch.uint8, device=dev)
+        moe_layer_workspace_init(self.desc(None, n), self.layer_ws)
 
     def weights(self):
         return (self.up, self.down, self.shared_up, self.shared_down)

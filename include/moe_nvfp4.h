@@ -237,19 +237,28 @@ typedef struct {
   int32_t *row_token;      /* [n*K] */
   int32_t *rows;           /* [n][K] */
   float *yg;               /* [n*K][d]: each routed expert's output rows */
-  int32_t *wait_error;     /* one word: nonzero after a call of the single-launch
-                              decode layer (below) in which a bounded
-                              inter-workgroup wait expired; that call's results
-                              are then invalid. */
-  int32_t *decode_launch;  /* one word: 1 after a call that ran the single-launch
-                              decode layer.  Both words are cleared by every
-                              call whose routing and gather share one launch. */
+  int32_t *wait_error;     /* one word: nonzero once a bounded inter-workgroup
+                              wait of the single-launch decode step (below)
+                              has expired -- that call's results are invalid;
+                              it stays set until moe_layer_workspace_init. */
+  int32_t *decode_launch;  /* one word: calls since moe_layer_workspace_init
+                              that ran the single-launch decode step. */
 } moe_layer_views;
 /* (moe_layer_forward does not materialise the packed activation rows: the
  * routed up projection reads x[row_token[r]] directly.) */
 
 /* Workspace bytes moe_layer_forward needs (0 for an invalid description). */
 size_t moe_layer_workspace_size(const moe_layer_desc *desc);
+
+/* Prepare a layer workspace for moe_layer_forward: clears the flags and
+ * counters at its start (with a kernel on `stream`; nothing is allocated).
+ * Required once after the workspace is allocated, before its first
+ * moe_layer_forward; every later call leaves them ready for the next, for any
+ * description whose workspace size fits ws_bytes.  A workspace belongs to one
+ * device.  MOE_INVALID_ARG for a bad description or an unaligned (256-byte)
+ * workspace, MOE_WORKSPACE_TOO_SMALL if ws_bytes < moe_layer_workspace_size. */
+moe_status moe_layer_workspace_init(const moe_layer_desc *desc, void *workspace, size_t ws_bytes,
+                                    hipStream_t stream);
 
 /* Fill `views` with the intermediates' addresses inside `workspace`. */
 moe_status moe_layer_get_views(const moe_layer_desc *desc, void *workspace, moe_layer_views *views);
@@ -260,13 +269,14 @@ moe_status moe_layer_get_views(const moe_layer_desc *desc, void *workspace, moe_
  * workgroup for small batches, the shared and the routed experts share each
  * up and each down launch, and nothing synchronises or allocates (Glq v0.2.13
  * "Remaining gap to bf16-native": fewer launches per layer).  For a decode
- * step -- routing and gather fit one workgroup, n_tokens <= min(2,
- * gemv_max_rows) and the weights fit the LDS of the CUs -- the up projections,
- * down projections and combine are ONE persistent launch whose workgroups hand
- * results to each other through counters in the workspace (waits are bounded;
- * see moe_layer_views.wait_error); its dot products run in fp32 on the vector
- * ALUs, so it agrees with the four calls to fp32 rounding rather than bit for
- * bit.  Calls that overlap on one workspace race.
+ * step -- n_tokens <= min(2, gemv_max_rows), d_model <= 16384 and the weights
+ * fit the LDS of the CUs -- the whole layer (routing, gather layout, up and
+ * down projections, combine) is ONE persistent launch whose workgroups hand
+ * results to each other through flags and counters in the workspace (waits
+ * are bounded; see moe_layer_views.wait_error); its dot products run in fp32
+ * on the vector ALUs, so it agrees with the four calls to fp32 rounding rather
+ * than bit for bit.  The workspace must have been prepared by
+ * moe_layer_workspace_init.  Calls that overlap on one workspace race.
  *   x       device [n][d] of desc->x_dtype (16-byte aligned)
  *   logits  device float [n][E]
  *   out     device float [n][d] (written, not accumulated)
@@ -279,7 +289,7 @@ moe_status moe_layer_forward(const moe_layer_desc *desc, const void *x, const fl
  * enabled) are recorded on `stream` before routing, after routing + gather,
  * after the activation split, after the up projections, after the down
  * projections and after the combine, so each phase's GPU time can be read
- * with hipEventElapsedTime.  With the single-launch decode layer, events 3..5
+ * with hipEventElapsedTime.  With the single-launch decode step, events 1..5
  * are all recorded after that launch.  events == NULL records nothing. */
 moe_status moe_layer_forward_profiled(const moe_layer_desc *desc, const void *x, const float *logits,
                                       float *out, void *workspace, size_t ws_bytes, hipEvent_t *events,

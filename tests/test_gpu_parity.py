@@ -400,8 +400,8 @@ def test_layer_forward_fused(ops, name):
         assert normwise(got, ref["out"]) <= TOL_DECODE
     assert int(host(v["wait_error"])[0]) == 0
     single = inp.n <= 2
-    if inp.n <= 64:  # routing and gather share one launch, which clears the word
-        assert int(host(v["decode_launch"])[0]) == (1 if single else 0)
+    # calls since the workspace was prepared that ran the single-launch step
+    assert int(host(v["decode_launch"])[0]) == (1 if single else 0)
     unfused = layer.forward(x, lg).clone()
     torch.cuda.synchronize()
     if single:  # fp32 dot products on the vector ALUs: equal to fp32 rounding
@@ -431,7 +431,8 @@ SINGLE_LAUNCH_CASES = [
 def test_layer_single_launch_decode(ops, case):
     """Back-to-back fused calls with different routings: each matches the
     oracle, leaves no expired wait, agrees with the four-call path (bit for bit
-    where the per-step launches run) and repeats bit for bit."""
+    where the per-step launches run) and repeats bit for bit; the last call's
+    routing and layout views match the oracle's."""
     name, ov, single = SINGLE_LAUNCH_CASES[case]
     inp = cached_layer(name, **ov)
     print(f"single-launch case {name} {ov}", flush=True)
@@ -445,8 +446,15 @@ def test_layer_single_launch_decode(ops, case):
     ran = host(v["decode_launch"]).copy()
     torch.cuda.synchronize()
     assert int(errs[0]) == 0
-    assert int(ran[0]) == (1 if single else 0)
+    assert int(ran[0]) == (3 if single else 0)
     assert torch.equal(outs[0], outs[2])
+    ids, w = oracle.route_topk(inp.logits, inp.K)
+    off, row_token, rows = oracle.gather_layout(ids, inp.E)
+    assert np.array_equal(host(v["ids"]), ids)
+    assert np.max(np.abs(host(v["w"]).astype(np.float64) - w)) <= 4e-7
+    assert np.array_equal(host(v["offsets"]), off)
+    assert np.array_equal(host(v["rows"]), rows)
+    assert np.array_equal(host(v["row_token"]), row_token)
     for lg_host, lg, got in zip(logit_sets, lgs, outs):
         ref = oracle.layer(inp, routing=oracle.route_topk(lg_host, inp.K))
         assert normwise(host(got).astype(np.float64), ref["out"]) <= TOL_DECODE
@@ -456,6 +464,26 @@ def test_layer_single_launch_decode(ops, case):
             assert normwise(host(got).astype(np.float64), host(unfused).astype(np.float64)) <= 2e-6
         else:
             assert torch.equal(got, unfused)
+
+
+def test_layer_single_launch_token_counts(ops):
+    """One workspace, prepared once, serves single-launch steps of one and of
+    two tokens in any order (its flags and counters carry over between
+    calls of different sizes)."""
+    inp = cached_layer("decode1", n=2, K=3, E=32, fs=1856, seed=19)
+    layer = ops.MoELayer(inp)
+    x, lg = dev(inp.x), dev(inp.logits)
+    order = [2, 1, 1, 2, 1, 2, 2]
+    outs = [layer.forward_fused(x[:m], lg[:m]).clone()[:m] for m in order]
+    v = layer.views(1)
+    errs = host(v["wait_error"]).copy()
+    ran = host(v["decode_launch"]).copy()
+    torch.cuda.synchronize()
+    assert int(errs[0]) == 0
+    assert int(ran[0]) == len(order)
+    full = oracle.layer(inp)["out"]
+    for m, got in zip(order, outs):
+        assert normwise(host(got).astype(np.float64), full[:m]) <= TOL_DECODE
 
 
 @pytest.mark.parametrize("name", ["decode1", "decode32_zipf"])
