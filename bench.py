@@ -13,9 +13,20 @@ weights in the 256 MB Infinity Cache.  Steps are replayed from a HIP graph
 (the layer allocates and synchronises nothing, so it captures whole).
 
 Prints ONE JSON line with the contract fields plus:
-  roofline      the routed-expert FFN of a step (its two decode GEMV launches,
-                timed with HIP events on the launch stream in an eager pass
-                over the same copies): algorithmic bytes / duration vs 8 TB/s
+  roofline      the step's dominant kernel against its roofline.  A decode
+                step of one or two tokens is one launch (k_decode_layer):
+                its average duration is the timed region measured with HIP
+                events on the launch stream, divided by the launches in it,
+                and it is held against 8 TB/s with the step's algorithmic
+                bytes (the picked experts' and the shared expert's NVFP4
+                weights once, x, the logits, the output).  A prefill step's
+                dominant kernel is the grouped GEMM (k_dq_gemm: one up and one
+                down launch), timed with HIP events between the library's
+                launch phases, against the dense bf16 matrix-core peak.
+                `traffic` is the HBM bytes per launch that rocprofv3 counted
+                (FETCH_SIZE + WRITE_SIZE, scaled by what the counters read for
+                a plain copy), taken from profiles/ only while the kernel's
+                sources are the ones that were counted (else null).
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -44,9 +55,6 @@ def parse():
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
-    p.add_argument("--traffic", default=None,
-                   help="JSON file with the measured HBM bytes per launch of the dominant kernel "
-                        "(from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
     p.add_argument("--copy-probe-mb", type=int, default=0,
                    help="only run a plain device-to-device copy of this many MiB, 5 times (the "
                         "reference for scaling FETCH_SIZE / WRITE_SIZE), then exit")
@@ -63,6 +71,38 @@ def copy_probe(mb: int):
     print(json.dumps({"copy_probe_bytes": mb << 20, "launches": 5}))
 
 
+DECODE_KERNEL_SOURCES = ("dq_layer.hip", "nvfp4_device.hpp", "route_device.hpp")
+
+
+def kernel_source_digest(files=DECODE_KERNEL_SOURCES) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "bit_block_scaled_topk_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of k_decode_layer from the committed counter
+    summary for this workload, if it was taken from the current sources."""
+    path = os.path.join(ROOT, "profiles", f"k_decode_layer_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_sources_sha256") != kernel_source_digest():
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def weight_bytes(t) -> int:
     return int(t.codes.nbytes + t.scales.nbytes + t.globals_.nbytes)
 
@@ -71,20 +111,18 @@ def per_expert_bytes(t) -> int:
     return weight_bytes(t) // t.n_experts
 
 
-def layer_ffn_bytes(inp, ids) -> dict:
-    """Algorithmic bytes of one step's expert FFN launches (the up and the down
-    decode GEMV, shared + routed experts): every picked expert's and the shared
-    expert's NVFP4 weights once (codes + scales + global), the activations read,
-    h written and read once at fp32, the expert outputs written at fp32."""
+def decode_step_bytes(inp, ids) -> dict:
+    """Algorithmic HBM bytes of one decode step: each picked expert's and the
+    shared expert's NVFP4 weights once (codes + scales + global), x, the
+    logits, the output written.  The intermediates (h, the expert outputs)
+    pass between workgroups through the caches and are not counted."""
     import numpy as np
     distinct = len(np.unique(ids))
-    R = inp.n * inp.K
     xb = 4 if inp.x_dtype == "f32" else 2
     w = distinct * (per_expert_bytes(inp.up) + per_expert_bytes(inp.down))
-    act = R * inp.d * xb + 2 * R * inp.f * 4 + R * inp.d * 4
     if inp.fs > 0:
         w += weight_bytes(inp.shared_up) + weight_bytes(inp.shared_down)
-        act += inp.n * inp.d * xb + 2 * inp.n * inp.fs * 4 + inp.n * inp.d * 4
+    act = inp.n * inp.d * xb + inp.n * inp.E * 4 + inp.n * inp.d * 4
     return dict(weights=w, activations=act, total=w + act, distinct_experts=distinct)
 
 
@@ -183,17 +221,23 @@ def main():
         torch.cuda.synchronize()
 
     # ---- timed region: exactly `steps` layer steps ----
+    launches0 = int(layer.views()["decode_launch"].cpu()[0])
+    ev_start, ev_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
+        ev_start.record()  # on `stream`, the launch stream
         if graph is not None:
             for _ in range(steps // L):
                 graph.replay()
         else:
             for i in range(steps):
                 layer.forward_fused(x, logits, weights=copies[i % L])
+        ev_end.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    region_us = ev_start.elapsed_time(ev_end) * 1e3
+    single_launch = int(layer.views()["decode_launch"].cpu()[0]) - launches0 == steps
     tokens_per_s = inp.n * steps / elapsed
 
     # ---- kernel timing: HIP events recorded by the library between its launch
@@ -211,28 +255,25 @@ def main():
     breakdown = {k: float(np.mean(v)) for k, v in phase.items()}
     v = layer.views()
     ids = v["ids"].cpu().numpy()
-    counts = np.diff(v["offsets"].cpu().numpy())
-    ffn_us = breakdown["up"] + breakdown["down"]
-    if counts.max() <= 32:
-        b = layer_ffn_bytes(inp, ids)
-        achieved = b["total"] / (ffn_us * 1e-6) / 1e9
+    if single_launch:
+        # one launch per step: the timed region's event time over its launches
+        us = region_us / steps
+        b = decode_step_bytes(inp, ids)
+        achieved = b["total"] / (us * 1e-6) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                    "kernel": "k_dq_gemv (decode dequant-GEMV: one up and one down launch per step, "
-                              "shared + routed experts)",
-                    "bytes_per_launch": b["total"] // 2, "us_per_launch": round(ffn_us / 2, 3),
-                    "bytes": b}
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(inp.name),
+                    "kernel": "k_decode_layer (the whole decode step in one persistent launch)",
+                    "bytes_per_launch": b["total"], "us_per_launch": round(us, 3), "bytes": b}
+        breakdown = {"decode_layer_eager": breakdown["route_gather"]}
     else:
         flops = layer_ffn_flops(inp)
+        ffn_us = breakdown["up"] + breakdown["down"]
         tf = flops / (ffn_us * 1e-6) / 1e12
         roofline = {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
                     "kernel": "k_dq_gemm (prefill grouped bf16 GEMM: one up and one down launch per step, "
                               "shared + routed experts)",
                     "flops_per_launch": flops // 2, "us_per_launch": round(ffn_us / 2, 3)}
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as fh:
-            roofline["traffic"] = json.load(fh).get("bytes_per_call")
 
     cpu = None
     if not args.no_cpu_baseline:
