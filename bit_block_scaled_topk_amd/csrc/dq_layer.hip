@@ -1,32 +1,38 @@
-// dq_layer.hip -- the expert FFN of a decode step (one or two tokens) in ONE
-// persistent launch: the shared and routed experts' up projections (+
-// activation), their down projections, and the WeightedRowSum combine (gllm PR
-// #91, "What changes"; Glq v0.2.13, "Remaining gap to bf16-native": a
-// single-launch parallel-experts kernel is the way past per-expert launches).
+// dq_layer.hip -- a whole decode step (one or two tokens) of the MoE layer in
+// ONE persistent launch: routing, the gather layout, the shared and routed
+// experts' up projections (+ activation), their down projections, and the
+// WeightedRowSum combine (gllm PR #91, "What changes"; Glq v0.2.13, "Remaining
+// gap to bf16-native": a single-launch parallel-experts kernel is the way past
+// per-expert launches).
 //
 // Work is split into 16-column tiles: every up tile of the shared expert and of
 // each active routed expert, then every down tile.  One workgroup per CU (all
-// resident); workgroup w owns a contiguous range of the up tiles (equal counts)
-// and a contiguous range of the down tiles (equal bytes).  Each workgroup
-// requests all of its weights before it computes anything, so the whole weight
-// stream is in flight at once and no tile waits out its own memory latency:
-//   1  x (registers, then LDS as fp32), its up tiles' weights (registers), its
-//      down tiles' weights (direct global->LDS copies); wait.
-//   2  compute the up tiles, store h (fp32); count each on its expert's
-//      counter.
+// resident).  Workgroups [0, gs) take the shared expert's tiles and the others
+// the routed experts' (gs in proportion to the bytes), each a contiguous range
+// of equal count.  Each workgroup requests all of its weights before it
+// computes anything, so the whole weight stream is in flight at once and no
+// tile waits out its own memory latency:
+//   0  the logits and x, then the routing; the shared expert's workgroups
+//      request their weights (step 1) before they route, the others after
+//      (they need the picks).
+//   1  up tiles' weights into registers, down tiles' weights into LDS (direct
+//      global->LDS copies); wait.
+//   2  compute the up tiles, store h (fp32); publish.
 //   3  for each down tile: wait for its expert's h, copy those h rows into LDS
 //      (once per expert), compute, store.
 //   4  count the down tiles; the last producer of a 16-column block of the
 //      output computes the combine for that block.
-// (Vector memory results return in issue order, so step 2 could not start
-// before the down weights land anyway.)
 //
 // With one or two tokens a 16-row matrix-core tile would be mostly padding, so
-// the dot products run on the vector ALUs in fp32: lane (n = lane%16, q =
-// lane/16) owns column n of the tile and, per iteration, k-group gb + 4i + q of
-// its wavefront's slice of K; the FP4 converter gives the exact e2m1 values;
-// each 16-element block's partial sum is scaled by its e4m3 scale; the four
-// q-lanes and then the eight wavefronts are summed in a fixed order.
+// the dot products run on the vector ALUs in fp32.  Half-wavefront hf of
+// wavefront w owns row 2w + hf of every tile (one output column) and its lane
+// c the 32-element k-groups c, c + 32, ...: the 32 lanes of a half read 512
+// contiguous bytes of one weight row per load, from HBM (up tiles) or from LDS
+// without bank conflicts (down tiles).  The FP4 converter gives the exact e2m1
+// values, each 16-element block's sum is scaled by its e4m3 scale, and the 32
+// lanes' sums are added by a fixed butterfly, so no workgroup-wide reduction
+// is needed.  Activations staged in LDS (x for two tokens or fp32 x, and h)
+// are transposed so that consecutive k-groups are 16 bytes apart.
 //
 // Results handed from one workgroup to another (h, the routed outputs yg, the
 // shared expert's output) are stored and loaded with device-coherent accesses
@@ -61,9 +67,10 @@
 // every flag and counter still ends as described.  No workgroup waits before
 // it has published all of its up tiles, so every wait ends once the whole grid
 // is resident (the host checks that with the occupancy query).
+#include <algorithm>
+
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
-#include "route_device.hpp"
 
 namespace moe {
 
@@ -74,19 +81,19 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kSpinLimit = 1 << 22;
 constexpr int kSc1 = 16;               // cache-policy bit of a buffer load: device-coherent access
 constexpr int kLdsLimit = 160 * 1024;  // LDS of one CU
+constexpr int kStaticLds = 11 * 1024;  // the kernel's own LDS arrays (checked exactly at launch)
 constexpr int kMaxUp = 4;              // up tiles one workgroup holds in registers
 constexpr int kMaxDown = 64;           // down tiles of one workgroup
 constexpr int kMaxRows = 2;            // token rows of the vector dot products
 constexpr int kXChunks = 4;            // 16-byte chunks of x per thread
-constexpr int kKD = 2;                 // k-group iterations of a down tile with h in registers
-constexpr int kKDMax = 4;              // ... with the rest read from LDS (one-token path)
-constexpr int kBatch = 4;              // one-token tiles whose sums are reduced together
+constexpr int kHReg = 2;               // one token: h k-group iterations kept in registers
 constexpr int kMaxGrid = 1024;         // workgroups (one per CU)
 constexpr int kCtStride = 16;          // words between column counters: one counter per 64 bytes (atomics
                                        // to one cache line serialise)
 constexpr int kMaxCt = 1024;           // column blocks: d <= 16384
 constexpr int kMaxPicks = kMaxRows * MOE_MAX_TOPK;  // routed rows of a step (<= 64: one wavefront)
 constexpr int kSyncWords = 2 + kMaxGrid + kMaxCt * kCtStride;
+constexpr int kLogitsPerThread = kMaxRows * MOE_MAX_EXPERTS / kThreads;
 
 struct LayerArgs {
   DecodeLayerProblem lp;
@@ -94,9 +101,10 @@ struct LayerArgs {
   int down_tiles;       // d / 16
   int n_up, n_down;     // tiles in the two lists
   long down_bytes[2];   // LDS bytes of one down tile's weights (shared, routed)
-  long down_total;      // LDS bytes of the whole down list
   int grid;
+  int gs;               // workgroups [0, gs) take the shared expert's tiles, the rest the routed ones
   int x_lds, h_lds;     // LDS bytes of x and of one expert's h (fp32)
+  int us_lds, us_blk;   // LDS bytes of the up tiles' scales, and of one 16-row block of them
 };
 
 struct Tile {
@@ -120,29 +128,36 @@ __device__ __forceinline__ Tile down_tile(const LayerArgs &a, int i) {
   return Tile{1, s, r - s * a.down_tiles};
 }
 
-// Byte offset of down tile i in the list (shared tiles first).
-__host__ __device__ __forceinline__ long down_prefix(int i, int n_shared_tiles, const long *bytes) {
-  return i <= n_shared_tiles ? (long)i * bytes[0]
-                             : (long)n_shared_tiles * bytes[0] + (long)(i - n_shared_tiles) * bytes[1];
+// Item range [first, last) of member v of a group of g that splits n items.
+__host__ __device__ __forceinline__ void split_range(int v, int g, int n, int &first, int &last) {
+  first = (int)((long)v * n / g);
+  last = (int)((long)(v + 1) * n / g);
 }
 
-// First down tile whose offset is >= byte position pos.
-__host__ __device__ __forceinline__ int down_first_at(long pos, int n_shared_tiles, int n_down, const long *bytes) {
-  const long sb = (long)n_shared_tiles * bytes[0];
-  long t;
-  if (pos <= sb)
-    t = bytes[0] > 0 ? (pos + bytes[0] - 1) / bytes[0] : 0;
-  else
-    t = n_shared_tiles + (pos - sb + bytes[1] - 1) / bytes[1];
-  return (int)(t < n_down ? t : n_down);
+// The member of a group of g splitting n items that holds item i.
+__host__ __device__ __forceinline__ int split_owner(int i, int n, int g) {
+  int w = (int)((long)i * g / n);
+  while (w + 1 < g && (long)(w + 1) * n / g <= i) ++w;
+  while (w > 0 && (long)w * n / g > i) --w;
+  return w;
 }
 
-// Down tiles [first, last) of workgroup w: those whose offsets fall in
-// [w * total / G, (w + 1) * total / G).
-__host__ __device__ __forceinline__ void down_range(int w, int grid, int n_shared_tiles, int n_down,
-                                                    const long *bytes, long total, int &first, int &last) {
-  first = down_first_at(total * w / grid, n_shared_tiles, n_down, bytes);
-  last = down_first_at(total * (w + 1) / grid, n_shared_tiles, n_down, bytes);
+// Tile ranges of workgroup w in a list of n_sh shared-expert tiles followed by
+// n - n_sh routed ones: workgroups [0, gs) split the shared tiles, the others
+// the routed tiles (both with equal counts; the tiles of a group are alike).
+__host__ __device__ __forceinline__ void group_range(int w, int grid, int gs, int n_sh, int n, int &first,
+                                                     int &last) {
+  if (w < gs) {
+    split_range(w, gs, n_sh, first, last);
+  } else {
+    split_range(w - gs, grid - gs, n - n_sh, first, last);
+    first += n_sh;
+    last += n_sh;
+  }
+}
+
+__host__ __device__ __forceinline__ int group_owner(int i, int grid, int gs, int n_sh, int n) {
+  return i < n_sh ? split_owner(i, n_sh, gs) : gs + split_owner(i - n_sh, n - n_sh, grid - gs);
 }
 
 __host__ __device__ __forceinline__ long round_kb(long b) { return (b + 1023) / 1024 * 1024; }
@@ -182,34 +197,33 @@ __device__ __forceinline__ ProbView pick(bool first, const ProbView &a, const Pr
   return r;
 }
 
-template <int NB, int KNI>
-struct WRegs {
-  u32x4_t wq[NB][KNI];
-  uint32_t sc[NB][KNI];
+// A lane's codes of one up tile: k-group iterations i = 0..KI-1 of NB rows
+// (NB = 2 for SwiGLU: the gate row and the up row).  (The tile's scales are
+// copied to LDS: 16 contiguous rows, a few 16-byte loads per tile instead of a
+// 2-byte load per lane and group.)
+template <int NB, int KI>
+struct RowW {
+  u32x4_t wq[NB][KI];
 };
 
-// Issue the weight loads of this lane's k-groups of one up tile (no waits).
-// NB = 2 (SwiGLU): rows col and col + n_out (gate and up) per lane.
-template <int NB, int KNI>
-__device__ __forceinline__ void issue_weights(const ProbView &p, int e, int tile, int lane, int wave,
-                                              WRegs<NB, KNI> &R) {
-  const int nl = lane & 15, q = lane >> 4;
+// Issue the code loads of this lane's k-groups of one up tile (no waits): lane
+// c of half hf reads k-groups c + 32 i of row 2 * wave + hf; the 32 lanes of a
+// half read 512 contiguous bytes per load.  Groups past the row repeat its
+// last group (their scale is zeroed where they are used).
+template <int NB, int KI>
+__device__ __forceinline__ void issue_rows(const ProbView &p, int e, int tile, int lane, int wave, RowW<NB, KI> &R) {
+  const int c = lane & 31;
   const int G = p.k >> 5;
-  const int gpw = (G + kWaves - 1) / kWaves;
-  const int gb = wave * gpw;
-  const int ge = min(G, gb + gpw);
-  const int col = min(tile * 16 + nl, p.n_out - 1);
-  const size_t crow = (size_t)(p.k >> 1), srow = (size_t)(p.k >> 4);
+  const int col = min(tile * 16 + 2 * wave + (lane >> 5), p.n_out - 1);
+  const size_t crow = (size_t)(p.k >> 1);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const size_t wr = (size_t)e * p.n_w + (size_t)col + (size_t)b * p.n_out;
     const uint8_t *wrow = p.codes + wr * crow;
-    const uint8_t *sptr = p.scales + wr * srow;
 #pragma unroll
-    for (int i = 0; i < KNI; ++i) {
-      const int gc = max(min(gb + 4 * i + q, ge - 1), 0);
+    for (int i = 0; i < KI; ++i) {
+      const int gc = min(c + 32 * i, G - 1);
       R.wq[b][i] = *(const u32x4_t *)(wrow + (size_t)gc * 16);
-      R.sc[b][i] = *(const uint16_t *)(sptr + (size_t)gc * 2);
     }
   }
 }
@@ -241,29 +255,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void *base
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
 }
 
+// Workgroup barrier for LDS only: unlike __syncthreads it does not wait for
+// this wavefront's outstanding global loads and stores.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ void memory_done() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): every copy, load and store of this wavefront has completed
   __syncthreads();
 }
-
-// Weights of a tile for one k-group: from registers (up tiles) or from the LDS
-// copy of the tile (down tiles: 16 code rows of k/2 bytes, then 16 scale rows
-// of k/16 bytes).
-template <int NB, int KNI>
-struct RegB {
-  const WRegs<NB, KNI> &R;
-  __device__ __forceinline__ void get(int b, int i, int, u32x4_t &wq, uint32_t &sc) const {
-    wq = R.wq[b][i];
-    sc = R.sc[b][i];
-  }
-};
-struct LdsB {
-  const uint8_t *codes, *scales;  // this lane's row
-  __device__ __forceinline__ void get(int, int, int g, u32x4_t &wq, uint32_t &sc) const {
-    wq = *(const u32x4_t *)(codes + g * 16);
-    sc = *(const uint16_t *)(scales + g * 2);
-  }
-};
 
 // 16 e2m1 codes (two words, element 0 in the low nibble of byte 0) times 16
 // fp32 activations: four chains of four elements in order, then
@@ -299,112 +302,6 @@ __device__ __forceinline__ float dot16(uint32_t w0, uint32_t w1, const float *x)
                 *(const f32x4_t *)(x + 12));
 }
 
-// Sum a tile's per-lane partials in a fixed order -- the four q-lanes
-// ((q0 + q1) + (q2 + q3)), then the wavefronts 0 + 1 + ... + 7 -- and store
-// output row r (< rows) at dst[(r0 + r) * ldo + column] (device-coherent):
-// gl * sum, or its activation (EPI_RELU2 / EPI_SWIGLU).  Ends with a
-// workgroup barrier.
-template <int NB, int EPI>
-__device__ __forceinline__ void reduce_store(float (&acc)[kMaxRows][NB], int rows, int n_out, float gl, int tile,
-                                             float *dst, long ldo, int r0, int lane, int wave, float *s_red) {
-  const int nl = lane & 15, q = lane >> 4;
-#pragma unroll
-  for (int r = 0; r < kMaxRows; ++r)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      float v = acc[r][b];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      if (q == 0) s_red[((wave * kMaxRows + r) * NB + b) * 16 + nl] = v;
-    }
-  __syncthreads();
-  if (wave == 0 && lane < 16) {
-    const int col = tile * 16 + nl;
-#pragma unroll
-    for (int r = 0; r < kMaxRows; ++r) {
-      if (r >= rows) break;
-      float sum[NB];
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        sum[b] = s_red[(r * NB + b) * 16 + nl];
-        for (int w = 1; w < kWaves; ++w) sum[b] += s_red[((w * kMaxRows + r) * NB + b) * 16 + nl];
-      }
-      float v;
-      if (EPI == EPI_F32) {
-        v = gl * sum[0];
-      } else if (EPI == EPI_RELU2) {
-        float u = gl * sum[0];
-        u = u > 0.f ? u : 0.f;
-        v = u * u;
-      } else {
-        const float av = gl * sum[0];
-        const float bv = gl * sum[NB - 1];
-        v = (av / (1.0f + expf(-av))) * bv;
-      }
-      if (col < n_out)
-        __hip_atomic_store(dst + (size_t)(r0 + r) * ldo + col, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  __syncthreads();  // s_red and the staged operands are reused next
-}
-
-// Lane (n, q) of wavefront w: k-group gb + 4i + q of the wavefront's slice.
-struct KSlice {
-  int gb, ge;
-  __device__ __forceinline__ KSlice(int k, int wave) {
-    const int G = k >> 5;
-    const int gpw = (G + kWaves - 1) / kWaves;
-    gb = wave * gpw;
-    ge = min(G, gb + gpw);
-  }
-};
-
-// One 16-column tile on the vector ALUs, activations from LDS: row r (< rows)
-// of the tile is LDS row xrow[r] of xs (pitch ldx floats).  KNI > 0: at most
-// KNI k-group iterations, unrolled (register weights); KNI == 0: a loop (LDS
-// weights).
-template <int NB, int KNI, int EPI, typename WSrc>
-__device__ __forceinline__ void tile_dot(int k, int n_out, float gl, int rows, const int *xrow, const float *xs,
-                                         int ldx, int tile, float *dst, long ldo, int r0, int lane, int wave,
-                                         const WSrc &ws, float *s_red) {
-  const int q = lane >> 4;
-  const KSlice ks(k, wave);
-  float acc[kMaxRows][NB];
-#pragma unroll
-  for (int r = 0; r < kMaxRows; ++r)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
-  auto body = [&](int i) {
-    const int g = ks.gb + 4 * i + q;
-    if (g >= ks.ge) return;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      u32x4_t wq;
-      uint32_t sc;
-      ws.get(b, i, g, wq, sc);
-      float s0, s1;
-      e4m3x2_to_f32(sc, s0, s1);
-#pragma unroll
-      for (int r = 0; r < kMaxRows; ++r) {
-        if (r >= rows) break;  // uniform
-        const float *x = xs + (size_t)xrow[r] * ldx + g * 32;
-        acc[r][b] = fmaf(s0, dot16(wq[0], wq[1], x), acc[r][b]);
-        acc[r][b] = fmaf(s1, dot16(wq[2], wq[3], x + 16), acc[r][b]);
-      }
-    }
-  };
-  if constexpr (KNI > 0) {
-#pragma unroll
-    for (int i = 0; i < KNI; ++i) {
-      if (ks.gb + 4 * i >= ks.ge) break;  // uniform
-      body(i);
-    }
-  } else {
-    for (int i = 0; ks.gb + 4 * i < ks.ge; ++i) body(i);
-  }
-  reduce_store<NB, EPI>(acc, rows, n_out, gl, tile, dst, ldo, r0, lane, wave, s_red);
-}
-
 // 16 e2m1 codes (two words) times 16 bf16 activations (8 packed pairs) with
 // the bf16 dot-product instruction (exact products, fp32 sums): two chains of
 // four pairs in order, then added.
@@ -430,125 +327,43 @@ __device__ __forceinline__ float dot16_bf16(uint32_t w0, uint32_t w1, const u32x
   return c0 + c1;
 }
 
-// Per-tile outputs of a batch (one token), for the threads that sum them (in
-// LDS: written by thread 0 before the batch's first barrier).
-struct BatchOut {
-  float *dst[kBatch];
-  float gl[kBatch];
-  int col0[kBatch], n_out[kBatch], valid[kBatch];
-};
+// 16-byte chunk t (0..7) of k-group g of row r of an activation staged in
+// LDS (G k-groups per row): consecutive groups are 16 bytes apart, so the
+// lanes of a half-wavefront read consecutive chunks.
+__device__ __forceinline__ int tchunk(int r, int t, int g, int G) { return (r * 8 + t) * G + g; }
 
-// Sum the partials of a batch of up to kBatch one-token tiles and store them:
-// every lane writes its partial per tile, then thread (t, n) adds the 32
-// partials of column n of tile t in a fixed order (wavefronts 0..7, in each the
-// q-lanes 0..3) and stores gl * sum, or its activation, device-coherently.  One
-// LDS round and two barriers per batch instead of per tile.
-template <int NB, int EPI>
-__device__ __forceinline__ void reduce_store_batch(const float (&acc)[kBatch][NB], const BatchOut &bo, int tid,
-                                                   int lane, int wave, float *s_red) {
-#pragma unroll
-  for (int t = 0; t < kBatch; ++t)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) s_red[((t * NB + b) * kWaves + wave) * 64 + lane] = acc[t][b];
-  __syncthreads();
-  if (tid < kBatch * 16) {
-    const int t = tid >> 4, nl = tid & 15;
-    if (bo.valid[t]) {
-      float sum[NB];
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const float *sr = s_red + (size_t)(t * NB + b) * kWaves * 64 + nl;
-        float pv[kWaves * 4];  // all loads first: one LDS latency, not 32
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) pv[w * 4 + q] = sr[w * 64 + q * 16];
-        float v = 0.f;
-#pragma unroll
-        for (int j = 0; j < kWaves * 4; ++j) v += pv[j];
-        sum[b] = v;
-      }
-      const float gl = bo.gl[t];
-      float v;
-      if (EPI == EPI_F32) {
-        v = gl * sum[0];
-      } else if (EPI == EPI_RELU2) {
-        float u = gl * sum[0];
-        u = u > 0.f ? u : 0.f;
-        v = u * u;
-      } else {
-        const float av = gl * sum[0];
-        const float bv = gl * sum[NB - 1];
-        v = (av / (1.0f + expf(-av))) * bv;
-      }
-      const int col = bo.col0[t] + nl;
-      if (col < bo.n_out[t]) __hip_atomic_store(bo.dst[t] + col, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  __syncthreads();  // s_red is reused next
+// acc + s0 * (codes 0..15 . x 0..15) + s1 * (codes 16..31 . x 16..31), x from
+// row r of a transposed LDS activation.
+__device__ __forceinline__ float dot32_lds(const u32x4_t &w, float s0, float s1, const f32x4_t *xs, int r, int g,
+                                           int G, float acc) {
+  acc = fmaf(s0, dot16v(w.x, w.y, xs[tchunk(r, 0, g, G)], xs[tchunk(r, 1, g, G)], xs[tchunk(r, 2, g, G)],
+                        xs[tchunk(r, 3, g, G)]),
+             acc);
+  return fmaf(s1, dot16v(w.z, w.w, xs[tchunk(r, 4, g, G)], xs[tchunk(r, 5, g, G)], xs[tchunk(r, 6, g, G)],
+                         xs[tchunk(r, 7, g, G)]),
+              acc);
 }
 
-// Partial sums of one up tile of a one-token step with bf16 x held in
-// registers: xb[i] is the 32 bf16 values of this lane's i-th k-group.
-template <int NB, int KU>
-__device__ __forceinline__ void partial_xreg(int k, const u32x4_t (&xb)[KU][4], int lane, int wave,
-                                             const WRegs<NB, KU> &R, float (&acc)[NB]) {
-  const int q = lane >> 4;
-  const KSlice ks(k, wave);
+// Sum over the 32 lanes of a half-wavefront, by a fixed butterfly: every lane
+// ends with the same bits.
+__device__ __forceinline__ float half_sum(float v) {
 #pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = 0.f;
-#pragma unroll
-  for (int i = 0; i < KU; ++i) {
-    if (ks.gb + 4 * i >= ks.ge) break;  // uniform
-    if (ks.gb + 4 * i + q >= ks.ge) continue;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      float s0, s1;
-      e4m3x2_to_f32(R.sc[b][i], s0, s1);
-      acc[b] = fmaf(s0, dot16_bf16(R.wq[b][i][0], R.wq[b][i][1], xb[i][0], xb[i][1]), acc[b]);
-      acc[b] = fmaf(s1, dot16_bf16(R.wq[b][i][2], R.wq[b][i][3], xb[i][2], xb[i][3]), acc[b]);
-    }
-  }
+  for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 32);
+  return v;
 }
 
-// Partial sum of one down tile of a one-token step: this lane's first KD
-// k-groups of h (fp32) are held in registers (xh[i]: 32 floats), later ones are
-// read from the staged h in LDS; weights from LDS.
-template <int KD>
-__device__ __forceinline__ float partial_hreg(int k, const f32x4_t (&xh)[KD][8], const float *s_h, int lane,
-                                              int wave, const LdsB &ws) {
-  const int q = lane >> 4;
-  const KSlice ks(k, wave);
-  float acc = 0.f;
-  u32x4_t wqs[kKDMax];  // every k-group's weights first: one LDS latency per tile
-  uint32_t scs[kKDMax];
-#pragma unroll
-  for (int i = 0; i < kKDMax; ++i) ws.get(0, i, max(min(ks.gb + 4 * i + q, ks.ge - 1), 0), wqs[i], scs[i]);
-#pragma unroll
-  for (int i = 0; i < kKDMax; ++i) {
-    if (ks.gb + 4 * i >= ks.ge) break;  // uniform
-    const int g = ks.gb + 4 * i + q;
-    if (g >= ks.ge) continue;
-    const u32x4_t wq = wqs[i];
-    float s0, s1;
-    e4m3x2_to_f32(scs[i], s0, s1);
-    if (i < KD) {
-      acc = fmaf(s0, dot16v(wq[0], wq[1], xh[i][0], xh[i][1], xh[i][2], xh[i][3]), acc);
-      acc = fmaf(s1, dot16v(wq[2], wq[3], xh[i][4], xh[i][5], xh[i][6], xh[i][7]), acc);
-    } else {
-      acc = fmaf(s0, dot16(wq[0], wq[1], s_h + g * 32), acc);
-      acc = fmaf(s1, dot16(wq[2], wq[3], s_h + g * 32 + 16), acc);
-    }
+// The output of a column from its sums: gl * a (EPI_F32), relu(gl * a)^2, or
+// silu(gl * a) * (gl * b) (SwiGLU, a the gate row).
+template <int EPI>
+__device__ __forceinline__ float epilogue(float gl, float a, float b) {
+  if (EPI == EPI_F32) return gl * a;
+  if (EPI == EPI_RELU2) {
+    float u = gl * a;
+    u = u > 0.f ? u : 0.f;
+    return u * u;
   }
-  return acc;
-}
-
-// The workgroup whose up range [w n_up / G, (w + 1) n_up / G) holds tile i.
-__device__ __forceinline__ int up_owner(int i, int n_up, int grid) {
-  int w = (int)((long)i * grid / n_up);
-  while (w + 1 < grid && (long)(w + 1) * n_up / grid <= i) ++w;
-  while (w > 0 && (long)w * n_up / grid > i) --w;
-  return w;
+  const float av = gl * a, bv = gl * b;
+  return (av / (1.0f + expf(-av))) * bv;
 }
 
 // Wavefront-wide wait until flags[w_lo .. w_hi] all read `target` (lane l
@@ -577,42 +392,55 @@ template <int NB, int KU, int EPI_UP, bool X_F32, bool XREG>
 __global__ void __launch_bounds__(kThreads) k_decode_layer(LayerArgs a) {
   extern __shared__ u32x4_t s_dyn[];  // x [n][d] f32 | h [rows][k] f32 | down weights
   __shared__ int s_e[kMaxPicks], s_r0[kMaxPicks], s_rows[kMaxPicks];  // per slot: expert, first row, rows
-  __shared__ int s_id[kMaxPicks], s_prow[kMaxPicks], s_both[kMaxPicks];   // per pick t*K+j: expert, packed row
+  __shared__ int s_id[kMaxPicks], s_prow[kMaxPicks];                      // per pick t*K+j: expert, packed row
   __shared__ float s_pw[kMaxPicks];                                        // ... and routing weight
+  __shared__ float s_lsel[kMaxPicks];                                      // ... and logit
+  __shared__ __attribute__((aligned(16))) float s_logit[kMaxRows * MOE_MAX_EXPERTS];  // [n][E rounded up to 4]
   __shared__ int s_rt[kMaxPicks];                                          // token of each packed row
   __shared__ int s_nact;
   __shared__ float s_dgl[kMaxDown];  // globals of this workgroup's down tiles
   __shared__ int s_last[kMaxDown];   // 1: this workgroup combines that tile's 16 columns
-  __shared__ float s_red[XREG ? kBatch * NB * kWaves * 64 : kWaves * kMaxRows * NB * 16];
-  __shared__ BatchOut s_bo;
   const DecodeLayerProblem &lp = a.lp;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, c32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rowl = 2 * wave + (lane >> 5);  // this lane's row of every tile
   int32_t *err = lp.sync;
   int32_t *up_flag = lp.sync + 2;
   int32_t *ct_done = up_flag + kMaxGrid;
-  float *s_x = (float *)s_dyn;
-  float *s_h = (float *)((uint8_t *)s_dyn + a.x_lds);
-  uint8_t *s_w = (uint8_t *)s_dyn + a.x_lds + a.h_lds;
+  f32x4_t *s_x = (f32x4_t *)s_dyn;  // transposed (tchunk)
+  f32x4_t *s_h = (f32x4_t *)((uint8_t *)s_dyn + a.x_lds);
+  uint8_t *s_us = (uint8_t *)s_dyn + a.x_lds + a.h_lds;  // [kMaxUp][NB] 16-row blocks of up scales
+  uint8_t *s_w = s_us + a.us_lds;                          // down tiles: codes, then scales
   const int n = lp.n_tokens;
+  const int Gx = lp.d >> 5;  // k-groups of x
 
-  // this workgroup's tiles
-  const int u_first = (int)((long)blockIdx.x * a.n_up / a.grid);
-  const int u_last = (int)((long)(blockIdx.x + 1) * a.n_up / a.grid);
+  // this workgroup's tiles: the shared expert's (blockIdx.x < gs) or routed ones
+  const int ups = lp.has_shared ? a.up_tiles[0] : 0;
   const int n_sd = lp.has_shared ? a.down_tiles : 0;
-  int d_first, d_last;
-  down_range(blockIdx.x, a.grid, n_sd, a.n_down, a.down_bytes, a.down_total, d_first, d_last);
+  const bool shared_wg = blockIdx.x < a.gs;
+  int u_first, u_last, d_first, d_last;
+  group_range(blockIdx.x, a.grid, a.gs, ups, a.n_up, u_first, u_last);
+  group_range(blockIdx.x, a.grid, a.gs, n_sd, a.n_down, d_first, d_last);
 
-  // x: issued first; XREG: this lane's k-groups into registers, else all of x
+  // the logits first: routing is the first step on the critical path
+  const int E = lp.n_experts, K = lp.top_k, P = n * K, NE = n * E;
+  const int Epad = (E + 3) & ~3;
+  float lg[kLogitsPerThread];
+#pragma unroll
+  for (int i = 0; i < kLogitsPerThread; ++i) {
+    const int c = tid + kThreads * i;
+    lg[i] = lp.logits[min(c, NE - 1)];
+  }
+
+  // x: XREG: this lane's k-groups into registers (bf16), else all of x
   // (written to LDS as fp32 after the wait)
   u32x4_t xv[XREG ? 1 : kXChunks];
   u32x4_t xb[XREG ? KU : 1][4];
   const int x_chunks = X_F32 ? n * lp.d / 4 : n * lp.d / 8;
   if constexpr (XREG) {
-    const KSlice ks(lp.d, wave);
 #pragma unroll
     for (int i = 0; i < KU; ++i) {
-      const int g = max(min(ks.gb + 4 * i + (lane >> 4), ks.ge - 1), 0);
+      const int g = min(c32 + 32 * i, Gx - 1);
 #pragma unroll
       for (int t = 0; t < 4; ++t) xb[i][t] = *((const u32x4_t *)lp.x + g * 4 + t);
     }
@@ -628,52 +456,10 @@ __global__ void __launch_bounds__(kThreads) k_decode_layer(LayerArgs a) {
   // its up tiles (read early, used late)
   const int32_t epoch = __hip_atomic_load(&up_flag[blockIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // routing: wavefront t picks token t's top-K experts and their weights
-  const int E = lp.n_experts, K = lp.top_k, P = n * K;
-  if (wave < n) {
-    int my_id;
-    float my_w;
-    route_one_token_any(lp.logits + (size_t)wave * E, E, K, lane, my_id, my_w);
-    if (lane < K) {
-      s_id[wave * K + lane] = my_id;
-      s_pw[wave * K + lane] = my_w;
-    }
-  }
-  __syncthreads();
-  // gather layout (picks in wavefront 0, P <= 64): rows grouped by expert in
-  // ascending id, tokens ascending within an expert; a slot per distinct
-  // expert, in ascending id.  s_both[p]: token 0's pick p is also token 1's.
-  if (tid < P) {
-    const int e = s_id[tid], t = tid >= K;
-    int other = 0;
-    for (int q = t ? 0 : K; q < (t ? K : P); ++q) other |= s_id[q] == e;
-    s_both[tid] = t == 0 && other;
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the flags are written
-    __builtin_amdgcn_wave_barrier();
-    int below = 0, dup_below = 0, n_dup = 0;
-    for (int q = 0; q < P; ++q) {
-      const int eq = s_id[q], bq = q < K ? s_both[q] : 0;
-      below += eq < e;
-      dup_below += bq && eq < e;
-      n_dup += bq;
-    }
-    const int r = below + (t == 1 && other);
-    s_prow[tid] = r;
-    s_rt[r] = t;
-    if (t == 0 || !other) {
-      const int slot = below - dup_below;
-      s_e[slot] = e;
-      s_r0[slot] = below;
-      s_rows[slot] = 1 + (t == 0 && other);
-    }
-    if (tid == 0) s_nact = P - n_dup;
-  }
-  __syncthreads();
-  const int n_active = s_nact;
-
   // the four projections, read once
   const ProbView U0 = view_of(lp.up[0], lp.h[0], lp.fs), U1 = view_of(lp.up[1], lp.h[1], lp.f);
   const ProbView D0 = view_of(lp.down[0], lp.h[0], lp.fs), D1 = view_of(lp.down[1], lp.h[1], lp.f);
+  int n_active = 0;  // distinct routed experts, once routed
   auto expert_of = [&](const Tile &t, const ProbView &p, int &e, int &r0, int &rows) -> bool {
     if (t.prob == 0) {
       e = 0;
@@ -694,25 +480,149 @@ __global__ void __launch_bounds__(kThreads) k_decode_layer(LayerArgs a) {
   //  first tile), and nothing loaded is used before the wait: a value merged
   //  across branches, or used at once, makes the compiler wait for every load
   //  issued before it.
-  WRegs<NB, KU> RU[kMaxUp];
+  RowW<NB, KU> RU[kMaxUp];
   float ugl[kMaxUp];
   int utok[kMaxUp][kMaxRows];  // token of each row of the tile's expert
   bool uok[kMaxUp];
-#pragma unroll
-  for (int u = 0; u < kMaxUp; ++u) {
-    const int ui = min(u_first + u, a.n_up - 1);
-    const Tile t = up_tile(a, ui);
-    const ProbView p = pick(t.prob == 0, U0, U1);
-    int e = 0, r0 = 0, rows = 0;
-    uok[u] = u_first + u < u_last && expert_of(t, p, e, r0, rows);
-    if (!uok[u]) e = 0, r0 = 0;
-    issue_weights<NB, KU>(p, e, uok[u] ? t.tile : 0, lane, wave, RU[u]);
-    ugl[u] = p.global[e];
-#pragma unroll
-    for (int r = 0; r < kMaxRows; ++r) utok[u][r] = s_rt[min(r0 + r, P - 1)];
-  }
   float dgl = 0.f;  // thread i: global of down tile d_first + i
-  {
+  auto route = [&]() {
+    // routing (the pages' rule: top-K by logit, the lower index first among
+    // equal logits, weights a softmax over the picks).  The rank of expert e
+    // among token t's logits is the number of experts that beat it; the experts
+    // of rank < K are the picks, slot = rank.  Threads split each expert's
+    // comparisons into `parts` interleaved 16-byte chunks of LDS.
+#pragma unroll
+    for (int i = 0; i < kLogitsPerThread; ++i) {
+      const int c = tid + kThreads * i;
+      if (c < NE) {
+        const int t = c >= E, e = c - t * E;
+        s_logit[t * Epad + e] = lg[i];
+      }
+    }
+    {  // padding: -inf at an index past E never beats an expert
+      const int padw = Epad - E;
+      if (padw > 0 && tid < n * padw) {
+        const int t = tid >= padw;
+        s_logit[t * Epad + E + tid - t * padw] = -__builtin_inff();
+      }
+    }
+    lds_barrier();
+    {
+      int parts = 1;
+      while (parts < 16 && 2 * parts * NE <= kThreads) parts <<= 1;
+      const int part = tid & (parts - 1);
+      for (int pr = tid / parts; pr - tid / parts < NE; pr += kThreads / parts) {
+        const bool ok = pr < NE;
+        const int t = ok && pr >= E, e = ok ? pr - t * E : 0;
+        const float *row = s_logit + t * Epad;
+        const float v = row[e];
+        int cnt = 0;
+        for (int c = part; 4 * c < E; c += parts) {
+          const f32x4_t w4 = *(const f32x4_t *)(row + 4 * c);
+          const int e0 = 4 * c;
+          cnt += (w4.x > v) | ((w4.x == v) & (e0 < e));
+          cnt += (w4.y > v) | ((w4.y == v) & (e0 + 1 < e));
+          cnt += (w4.z > v) | ((w4.z == v) & (e0 + 2 < e));
+          cnt += (w4.w > v) | ((w4.w == v) & (e0 + 3 < e));
+        }
+        for (int o = 1; o < parts; o <<= 1) cnt += __shfl_xor(cnt, o, 64);
+        if (ok && part == 0 && cnt < K) {
+          s_id[t * K + cnt] = e;
+          s_lsel[t * K + cnt] = v;
+        }
+      }
+    }
+    lds_barrier();
+    // weights and gather layout (picks in wavefront 0, P <= 64): rows grouped by
+    // expert in ascending id, tokens ascending within an expert; a slot per
+    // distinct expert, in ascending id
+    if (wave == 0) {
+      const bool ok = lane < P;
+      const int t = lane >= K;
+      const int e = ok ? s_id[lane] : 0x7FFFFFFF;
+      const float l = ok ? s_lsel[lane] : 0.f;
+      const float l0 = s_lsel[ok ? t * K : 0];
+      const float ex = ok ? expf(l - l0) : 0.f;
+      float sum0 = 0.f, sum1 = 0.f;  // in slot order
+      for (int j = 0; j < K; ++j) {
+        sum0 += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+        if (n > 1) sum1 += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), K + j));
+      }
+      // other: the other token picked e too
+      int other = 0;
+      for (int q = 0; q < P; ++q) other |= ((q >= K) != t) & (__builtin_amdgcn_readlane(e, q) == e);
+      const unsigned long long both = __ballot(ok && t == 0 && other);  // token 0's picks shared with token 1
+      int below = 0, dup_below = 0;
+      for (int q = 0; q < P; ++q) {
+        const int eq = __builtin_amdgcn_readlane(e, q);
+        below += eq < e;
+        dup_below += (int)((both >> q) & 1ull) & (eq < e);
+      }
+      if (ok) {
+        s_pw[lane] = ex / (t ? sum1 : sum0);
+        const int r = below + (t == 1 && other);
+        s_prow[lane] = r;
+        s_rt[r] = t;
+        if (t == 0 || !other) {
+          const int slot = below - dup_below;
+          s_e[slot] = e;
+          s_r0[slot] = below;
+          s_rows[slot] = 1 + (t == 0 && other);
+        }
+      }
+      if (lane == 0) s_nact = P - __popcll(both);
+    }
+    lds_barrier();
+    n_active = s_nact;
+    // workgroup 0: the routing and layout views
+    if (blockIdx.x == 0) {
+      if (tid < P) {
+        lp.ids[tid] = s_id[tid];
+        lp.topk_w[tid] = s_pw[tid];
+        lp.rows[tid] = s_prow[tid];
+        lp.row_token[tid] = s_rt[tid];
+      }
+      for (int e = tid; e <= E; e += kThreads) {
+        int below = 0;
+        for (int q = 0; q < P; ++q) below += s_id[q] < e;
+        lp.offsets[e] = below;
+      }
+      if (tid == 0) __hip_atomic_fetch_add(lp.sync + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  auto issue = [&]() {
+#pragma unroll
+    for (int u = 0; u < kMaxUp; ++u) {
+      const int ui = min(u_first + u, a.n_up - 1);
+      const Tile t = up_tile(a, ui);
+      const ProbView p = pick(t.prob == 0, U0, U1);
+      int e = 0, r0 = 0, rows = 0;
+      uok[u] = u_first + u < u_last && expert_of(t, p, e, r0, rows);
+      if (!uok[u]) e = 0, r0 = 0;
+      issue_rows<NB, KU>(p, e, uok[u] ? t.tile : 0, lane, wave, RU[u]);
+      if (uok[u]) {
+        const __amdgpu_buffer_rsrc_t none = coherent_rsrc(lp.x, 16);  // unused by plain copies
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const size_t row0 = (size_t)e * p.n_w + (size_t)t.tile * 16 + (size_t)b * p.n_out;
+          copy_to_lds<false>(p.scales + row0 * (p.k / 16), none, 0, 16L * (p.k / 16),
+                             s_us + (size_t)(u * NB + b) * a.us_blk, wave, lane);
+        }
+      }
+      ugl[u] = p.global[e];
+#pragma unroll
+      for (int r = 0; r < kMaxRows; ++r) utok[u][r] = s_rt[min(r0 + r, P - 1)];
+    }
+    // thread i: the global of down tile d_first + i
+    if (tid < d_last - d_first) {
+      const Tile t = down_tile(a, d_first + tid);
+      const ProbView p = pick(t.prob == 0, D0, D1);
+      int e, r0, rows;
+      if (expert_of(t, p, e, r0, rows)) dgl = p.global[e];
+    }
+  };
+  // the down tiles' weights into LDS
+  auto issue_down = [&]() {
     long off = 0;
     const __amdgpu_buffer_rsrc_t none = coherent_rsrc(lp.x, 16);  // unused by plain copies
     for (int i = d_first; i < d_last; ++i) {
@@ -725,23 +635,18 @@ __global__ void __launch_bounds__(kThreads) k_decode_layer(LayerArgs a) {
       copy_to_lds<false>(p.codes + row0 * (p.k / 2), none, 0, cb, s_w + off, wave, lane);
       copy_to_lds<false>(p.scales + row0 * (p.k / 16), none, 0, sb, s_w + off + round_kb(cb), wave, lane);
       off += round_kb(cb) + round_kb(sb);
-      if (tid == i - d_first) dgl = p.global[e];
     }
-  }
-  // workgroup 0: the routing and layout views, while the weights stream in
-  if (blockIdx.x == 0) {
-    if (tid < P) {
-      lp.ids[tid] = s_id[tid];
-      lp.topk_w[tid] = s_pw[tid];
-      lp.rows[tid] = s_prow[tid];
-      lp.row_token[tid] = s_rt[tid];
-    }
-    for (int e = tid; e <= E; e += kThreads) {
-      int below = 0;
-      for (int q = 0; q < P; ++q) below += s_id[q] < e;
-      lp.offsets[e] = below;
-    }
-    if (tid == 0) __hip_atomic_fetch_add(lp.sync + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  // The shared expert's tiles need no routing: their workgroups request their
+  // weights first and route while they stream in.
+  if (shared_wg) {
+    issue();
+    issue_down();
+    route();
+  } else {
+    route();
+    issue();
+    issue_down();
   }
   memory_done();
   if (tid < d_last - d_first) s_dgl[tid] = dgl;
@@ -750,8 +655,10 @@ __global__ void __launch_bounds__(kThreads) k_decode_layer(LayerArgs a) {
     const int c = tid + kThreads * j;
     if (c >= x_chunks) break;
     if (X_F32) {
-      *((u32x4_t *)s_x + c) = xv[j];
+      const int e0 = 4 * c, r = e0 / lp.d, col = e0 - r * lp.d;
+      s_x[tchunk(r, (col & 31) >> 2, col >> 5, Gx)] = __builtin_bit_cast(f32x4_t, xv[j]);
     } else {
+      const int e0 = 8 * c, r = e0 / lp.d, col = e0 - r * lp.d;
       f32x4_t lo, hi;  // bf16 -> f32: the bits in the upper half
       lo.x = __uint_as_float(xv[j].x << 16);
       lo.y = __uint_as_float(xv[j].x & 0xFFFF0000u);
@@ -761,50 +668,60 @@ __global__ void __launch_bounds__(kThreads) k_decode_layer(LayerArgs a) {
       hi.y = __uint_as_float(xv[j].z & 0xFFFF0000u);
       hi.z = __uint_as_float(xv[j].w << 16);
       hi.w = __uint_as_float(xv[j].w & 0xFFFF0000u);
-      *((f32x4_t *)s_x + 2 * c) = lo;
-      *((f32x4_t *)s_x + 2 * c + 1) = hi;
+      s_x[tchunk(r, (col & 31) >> 2, col >> 5, Gx)] = lo;
+      s_x[tchunk(r, ((col & 31) >> 2) + 1, col >> 5, Gx)] = hi;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
-  // ---- 2. up tiles; count them once their h stores have completed
-  if constexpr (XREG) {
-    static_assert(kMaxUp <= kBatch, "the up tiles form one batch");
-    float uacc[kBatch][NB];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      if (tid == 0) s_bo.valid[u] = 0;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) uacc[u][b] = 0.f;
-      if (u >= kMaxUp || !uok[u]) continue;
-      const Tile t = up_tile(a, u_first + u);
-      const ProbView p = pick(t.prob == 0, U0, U1);
-      int e, r0, rows;
-      expert_of(t, p, e, r0, rows);
-      partial_xreg<NB, KU>(p.k, xb, lane, wave, RU[u], uacc[u]);
-      if (tid == 0) {
-        s_bo.valid[u] = 1;
-        s_bo.dst[u] = p.h + (size_t)r0 * p.ldh;
-        s_bo.gl[u] = ugl[u];
-        s_bo.col0[u] = t.tile * 16;
-        s_bo.n_out[u] = p.n_out;
-      }
-    }
-    reduce_store_batch<NB, EPI_UP>(uacc, s_bo, tid, lane, wave, s_red);
-  }
+  // ---- 2. up tiles; publish them once their h stores have completed
 #pragma unroll
   for (int u = 0; u < kMaxUp; ++u) {
-    if (XREG || !uok[u]) continue;
+    if (!uok[u]) continue;  // uniform
     const Tile t = up_tile(a, u_first + u);
     const ProbView p = pick(t.prob == 0, U0, U1);
     int e, r0, rows;
     expert_of(t, p, e, r0, rows);
-    {
-      int xr[kMaxRows];  // x rows: tokens 0..n-1 for the shared expert, row_token for a routed one
+    float acc[kMaxRows][NB];
 #pragma unroll
-      for (int r = 0; r < kMaxRows; ++r) xr[r] = t.prob == 0 ? r : max(utok[u][r], 0);
-      tile_dot<NB, KU, EPI_UP>(p.k, p.n_out, ugl[u], rows, xr, s_x, lp.d, t.tile, p.h, p.ldh, r0, lane, wave,
-                               RegB<NB, KU>{RU[u]}, s_red);
+    for (int r = 0; r < kMaxRows; ++r)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
+#pragma unroll
+    for (int i = 0; i < KU; ++i) {
+      const int g = c32 + 32 * i, gc = min(g, Gx - 1);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        float s0, s1;
+        e4m3x2_to_f32(*(const uint16_t *)(s_us + (size_t)(u * NB + b) * a.us_blk + rowl * (Gx * 2) + gc * 2), s0,
+                      s1);
+        if (g >= Gx) s0 = s1 = 0.f;  // a repeated group
+        const u32x4_t w = RU[u].wq[b][i];
+        if constexpr (XREG) {
+          acc[0][b] = fmaf(s0, dot16_bf16(w.x, w.y, xb[i][0], xb[i][1]), acc[0][b]);
+          acc[0][b] = fmaf(s1, dot16_bf16(w.z, w.w, xb[i][2], xb[i][3]), acc[0][b]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < kMaxRows; ++r) {
+            if (r >= rows) break;  // uniform
+            // x row: token r for the shared expert, the row's token for a routed one
+            const int xr = t.prob == 0 ? r : max(utok[u][r], 0);
+            acc[r][b] = dot32_lds(w, s0, s1, s_x, xr, gc, Gx, acc[r][b]);
+          }
+        }
+      }
+      // one k-group's activations in registers at a time
+      if constexpr (!XREG) __builtin_amdgcn_sched_barrier(0);
+    }
+    const int col = t.tile * 16 + rowl;
+#pragma unroll
+    for (int r = 0; r < kMaxRows; ++r) {
+      if (r >= rows) break;  // uniform
+      const float v0 = half_sum(acc[r][0]);
+      const float v1 = NB > 1 ? half_sum(acc[r][NB - 1]) : 0.f;
+      if (c32 == 0 && col < p.n_out)
+        __hip_atomic_store(p.h + (size_t)(r0 + r) * p.ldh + col, epilogue<EPI_UP>(ugl[u], v0, v1), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   memory_done();
@@ -813,77 +730,98 @@ __global__ void __launch_bounds__(kThreads) k_decode_layer(LayerArgs a) {
   // ---- 3. down tiles, each once its expert's h is complete
   long off = 0;
   int staged = -1;  // problem slot whose h is in LDS
-  const int hrow[kMaxRows] = {0, 1};
-  f32x4_t hreg[XREG ? kKD : 1][8];  // XREG: this lane's k-groups of the staged h
-  // XREG: down tiles of one expert are summed in batches
-  float dacc[kBatch][1];
-#pragma unroll
-  for (int c = 0; c < kBatch; ++c) dacc[c][0] = 0.f;
-  int nb = 0;
-  auto flush = [&]() {
-    if (nb == 0) return;
-    if (tid == 0)  // slots past nb hold no tile of this batch
-      for (int c = nb; c < kBatch; ++c) s_bo.valid[c] = 0;
-    reduce_store_batch<1, EPI_F32>(dacc, s_bo, tid, lane, wave, s_red);
-    nb = 0;
-  };
+  bool use_hreg = false;
+  f32x4_t hreg[XREG ? kHReg : 1][8];  // XREG: this lane's k-groups of the staged h
   for (int i = d_first; i < d_last; ++i) {
     const Tile t = down_tile(a, i);
     const ProbView p = pick(t.prob == 0, D0, D1);
     int e, r0, rows;
     if (!expert_of(t, p, e, r0, rows)) continue;
+    const int G = p.k >> 5;
     const int pslot = t.prob == 0 ? 0 : 1 + t.slot;
     if (pslot != staged) {
-      if (XREG) flush();
       if (wave == 0) {
         // the owners of this expert's up tiles
-        const int ups = lp.has_shared ? a.up_tiles[0] : 0;
         const int u0 = t.prob == 0 ? 0 : ups + t.slot * a.up_tiles[1];
         const int u1 = u0 + a.up_tiles[t.prob] - 1;
-        wait_flags(up_flag, up_owner(u0, a.n_up, a.grid), up_owner(u1, a.n_up, a.grid), epoch + 1, lane, err);
+        wait_flags(up_flag, group_owner(u0, a.grid, a.gs, ups, a.n_up), group_owner(u1, a.grid, a.gs, ups, a.n_up),
+                   epoch + 1, lane, err);
       }
-      __syncthreads();
-      const long ldh = p.ldh;
+      __syncthreads();  // also: every wavefront is done with the previous h
+      // h rows [r0, r0 + rows), device-coherent loads, transposed into LDS
       const long hrows = t.prob == 0 ? n : lp.n_rows;
-      const __amdgpu_buffer_rsrc_t hr = coherent_rsrc(p.h, (size_t)hrows * ldh * 4);
-      copy_to_lds<true>(nullptr, hr, (uint32_t)((size_t)r0 * ldh * 4), (long)rows * ldh * 4, (uint8_t *)s_h, wave,
-                        lane);
-      memory_done();
+      const __amdgpu_buffer_rsrc_t hr = coherent_rsrc(p.h, (size_t)hrows * p.ldh * 4);
+      const int cpr = p.k >> 2, nq = rows * cpr;  // 16-byte chunks per row, in all
+      for (int q0 = 0; q0 < nq; q0 += kThreads * 2) {  // two loads in flight per thread
+        u32x4_t v[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int q = min(q0 + kThreads * j + tid, nq - 1), r = q / cpr, rem = q - r * cpr;
+          v[j] = __builtin_amdgcn_raw_buffer_load_b128(hr, (uint32_t)(((size_t)(r0 + r) * p.ldh) * 4 + rem * 16), 0,
+                                                       kSc1);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int q = q0 + kThreads * j + tid, r = q / cpr, rem = q - r * cpr;
+          if (q < nq) s_h[tchunk(r, rem & 7, rem >> 3, G)] = __builtin_bit_cast(f32x4_t, v[j]);
+        }
+      }
+      lds_barrier();
       staged = pslot;
-      if constexpr (XREG) {
-        const KSlice ks(p.k, wave);
+      use_hreg = XREG && G <= 32 * kHReg;
+      if (XREG && use_hreg) {
 #pragma unroll
-        for (int i = 0; i < kKD; ++i) {
-          const int g = max(min(ks.gb + 4 * i + (lane >> 4), ks.ge - 1), 0);
+        for (int ii = 0; ii < kHReg; ++ii) {
+          const int gc = min(c32 + 32 * ii, G - 1);
 #pragma unroll
-          for (int t4 = 0; t4 < 8; ++t4) hreg[i][t4] = *((const f32x4_t *)s_h + g * 8 + t4);
+          for (int t4 = 0; t4 < 8; ++t4) hreg[ii][t4] = s_h[tchunk(0, t4, gc, G)];
         }
       }
     }
     const long cb = round_kb(16L * (p.k / 2));
-    const LdsB bsrc{s_w + off + (size_t)(lane & 15) * (p.k / 2), s_w + off + cb + (size_t)(lane & 15) * (p.k / 16)};
-    float *dst = t.prob == 0 ? lp.out : lp.yg;
-    if constexpr (XREG) {
-      const float pv = partial_hreg<kKD>(p.k, hreg, s_h, lane, wave, bsrc);
-      const float gl = s_dgl[i - d_first];
+    const uint8_t *wrow = s_w + off + (size_t)rowl * (p.k / 2);
+    const uint8_t *srow = s_w + off + cb + (size_t)rowl * (p.k / 16);
+    float acc[kMaxRows];
 #pragma unroll
-      for (int c = 0; c < kBatch; ++c)
-        if (c == nb) dacc[c][0] = pv;
-      if (tid == 0) {
-        s_bo.valid[nb] = 1;
-        s_bo.dst[nb] = dst + (size_t)r0 * lp.d;
-        s_bo.gl[nb] = gl;
-        s_bo.col0[nb] = t.tile * 16;
-        s_bo.n_out[nb] = p.n_out;
+    for (int r = 0; r < kMaxRows; ++r) acc[r] = 0.f;
+    if (XREG && use_hreg) {
+#pragma unroll
+      for (int ii = 0; ii < kHReg; ++ii) {
+        if (32 * ii >= G) break;  // uniform
+        const int g = c32 + 32 * ii, gc = min(g, G - 1);
+        const u32x4_t w = *(const u32x4_t *)(wrow + gc * 16);
+        float s0, s1;
+        e4m3x2_to_f32(*(const uint16_t *)(srow + gc * 2), s0, s1);
+        if (g >= G) s0 = s1 = 0.f;
+        acc[0] = fmaf(s0, dot16v(w.x, w.y, hreg[ii][0], hreg[ii][1], hreg[ii][2], hreg[ii][3]), acc[0]);
+        acc[0] = fmaf(s1, dot16v(w.z, w.w, hreg[ii][4], hreg[ii][5], hreg[ii][6], hreg[ii][7]), acc[0]);
       }
-      if (++nb == kBatch) flush();
     } else {
-      tile_dot<1, 0, EPI_F32>(p.k, p.n_out, s_dgl[i - d_first], rows, hrow, s_h, p.k, t.tile, dst, lp.d, r0, lane,
-                              wave, bsrc, s_red);
+      for (int g0 = 0; g0 < G; g0 += 32) {
+        const int g = g0 + c32, gc = min(g, G - 1);
+        const u32x4_t w = *(const u32x4_t *)(wrow + gc * 16);
+        float s0, s1;
+        e4m3x2_to_f32(*(const uint16_t *)(srow + gc * 2), s0, s1);
+        if (g >= G) s0 = s1 = 0.f;
+#pragma unroll
+        for (int r = 0; r < kMaxRows; ++r) {
+          if (r >= rows) break;  // uniform
+          acc[r] = dot32_lds(w, s0, s1, s_h, r, gc, G, acc[r]);
+        }
+      }
+    }
+    float *dst = t.prob == 0 ? lp.out : lp.yg;
+    const int col = t.tile * 16 + rowl;
+    const float gl = s_dgl[i - d_first];
+#pragma unroll
+    for (int r = 0; r < kMaxRows; ++r) {
+      if (r >= rows) break;  // uniform
+      const float v = half_sum(acc[r]);
+      if (c32 == 0 && col < p.n_out)
+        __hip_atomic_store(dst + (size_t)(r0 + r) * lp.d + col, gl * v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     off += cb + round_kb(16L * (p.k / 16));
   }
-  if (XREG) flush();
 
   // ---- 4. count the down tiles once their stores have completed; the last
   //         producer of a 16-column block computes its combine, in slot order
@@ -1004,8 +942,8 @@ hipError_t launch_decode_layer(const DecodeLayerProblem &lp, hipStream_t stream)
     return hipErrorNotSupported;
   if (lp.max_slots != (lp.n_experts < lp.n_rows ? lp.n_experts : lp.n_rows)) return hipErrorNotSupported;
   if ((long)n * d * (lp.x_f32 ? 4 : 2) > 16L * kThreads * kXChunks) return hipErrorNotSupported;
-  // k-group iterations of an up tile per lane
-  const int ku = ((d / 32 + kWaves - 1) / kWaves + 3) / 4;
+  // k-group iterations of an up tile per lane (32 lanes per row)
+  const int ku = (d / 32 + 31) / 32;
   long h_lds = 0;
   a.down_bytes[0] = 0;
   for (int i = 0; i < 2; ++i) {
@@ -1018,35 +956,59 @@ hipError_t launch_decode_layer(const DecodeLayerProblem &lp, hipStream_t stream)
   // coherent loads of h use 32-bit byte offsets
   if ((long)lp.n_rows * lp.f * 4 > 0x7FFFFFF0L || (long)n * lp.fs * 4 > 0x7FFFFFF0L) return hipErrorNotSupported;
   const int n_sd = lp.has_shared ? a.down_tiles : 0;
-  a.down_total = down_prefix(a.n_down, n_sd, a.down_bytes);
-  // one token, bf16 x, every down tile within kKD iterations: activations in registers
-  bool xreg = n == 1 && !lp.x_f32;
-  for (int i = 0; i < 2; ++i)
-    if ((i == 1 || lp.has_shared) && ((lp.down[i].k / 32 + kWaves - 1) / kWaves + 3) / 4 > kKDMax) xreg = false;
+  const int ups = lp.has_shared ? a.up_tiles[0] : 0;
+  // one token, bf16 x: x in registers
+  const bool xreg = n == 1 && !lp.x_f32;
   a.x_lds = xreg ? 0 : (int)round_kb((long)n * d * 4);
   a.h_lds = (int)h_lds;
+  a.us_blk = (int)round_kb(16L * (d / 16));
+  a.us_lds = kMaxUp * (swiglu ? 2 : 1) * a.us_blk;
+  for (int i = 0; i < 2; ++i)  // whole 16-row tiles
+    if (lp.up[i].n_out % 16 != 0 || lp.down[i].n_out % 16 != 0) return hipErrorNotSupported;
   // one workgroup per CU
   int cus = 0, dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidValue;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return hipErrorInvalidValue;
   a.grid = cus;
-  if (a.grid > kMaxGrid || (a.n_up + a.grid - 1) / a.grid > kMaxUp) return hipErrorNotSupported;
-  long w_lds = 0;
-  for (int g = 0; g < a.grid; ++g) {
-    int f, l;
-    down_range(g, a.grid, n_sd, a.n_down, a.down_bytes, a.down_total, f, l);
-    const long b = down_prefix(l, n_sd, a.down_bytes) - down_prefix(f, n_sd, a.down_bytes);
-    w_lds = b > w_lds ? b : w_lds;
-    if (l - f > kMaxDown) return hipErrorNotSupported;
+  if (a.grid > kMaxGrid || a.grid < 2) return hipErrorNotSupported;
+  // Workgroups for the shared expert in proportion to its bytes (it is
+  // requested while the others route); the nearest split that fits.
+  const long wb_sh = lp.has_shared ? (long)a.up_tiles[0] * down_tile_bytes(lp.up[0].k) + (long)n_sd * a.down_bytes[0]
+                                   : 0;
+  const long wb_rt = (long)lp.max_slots * ((long)a.up_tiles[1] * down_tile_bytes(lp.up[1].k) * (swiglu ? 2 : 1) +
+                                           (long)a.down_tiles * a.down_bytes[1]);
+  const int gs0 = lp.has_shared ? (int)((a.grid * wb_sh + (wb_sh + wb_rt) / 2) / (wb_sh + wb_rt)) : 0;
+  // the largest share of a group of g splitting n items
+  auto most = [](int n_items, int g) { return g > 0 ? (n_items + g - 1) / g : 0; };
+  long w_lds = -1;
+  for (int dg = 0; dg < a.grid && w_lds < 0; ++dg) {
+    for (int sgn = 0; sgn < 2 && w_lds < 0; ++sgn) {
+      if (sgn == 1 && dg == 0) continue;
+      const int gs = lp.has_shared ? gs0 + (sgn ? -dg : dg) : 0;
+      if (lp.has_shared && (gs < 1 || gs > a.grid - 1)) continue;
+      const int gr = a.grid - gs;
+      const int up_most = std::max(most(ups, gs), most(a.n_up - ups, gr));
+      const int dn_most = std::max(most(n_sd, gs), most(a.n_down - n_sd, gr));
+      const long worst =
+          std::max((long)most(n_sd, gs) * a.down_bytes[0], (long)most(a.n_down - n_sd, gr) * a.down_bytes[1]);
+      if (up_most <= kMaxUp && dn_most <= kMaxDown && a.x_lds + a.h_lds + a.us_lds + worst + kStaticLds <= kLdsLimit) {
+        a.gs = gs;
+        w_lds = worst;
+      }
+    }
+    if (!lp.has_shared) break;
   }
-  const long lds = a.x_lds + a.h_lds + w_lds;  // the kernel's static LDS is added in launch_one
+  if (w_lds < 0) return hipErrorNotSupported;
+  const long lds = a.x_lds + a.h_lds + a.us_lds + w_lds;  // the kernel's static LDS is added in launch_one
   if (lds > kLdsLimit) return hipErrorNotSupported;
   if (swiglu) {
+    if (ku <= 1) return launch_x<2, 1, EPI_SWIGLU>(a, xreg, (size_t)lds, stream);
     if (ku <= 2) return launch_x<2, 2, EPI_SWIGLU>(a, xreg, (size_t)lds, stream);
     if (ku <= 4) return launch_x<2, 4, EPI_SWIGLU>(a, xreg, (size_t)lds, stream);
     return hipErrorNotSupported;
   }
+  if (ku <= 1) return launch_x<1, 1, EPI_RELU2>(a, xreg, (size_t)lds, stream);
   if (ku <= 2) return launch_x<1, 2, EPI_RELU2>(a, xreg, (size_t)lds, stream);
   if (ku <= 3) return launch_x<1, 3, EPI_RELU2>(a, xreg, (size_t)lds, stream);
   if (ku <= 4) return launch_x<1, 4, EPI_RELU2>(a, xreg, (size_t)lds, stream);
