@@ -265,6 +265,16 @@ def main():
                     "kernel": "k_decode_layer (the whole decode step in one persistent launch)",
                     "bytes_per_launch": b["total"], "us_per_launch": round(us, 3), "bytes": b}
         breakdown = {"decode_layer_eager": breakdown["route_gather"]}
+    elif np.diff(v["offsets"].cpu().numpy()).max() <= layer.gemv_max_rows:
+        # every expert on the decode GEMV: one up and one down launch of k_dq_gemv
+        ffn_us = breakdown["up"] + breakdown["down"]
+        b = decode_step_bytes(inp, ids)
+        achieved = b["weights"] / (ffn_us * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "k_dq_gemv (decode dequant-GEMV: one up and one down launch per step, "
+                              "shared + routed experts)",
+                    "bytes_per_launch": b["weights"] // 2, "us_per_launch": round(ffn_us / 2, 3), "bytes": b}
     else:
         flops = layer_ffn_flops(inp)
         ffn_us = breakdown["up"] + breakdown["down"]

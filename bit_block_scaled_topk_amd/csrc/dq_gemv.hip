@@ -3,15 +3,18 @@
 // <= 32 tokens; TensorFold issue #2265, "What ncu shows" / "Proposal": decode
 // expert kernels must keep several k-groups of weight loads in flight).
 //
-// Work item = (expert, 16 output columns).  A workgroup of WAVES wavefronts
-// splits K into WAVES contiguous slices; inside a wavefront, lane
+// Work item = (expert, CT tiles of 16 output columns).  A workgroup of WAVES
+// wavefronts splits K into WAVES contiguous slices; inside a wavefront, lane
 // (n = lane%16, q = lane/16) owns output column n and, per iteration, the whole
 // 32-element k-group g = g0 + 4*i + q of that column's weight row: one 16-byte
 // code load plus two scale bytes.  A chunk's weight loads are all issued before
 // any is used, so each lane keeps kNI k-groups in flight.  The 32 codes become
 // 4 bf16x8 B operands (exact: e2m1 * e4m3 has <= 6 significant bits) and feed 4
 // MFMA 16x16x32 steps; the A operand holds the same 32 k-values of up to 16
-// activation rows, so the MFMA sums the dot product over the group.
+// activation rows, so the MFMA sums the dot product over the group.  The A
+// operands of a k-group are loaded once and used for all CT tiles: with one
+// tile per workgroup the activation rows would be read once per 16 columns,
+// several times the bytes of the weights themselves.
 //
 // Activations arrive as NT bf16 planes whose sum is the activation: NT = 1 for
 // bf16 inputs (exact), NT = 3 for fp32 inputs split hi + mid + lo (24
@@ -32,13 +35,17 @@ namespace moe {
 
 namespace {
 
-#ifndef MOE_GEMV_NI
-#define MOE_GEMV_NI 8
-#endif
 #ifndef MOE_GEMV_WAVES
 #define MOE_GEMV_WAVES 4
 #endif
-constexpr int kNI = MOE_GEMV_NI;  // k-group iterations whose weight loads are in flight per lane
+#ifndef MOE_GEMV_CT
+#define MOE_GEMV_CT 4
+#endif
+#ifndef MOE_GEMV_NIT
+#define MOE_GEMV_NIT 8
+#endif
+constexpr int kCT = MOE_GEMV_CT;    // 16-column tiles per workgroup
+constexpr int kNIT = MOE_GEMV_NIT;  // weight loads in flight per lane (tiles x k-groups)
 
 struct GemvBatch {
   ProjProblem p[2];
@@ -97,11 +104,12 @@ __device__ __forceinline__ void find_expert(const int32_t *__restrict__ offsets,
   }
 }
 
-template <int WAVES, int MT, int NT, int EPI>
+template <int WAVES, int MT, int NT, int EPI, int CT>
 __global__ void __launch_bounds__(64 * WAVES) k_dq_gemv(GemvBatch batch) {
   constexpr int NB = (EPI == EPI_SWIGLU) ? 2 : 1;
+  constexpr int kNI = kNIT / CT > 0 ? kNIT / CT : 1;  // k-group iterations per round
   __shared__ int s_info[3];
-  __shared__ f32x4_t s_red[WAVES > 1 ? WAVES - 1 : 1][MT][NB][64];
+  __shared__ f32x4_t s_red[WAVES > 1 ? WAVES - 1 : 1][CT][MT][NB][64];
 
   int bid = blockIdx.x;
   const bool second = batch.count > 1 && bid >= batch.p[0].blocks;
@@ -109,8 +117,8 @@ __global__ void __launch_bounds__(64 * WAVES) k_dq_gemv(GemvBatch batch) {
   if (second) bid -= batch.p[0].blocks;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int slot = bid / p.n_tiles;
-  const int tile = bid - slot * p.n_tiles;
+  const int slot = bid / p.n_tiles;  // n_tiles: tile blocks of CT tiles per expert
+  const int tile0 = (bid - slot * p.n_tiles) * CT;
   int e, r0, rows;
   if (p.known_rows >= 0) {
     e = 0;
@@ -130,19 +138,13 @@ __global__ void __launch_bounds__(64 * WAVES) k_dq_gemv(GemvBatch batch) {
   const int gpw = (G + WAVES - 1) / WAVES;
   const int gb = wave * gpw;
   const int ge = min(G, gb + gpw);
-  const int col_raw = tile * 16 + nl;
-  const bool col_ok = col_raw < p.n_out;
-  const int col = col_ok ? col_raw : p.n_out - 1;
 
   const size_t crow = (size_t)(p.k >> 1), srow = (size_t)(p.k >> 4);
-  const uint8_t *wrow[NB];
-  const uint8_t *sptr[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const size_t wr = (size_t)e * p.n_w + (size_t)col + (size_t)b * p.n_out;
-    wrow[b] = p.codes + wr * crow;
-    sptr[b] = p.scales + wr * srow;
-  }
+  // this lane's weight row of tile ct: column (tile0 + ct) * 16 + nl (clamped)
+  auto wrow_of = [&](int ct, int b, const uint8_t *base, size_t pitch) {
+    const int col = min((tile0 + ct) * 16 + nl, p.n_out - 1);
+    return base + ((size_t)e * p.n_w + (size_t)col + (size_t)b * p.n_out) * pitch;
+  };
   const uint16_t *arow[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -151,31 +153,35 @@ __global__ void __launch_bounds__(64 * WAVES) k_dq_gemv(GemvBatch batch) {
     arow[mt] = p.a + (size_t)ar * p.lda;
   }
 
-  f32x4_t acc[MT][NB];
+  f32x4_t acc[CT][MT][NB];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[mt][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[ct][mt][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int g0 = gb; g0 < ge; g0 += 4 * kNI) {
-    u32x4_t wq[NB][kNI];
-    uint32_t sc[NB][kNI];
+    u32x4_t wq[CT][NB][kNI];
+    uint32_t sc[CT][NB][kNI];
 #pragma unroll
     for (int i = 0; i < kNI; ++i) {
       const int g = g0 + 4 * i + q;
       const int gc = min(g, ge - 1);
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        wq[b][i] = *(const u32x4_t *)(wrow[b] + (size_t)gc * 16);
-        const uint32_t s2 = *(const uint16_t *)(sptr[b] + (size_t)gc * 2);
-        sc[b][i] = (g < ge) ? s2 : 0u;  // a zero scale neutralises a clamped group
-      }
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          wq[ct][b][i] = *(const u32x4_t *)(wrow_of(ct, b, p.codes, crow) + (size_t)gc * 16);
+          const uint32_t s2 = *(const uint16_t *)(wrow_of(ct, b, p.scales, srow) + (size_t)gc * 2);
+          sc[ct][b][i] = (g < ge) ? s2 : 0u;  // a zero scale neutralises a clamped group
+        }
     }
 #pragma unroll
     for (int i = 0; i < kNI; ++i) {
       if (g0 + 4 * i >= ge) break;  // uniform: no group of this iteration is in range
       const int gc = min(g0 + 4 * i + q, ge - 1);
-      u32x4_t a[MT][NT][4];
+      u32x4_t a[MT][NT][4];  // loaded once, used for every tile
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const uint16_t *ap = arow[mt] + (size_t)gc * 32;
@@ -185,23 +191,25 @@ __global__ void __launch_bounds__(64 * WAVES) k_dq_gemv(GemvBatch batch) {
           for (int t = 0; t < 4; ++t) a[mt][tt][t] = *(const u32x4_t *)(ap + (size_t)tt * p.plane + 8 * t);
       }
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        float s0, s1;
-        e4m3x2_to_f32(sc[b][i], s0, s1);
-        u32x4_t B[4];
-        B[0] = dq8_bf16(wq[b][i][0], s0);
-        B[1] = dq8_bf16(wq[b][i][1], s0);
-        B[2] = dq8_bf16(wq[b][i][2], s1);
-        B[3] = dq8_bf16(wq[b][i][3], s1);
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          if (mt > 0 && rows <= 16 * mt) break;  // uniform
+        for (int b = 0; b < NB; ++b) {
+          float s0, s1;
+          e4m3x2_to_f32(sc[ct][b][i], s0, s1);
+          u32x4_t B[4];
+          B[0] = dq8_bf16(wq[ct][b][i][0], s0);
+          B[1] = dq8_bf16(wq[ct][b][i][1], s0);
+          B[2] = dq8_bf16(wq[ct][b][i][2], s1);
+          B[3] = dq8_bf16(wq[ct][b][i][3], s1);
 #pragma unroll
-          for (int tt = 0; tt < NT; ++tt)
+          for (int mt = 0; mt < MT; ++mt) {
+            if (mt > 0 && rows <= 16 * mt) break;  // uniform
 #pragma unroll
-            for (int t = 0; t < 4; ++t) acc[mt][b] = mfma16x16x32(a[mt][tt][t], B[t], acc[mt][b]);
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+              for (int t = 0; t < 4; ++t) acc[ct][mt][b] = mfma16x16x32(a[mt][tt][t], B[t], acc[ct][mt][b]);
+          }
         }
-      }
     }
   }
 
@@ -209,53 +217,62 @@ __global__ void __launch_bounds__(64 * WAVES) k_dq_gemv(GemvBatch batch) {
   if (WAVES > 1) {
     if (wave > 0) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int b = 0; b < NB; ++b) s_red[wave - 1][mt][b][lane] = acc[mt][b];
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) s_red[wave - 1][ct][mt][b][lane] = acc[ct][mt][b];
     }
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
     for (int w = 0; w < WAVES - 1; ++w)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const f32x4_t v = s_red[w][mt][b][lane];
-          acc[mt][b].x += v.x;
-          acc[mt][b].y += v.y;
-          acc[mt][b].z += v.z;
-          acc[mt][b].w += v.w;
-        }
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const f32x4_t v = s_red[w][ct][mt][b][lane];
+            acc[ct][mt][b].x += v.x;
+            acc[ct][mt][b].y += v.y;
+            acc[ct][mt][b].z += v.z;
+            acc[ct][mt][b].w += v.w;
+          }
   }
 
   // epilogue: lane holds D[m = 16*mt + 4*q + i][col], i = 0..3
   const float gl = p.global[e];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+  for (int ct = 0; ct < CT; ++ct) {
+    const int col = (tile0 + ct) * 16 + nl;
+    if (col >= p.n_out) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = mt * 16 + 4 * q + i;
-      if (!col_ok || m >= rows) continue;
-      const size_t o = (size_t)(r0 + m) * p.ldo + col;
-      if (EPI == EPI_F32) {
-        p.out_f32[o] = gl * acc[mt][0][i];
-      } else {
-        float h;
-        if (EPI == EPI_RELU2) {
-          float u = gl * acc[mt][0][i];
-          u = u > 0.f ? u : 0.f;
-          h = u * u;
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = mt * 16 + 4 * q + i;
+        if (m >= rows) continue;
+        const size_t o = (size_t)(r0 + m) * p.ldo + col;
+        if (EPI == EPI_F32) {
+          p.out_f32[o] = gl * acc[ct][mt][0][i];
         } else {
-          const float a = gl * acc[mt][0][i];
-          const float bb = gl * acc[mt][NB - 1][i];
-          h = (a / (1.0f + expf(-a))) * bb;
+          float h;
+          if (EPI == EPI_RELU2) {
+            float u = gl * acc[ct][mt][0][i];
+            u = u > 0.f ? u : 0.f;
+            h = u * u;
+          } else {
+            const float a = gl * acc[ct][mt][0][i];
+            const float bb = gl * acc[ct][mt][NB - 1][i];
+            h = (a / (1.0f + expf(-a))) * bb;
+          }
+          uint32_t hi, mid, lo;
+          split3_bf16(h, hi, mid, lo);
+          p.out_h[o] = (uint16_t)hi;
+          p.out_h[o + p.h_plane] = (uint16_t)mid;
+          p.out_h[o + 2 * p.h_plane] = (uint16_t)lo;
         }
-        uint32_t hi, mid, lo;
-        split3_bf16(h, hi, mid, lo);
-        p.out_h[o] = (uint16_t)hi;
-        p.out_h[o + p.h_plane] = (uint16_t)mid;
-        p.out_h[o + 2 * p.h_plane] = (uint16_t)lo;
       }
     }
   }
@@ -282,9 +299,9 @@ template <int WAVES, int MT, int NT>
 hipError_t dispatch_epi(const GemvBatch &b, int epi, dim3 grid, hipStream_t s) {
   dim3 block(64 * WAVES);
   switch (epi) {
-    case EPI_F32: hipLaunchKernelGGL((k_dq_gemv<WAVES, MT, NT, EPI_F32>), grid, block, 0, s, b); break;
-    case EPI_RELU2: hipLaunchKernelGGL((k_dq_gemv<WAVES, MT, NT, EPI_RELU2>), grid, block, 0, s, b); break;
-    default: hipLaunchKernelGGL((k_dq_gemv<WAVES, MT, NT, EPI_SWIGLU>), grid, block, 0, s, b); break;
+    case EPI_F32: hipLaunchKernelGGL((k_dq_gemv<WAVES, MT, NT, EPI_F32, kCT>), grid, block, 0, s, b); break;
+    case EPI_RELU2: hipLaunchKernelGGL((k_dq_gemv<WAVES, MT, NT, EPI_RELU2, kCT>), grid, block, 0, s, b); break;
+    default: hipLaunchKernelGGL((k_dq_gemv<WAVES, MT, NT, EPI_SWIGLU, kCT>), grid, block, 0, s, b); break;
   }
   return hipGetLastError();
 }
@@ -312,7 +329,7 @@ hipError_t launch_dq_gemv(ProjProblem *probs, const int *max_active, int count, 
     } else if (max_active[i] <= 0 || p.max_rows <= 0) {
       continue;
     }
-    p.n_tiles = (p.n_out + 15) / 16;
+    p.n_tiles = ((p.n_out + 15) / 16 + kCT - 1) / kCT;  // blocks of kCT tiles
     const int slots = p.known_rows >= 0 ? 1 : max_active[i];
     p.blocks = slots * p.n_tiles;
     const int rb = p.known_rows >= 0 ? p.known_rows : p.max_rows;

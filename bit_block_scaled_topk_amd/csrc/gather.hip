@@ -70,7 +70,8 @@ __device__ __forceinline__ int wave_scan_incl(int v, int lane) {
 // the expert (larger logit, or equal logit and lower index: a strict total
 // order, so ranks are unique), the parts are summed with LDS atomics, and the
 // expert of rank j < K becomes slot j.  Softmax over the picks per token, the
-// sum in slot order.  Requires n*E <= kRankPairs.
+// sum in slot order.  Requires n*E <= kRankPairs; used while every thread has
+// at most 64 comparisons.
 constexpr int kRankPairs = 8192;
 
 __device__ void route_by_rank(const float *__restrict__ logits, int n, int E, int K, float *s_logit, int *s_rank,
@@ -153,7 +154,9 @@ k_gather_small(const float *__restrict__ logits, float *__restrict__ topk_w, int
 
   for (int i = tid; i < E * W; i += blockDim.x) bits[i] = 0u;
   if (ROUTE) {
-    if (n * E <= kRankPairs) {
+    // ranks cost E comparisons per (token, expert): for more than a few
+    // tokens a wavefront per token (K argmax rounds) is cheaper
+    if (n * E <= kRankPairs && (long)n * E * E <= 64L * kSmallThreads) {
       route_by_rank(logits, n, E, K, s_logit, s_rank, s_sel, ids, topk_w, s_ids);
     } else {
       for (int t = wave; t < n; t += nwaves) {
