@@ -124,6 +124,12 @@ __global__ void __launch_bounds__(64 * WAVES) k_dq_gemv(GemvBatch batch) {
     e = 0;
     r0 = 0;
     rows = p.known_rows;
+  } else if (p.blocks == p.n_experts * p.n_tiles) {
+    // a slot per expert: read its two offsets instead of scanning them all
+    e = slot;
+    r0 = p.offsets[e];
+    rows = p.offsets[e + 1] - r0;
+    if (rows < 1 || rows > p.max_rows || r0 < 0 || r0 > p.n_rows - rows) return;  // uniform
   } else {
     if (wave == 0) find_expert(p.offsets, p.n_experts, p.n_rows, p.max_rows, slot, lane, s_info);
     __syncthreads();

@@ -309,8 +309,18 @@ def test_layer_decode_workloads(ops, name):
     assert normwise(host(layer.yg)[:R], ref["yg"]) <= TOL_DECODE
 
 
-def test_layer_tiny_forced_onto_prefill_path(ops):
-    inp = cached_layer("tiny16")
+# Every expert forced onto the prefill GEMM: a k that is not a whole number of
+# 64-wide steps (d 96, d_ff 160, shared 224) and the gated FFN (SwiGLU gate
+# and up rows side by side in the weight tile).
+FORCED_PREFILL_CASES = [("tiny16", dict()), ("tiny16", dict(n=24, d=96, f=160, fs=224, seed=21)),
+                        ("gated2", dict(n=40, seed=22))]
+
+
+@pytest.mark.parametrize("case", range(len(FORCED_PREFILL_CASES)))
+def test_layer_forced_onto_prefill_path(ops, case):
+    name, ov = FORCED_PREFILL_CASES[case]
+    inp = cached_layer(name, **ov)
+    print(f"forced prefill case {name} {ov}", flush=True)
     _, got = _run_layer(ops, inp, gemv_max_rows=0)
     assert normwise(got, oracle.layer(inp)["out"]) <= TOL_PREFILL
     # against the oracle's bf16-activation mode the only differences are
