@@ -44,6 +44,7 @@ ProjProblem make_problem(const uint16_t *a, long plane, long lda, const int32_t 
   p.row_map = nullptr;
   p.plane = plane;
   p.lda = lda;
+  p.a_rows = n_rows;
   p.offsets = offsets;
   p.n_experts = n_experts;
   p.n_rows = n_rows;
@@ -485,6 +486,7 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, 
 
   ProjProblem ru = make_problem(a_x, plane_x, p.d, offsets, p.E, p.R, -1, &dsc->up, p.f, nullptr, h, p.f, h_plane);
   ru.row_map = row_token;  // gather on load
+  ru.a_rows = p.n;
   ProjProblem rd = make_problem(h, h_plane, p.f, offsets, p.E, p.R, -1, &dsc->down, p.d, yg, nullptr, p.d, 0);
   ProjProblem su{}, sd{};
   if (p.has_shared) {

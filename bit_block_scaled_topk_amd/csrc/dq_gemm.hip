@@ -4,13 +4,11 @@
 // GEMM (CUDA)": unpack dropping the global, exact in bf16; global in alpha;
 // activation rounded to bf16).
 //
-// One workgroup (4 wavefronts, 2 x 2) computes a 128-row x 128-column tile of
-// one expert; the tile list is derived on the device from expert_offsets, so
-// the host never reads routing results.  Per 64-wide k step, the activation
-// tile (bf16) and the unpacked weight tile (bf16, decoded from 16-byte code
-// loads in registers) are staged through LDS; the next step's global loads are
-// issued before the current step's MFMAs.  Each wavefront owns a 64 x 64
-// sub-tile as 4 x 4 MFMA 16x16x32 accumulators.
+// Workgroups take 128-row x 256-column tiles of one expert (4 wavefronts, each
+// all 128 rows x 64 columns); the tile list is derived on the device from
+// expert_offsets, so the host never reads routing results.  The weights are
+// decoded in registers straight into MFMA operands (no bf16 copy in LDS or
+// HBM); only the activation tile is staged through LDS.
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
@@ -18,12 +16,29 @@ namespace moe {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;  // +8 bf16 pad per LDS row
+constexpr int BM = 128, BN = 256, BK = 128;
+constexpr int A_BYTES = BM * BK * 2;  // one LDS activation buffer: 128 rows x 256 B, XOR-swizzled
+constexpr uint32_t OOB = 0x80000000u; // a buffer offset past every extent: the load returns 0
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct GemmBatch {
   ProjProblem p[2];
   int count;
 };
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Wait until this wavefront's loads have landed (register and LDS
+// destinations), then a workgroup barrier that orders LDS only.
+__device__ __forceinline__ void loads_done_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // Which expert and which of its 128-row tiles the m-tile index `mt` names.
 // Experts whose row range is not inside [0, n_rows) are skipped.
@@ -61,21 +76,47 @@ __device__ __forceinline__ void find_tile(const int32_t *offsets, int E, int n_r
   if (lane == 0) s_info[0] = -1;
 }
 
+// One workgroup: a 128-row x 256-column tile of one expert (SwiGLU: 128 h
+// columns, i.e. 128 gate + 128 up weight rows).  Wavefront w owns weight
+// columns [64w, 64w + 64) of the tile and all 128 rows: 8 x 4 MFMA 16x16x32
+// accumulators.
+//
+// The weights never pass through LDS.  Per 128-wide k chunk, lane (n, q) of a
+// wavefront loads 16 bytes of codes -- 32 consecutive k of column n, at
+// k = 32q .. 32q + 31 -- and the two e4m3 scales of those 32 k, for each of its
+// four 16-column blocks, and decodes them in registers, exactly, into the
+// B operands of four MFMA steps s = 0..3 (step s takes k = 32q + 8s .. +7).
+// The k order inside a chunk is thereby permuted relative to the MFMA's own
+// (slice q = k 8q .. 8q + 7); the activation fragments are read from LDS in
+// the same permuted order, so every product still pairs equal k.  Each weight
+// element is loaded and decoded once per workgroup.
+//
+// The activation tile (bf16, 128 rows x 128 k) is double-buffered in LDS and
+// filled one chunk ahead by buffer-to-LDS loads: 16-byte cell c of row r sits
+// in slot c ^ (r & 15) of the row, so the 16 rows an MFMA fragment reads fall
+// in distinct banks, while each load instruction still fills 1 KB of LDS
+// contiguously.  Rows past the expert's and k past K load as zero (offsets
+// beyond the buffer's extent), so partial tiles need no branches.  One barrier
+// per chunk.
 template <int EPI>
-__global__ void __launch_bounds__(256) k_dq_gemm(GemmBatch batch) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) k_dq_gemm(GemmBatch batch) {
   __shared__ int s_info[3];
-  __shared__ __attribute__((aligned(16))) uint16_t sA[BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[BN * LDK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA[2 * A_BYTES];
 
-  int bid = blockIdx.x;
-  const bool second = batch.count > 1 && bid >= batch.p[0].blocks;
+  // Tiles in launch order, column tile fastest.  Workgroups are dealt
+  // round-robin over the 8 XCDs, so with 8 column tiles (the routed up
+  // projection) each XCD keeps one column slice of every expert's weights in
+  // its L2 for both of the expert's m-tiles.  (Grouping each XCD's tiles by
+  // m-tile instead was measured 20-40 % slower.)
+  int t = (int)blockIdx.x;
+  const bool second = batch.count > 1 && t >= batch.p[0].blocks;
   const ProjProblem p = second ? batch.p[1] : batch.p[0];
-  if (second) bid -= batch.p[0].blocks;
+  if (second) t -= batch.p[0].blocks;
   const int n_ntiles = p.n_tiles;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int mt = bid / n_ntiles;
-  const int nt = bid - mt * n_ntiles;
+  const int mt = t / n_ntiles;
+  const int nt = t - mt * n_ntiles;
   int e, r0, mrows;
   if (p.known_rows >= 0) {
     e = 0;
@@ -90,94 +131,127 @@ __global__ void __launch_bounds__(256) k_dq_gemm(GemmBatch batch) {
     r0 = s_info[1];
     mrows = s_info[2];
   }
+  const int K = p.k;
 
-  // loader roles: thread -> (tile row, 32-wide half of the k step)
-  const int lrow = tid >> 1, lhalf = tid & 1;
-  const bool a_ok = lrow < mrows;
-  const int a_row = p.row_map ? max(p.row_map[r0 + (a_ok ? lrow : 0)], 0) : r0 + (a_ok ? lrow : 0);
-  const uint16_t *a_ptr = p.a + (size_t)a_row * p.lda + lhalf * 32;
-
-  int hcol, wrow_idx;
-  if (EPI == EPI_SWIGLU) {
-    // LDS row j: wavefront-column wn = j/64, sub-tile s = (j%64)/16: s = 0,1 gate, 2,3 up
-    const int wn = lrow >> 6, s = (lrow & 63) >> 4, jj = lrow & 15;
-    hcol = nt * 64 + wn * 32 + (s & 1) * 16 + jj;
-    wrow_idx = hcol + (s >> 1) * p.n_out;
-  } else {
-    hcol = nt * BN + lrow;
-    wrow_idx = hcol;
-  }
-  const bool b_ok = hcol < p.n_out;
-  const size_t wr = (size_t)e * p.n_w + (size_t)(b_ok ? wrow_idx : 0);
-  const uint8_t *c_ptr = p.codes + wr * (size_t)(p.k >> 1) + lhalf * 16;
-  const uint8_t *s_ptr = p.scales + wr * (size_t)(p.k >> 4) + lhalf * 2;
-
-  const int nl = lane & 15, q = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
-
-  f32x4_t acc[4][4];
+  // Activation loads: instruction i of wavefront w fills rows 4g .. 4g + 3,
+  // g = 8w + i; lane l takes row 4g + l/16, slot l%16, i.e. cell
+  // (l%16) ^ (row & 15) of the row.
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.a, p.a_bytes);
+  uint32_t a_off[8];
+  int a_k[8];  // first k of the lane's cell
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i) {
+    const int r = 4 * (8 * wave + i) + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    const bool ok = r < mrows;
+    const int src = p.row_map ? p.row_map[r0 + (ok ? r : 0)] : r0 + (ok ? r : 0);
+    a_off[i] = (ok && src >= 0) ? (uint32_t)src * (uint32_t)(p.lda * 2) + 16u * c : OOB;
+    a_k[i] = 8 * c;
+  }
+
+  // Weight loads: lane (nl, q), four 16-column blocks j of this wavefront.
+  const int nl = lane & 15, q = lane >> 4;
+  const size_t e_rows = (size_t)e * p.n_w;
+  const __amdgpu_buffer_rsrc_t c_rsrc = make_rsrc(p.codes + e_rows * (size_t)(K >> 1), (uint32_t)p.n_w * (uint32_t)(K >> 1));
+  const __amdgpu_buffer_rsrc_t s_rsrc = make_rsrc(p.scales + e_rows * (size_t)(K >> 4), (uint32_t)p.n_w * (uint32_t)(K >> 4));
+  int wrow0, dj[4];
+  if (EPI == EPI_SWIGLU) {  // blocks 0, 1: gate rows; 2, 3: the matching up rows
+    wrow0 = nt * 128 + wave * 32 + nl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dj[j] = (j & 1) * 16 + (j >> 1) * p.n_out;
+  } else {
+    wrow0 = nt * BN + wave * 64 + nl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dj[j] = 16 * j;
+  }
+  // a column past n_out reads past the expert's rows (zero), or -- for the
+  // gate half of a partial SwiGLU tile -- rows whose results are not stored
+  const uint32_t c_off0 = (uint32_t)wrow0 * (uint32_t)(K >> 1) + 16u * q;
+  const uint32_t s_off0 = (uint32_t)wrow0 * (uint32_t)(K >> 4) + 2u * q;
+
+  f32x4_t acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  u32x4_t ra[4];
-  u32x4_t rc;
-  uint32_t rs;
-  auto load = [&](int k0) {
-    const bool kin = (k0 + lhalf * 32) < p.k;
+  u32x4_t rc[4];
+  uint32_t rs[4];
+  auto load = [&](int k0, int buf) {
+    uint8_t *dst = sA + buf * A_BYTES + wave * 8192;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      ra[t] = (a_ok && kin) ? *(const u32x4_t *)(a_ptr + k0 + 8 * t) : u32x4_t{0u, 0u, 0u, 0u};
-    rc = (b_ok && kin) ? *(const u32x4_t *)(c_ptr + (k0 >> 1)) : u32x4_t{0u, 0u, 0u, 0u};
-    rs = (b_ok && kin) ? (uint32_t)(*(const uint16_t *)(s_ptr + (k0 >> 4))) : 0u;
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t off = (k0 + a_k[i] < K) ? a_off[i] + 2u * (uint32_t)k0 : OOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void *)(dst + i * 1024), 16, off, 0, 0, 0);
+    }
+    const bool b_in = k0 + 32 * q < K;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t co = b_in ? c_off0 + (uint32_t)(dj[j] * (K >> 1)) + (uint32_t)(k0 >> 1) : OOB;
+      const uint32_t so = b_in ? s_off0 + (uint32_t)(dj[j] * (K >> 4)) + (uint32_t)(k0 >> 4) : OOB;
+      rc[j] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, co, 0, 0);
+      rs[j] = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, so, 0, 0);
+    }
   };
 
-  load(0);
-  for (int k0 = 0; k0 < p.k; k0 += BK) {
-    // registers -> LDS (weights unpacked exactly to bf16 on the way)
-    u32x4_t *da = (u32x4_t *)(sA + lrow * LDK + lhalf * 32);
+  // LDS byte offset of fragment (i, s) for this lane: row 16 i + nl, cell 4q + s
+  uint32_t fa[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) da[t] = ra[t];
-    float s0, s1;
-    e4m3x2_to_f32(rs, s0, s1);
-    u32x4_t *db = (u32x4_t *)(sB + lrow * LDK + lhalf * 32);
-    db[0] = dq8_bf16(rc[0], s0);
-    db[1] = dq8_bf16(rc[1], s0);
-    db[2] = dq8_bf16(rc[2], s1);
-    db[3] = dq8_bf16(rc[3], s1);
-    __syncthreads();
-    if (k0 + BK < p.k) load(k0 + BK);
+  for (int s = 0; s < 4; ++s) fa[s] = nl * 256 + (((4 * q + s) ^ nl) << 4);
+
+  load(0, 0);
+  int buf = 0;
+  for (int k0 = 0; k0 < K; k0 += BK, buf ^= 1) {
+    loads_done_barrier();
+    u32x4_t cc[4];
+    float s0[4], s1[4];
 #pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      u32x4_t af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *(const u32x4_t *)(sA + (wm * 64 + i * 16 + nl) * LDK + kk * 32 + q * 8);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bf[j] = *(const u32x4_t *)(sB + (wn * 64 + j * 16 + nl) * LDK + kk * 32 + q * 8);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[i], bf[j], acc[i][j]);
+    for (int j = 0; j < 4; ++j) {
+      cc[j] = rc[j];
+      e4m3x2_to_f32(rs[j], s0[j], s1[j]);
     }
-    __syncthreads();
+    if (k0 + BK < K) load(k0 + BK, buf ^ 1);
+    const uint8_t *sa = sA + buf * A_BYTES;
+    // Software pipeline over the chunk's 32 groups g = 8 s + i (step s,
+    // fragment i): group g issues the LDS read of fragment g + 2, its four
+    // MFMAs, and a quarter of the next step's weight decode; sched_barriers
+    // keep that order, so LDS latency and the decode hide under the MFMAs.
+    u32x4_t bw[4], bn[4], af[3];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bw[j] = dq8_bf16(cc[j][0], s0[j]);
+    af[0] = *(const u32x4_t *)(sa + fa[0]);
+    af[1] = *(const u32x4_t *)(sa + fa[0] + 4096);
+#pragma unroll
+    for (int g = 0; g < 32; ++g) {
+      const int st = g >> 3, i = g & 7;
+      if (g + 2 < 32) {
+        const int g2 = g + 2;
+        af[g2 % 3] = *(const u32x4_t *)(sa + fa[g2 >> 3] + (g2 & 7) * 4096);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[g % 3], bw[j], acc[i][j]);
+      if (st < 3 && i < 4) bn[i] = dq8_bf16(cc[i][st + 1], st + 1 < 2 ? s0[i] : s1[i]);
+      if (st < 3 && i == 7) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bw[j] = bn[j];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
-  // epilogue: lane holds D[m = wm*64 + i*16 + 4q + r][n = wn*64 + j*16 + nl]
+  // epilogue: lane holds D[m = 16 i + 4 q + r][column 16 j + nl of the wavefront]
   const float gl = p.global[e];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int m = wm * 64 + i * 16 + 4 * q + r;
+      const int m = 16 * i + 4 * q + r;
       if (m >= mrows) continue;
       const size_t orow = (size_t)(r0 + m) * p.ldo;
       if (EPI == EPI_SWIGLU) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int col = nt * 64 + wn * 32 + j * 16 + nl;
+          const int col = nt * 128 + wave * 32 + j * 16 + nl;
           if (col >= p.n_out) continue;
           const float a = gl * acc[i][j][r];
           const float b = gl * acc[i][j + 2][r];
@@ -187,7 +261,7 @@ __global__ void __launch_bounds__(256) k_dq_gemm(GemmBatch batch) {
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int col = nt * BN + wn * 64 + j * 16 + nl;
+          const int col = nt * BN + wave * 64 + j * 16 + nl;
           if (col >= p.n_out) continue;
           float u = gl * acc[i][j][r];
           if (EPI == EPI_F32) {
@@ -222,7 +296,12 @@ hipError_t launch_dq_gemm(ProjProblem *probs, int count, int epi, hipStream_t st
       if (big > p.n_experts) big = p.n_experts;
       m_tiles = (p.n_rows + BM - 1) / BM + big;
     }
-    p.n_tiles = (epi == EPI_SWIGLU) ? (p.n_out + 63) / 64 : (p.n_out + BN - 1) / BN;
+    // the kernel addresses a (plane 0) and one expert's codes and scales with
+    // 32-bit buffer offsets, and marks skipped loads with offsets >= 2^31
+    const long a_bytes = p.a_rows * p.lda * 2;
+    if (a_bytes >= (1L << 31) || (long)p.n_w * (p.k >> 1) >= (1L << 31)) return hipErrorInvalidValue;
+    p.a_bytes = (uint32_t)a_bytes;
+    p.n_tiles = (epi == EPI_SWIGLU) ? (p.n_out + 127) / 128 : (p.n_out + BN - 1) / BN;
     p.blocks = (int)(m_tiles * p.n_tiles);
     total += p.blocks;
     b.p[b.count++] = p;

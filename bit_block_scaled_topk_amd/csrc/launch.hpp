@@ -50,6 +50,7 @@ struct ProjProblem {
   const int32_t *row_map; // optional: packed row r reads activation row row_map[r] (gather on load)
   long plane;
   long lda;
+  long a_rows;            // rows of a (row_map values index them); loads stay inside a_rows * lda
   const int32_t *offsets; // [n_experts + 1] device (unused when known_rows >= 0)
   int n_experts;
   int n_rows;             // rows of a / out
@@ -66,6 +67,7 @@ struct ProjProblem {
   // filled by the launchers
   int n_tiles;            // output-column tiles
   int blocks;             // workgroups of this problem
+  uint32_t a_bytes;       // prefill launcher: bytes of plane 0 of a
 };
 
 // Decode path: up to two problems in one launch (e.g. the shared and the routed
