@@ -72,6 +72,7 @@ def copy_probe(mb: int):
 
 
 DECODE_KERNEL_SOURCES = ("dq_layer.hip", "nvfp4_device.hpp", "route_device.hpp")
+PREFILL_KERNEL_SOURCES = ("dq_gemm.hip", "nvfp4_device.hpp", "launch.hpp")
 
 
 def kernel_source_digest(files=DECODE_KERNEL_SOURCES) -> str:
@@ -83,10 +84,10 @@ def kernel_source_digest(files=DECODE_KERNEL_SOURCES) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of k_decode_layer from the committed counter
-    summary for this workload, if it was taken from the current sources."""
-    path = os.path.join(ROOT, "profiles", f"k_decode_layer_{workload}_traffic.md")
+def measured_traffic(kernel: str, workload: str, sources):
+    """HBM bytes per launch of `kernel` from the committed counter summary for
+    this workload, if it was taken from the current sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -95,7 +96,7 @@ def measured_traffic(workload: str):
             if ":" in line and line.startswith("- "):
                 k, v = line[2:].split(":", 1)
                 fields[k.strip()] = v.strip().strip("`")
-    if fields.get("kernel_sources_sha256") != kernel_source_digest():
+    if fields.get("kernel_sources_sha256") != kernel_source_digest(sources):
         return None
     try:
         return int(fields["hbm_bytes_per_launch"])
@@ -261,7 +262,8 @@ def main():
         b = decode_step_bytes(inp, ids)
         achieved = b["total"] / (us * 1e-6) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(inp.name),
+                    "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic("k_decode_layer", inp.name, DECODE_KERNEL_SOURCES),
                     "kernel": "k_decode_layer (the whole decode step in one persistent launch)",
                     "bytes_per_launch": b["total"], "us_per_launch": round(us, 3), "bytes": b}
         breakdown = {"decode_layer_eager": breakdown["route_gather"]}
@@ -280,7 +282,8 @@ def main():
         ffn_us = breakdown["up"] + breakdown["down"]
         tf = flops / (ffn_us * 1e-6) / 1e12
         roofline = {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                    "traffic": measured_traffic("k_dq_gemm", inp.name, PREFILL_KERNEL_SOURCES),
                     "kernel": "k_dq_gemm (prefill grouped bf16 GEMM: one up and one down launch per step, "
                               "shared + routed experts)",
                     "flops_per_launch": flops // 2, "us_per_launch": round(ffn_us / 2, 3)}
