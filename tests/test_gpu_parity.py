@@ -346,6 +346,28 @@ def test_layer_prefill_4314_tokens(ops):
     assert np.all(np.isfinite(got))
 
 
+def test_layer_gated_prefill_scale(ops):
+    """SwiGLU experts at prefill scale on the bf16 MFMA GEMM: 2048 tokens over
+    64 experts with topK 8 give about 256 rows per expert, so every expert spans
+    two or three 128-row m-tiles and each weight tile carries gate and up rows
+    side by side.  Sampled tokens against the oracle."""
+    inp = cached_layer("gated2", n=2048, E=64, seed=23)
+    print("gated prefill-scale case: n 2048, E 64, K 8, SwiGLU f 1024", flush=True)
+    layer, got = _run_layer(ops, inp)
+    ids, w = oracle.route_topk(inp.logits, inp.K)
+    assert np.array_equal(host(layer.ids), ids)
+    off, row_token, rows = oracle.gather_layout(ids, inp.E)
+    assert np.array_equal(host(layer.offsets), off)
+    assert np.array_equal(host(layer.rows), rows)
+    counts = np.diff(off)
+    assert counts.min() > 32 and counts.max() > 128   # GEMM path, several m-tiles
+    tokens = [0, 5, 1023, 2047]
+    ref = oracle.layer_sampled(inp, tokens, ids, w)
+    assert normwise(got[tokens], ref) <= TOL_PREFILL
+    ref_bf = oracle.layer_sampled(inp, tokens, ids, w, bf16_act_of_expert=lambda e: True)
+    assert normwise(got[tokens], ref_bf) <= 2e-3
+
+
 def test_layer_is_deterministic_and_stream_independent(ops):
     inp = cached_layer("decode32_zipf")
     layer = ops.MoELayer(inp)
