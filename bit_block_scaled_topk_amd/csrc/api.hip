@@ -23,6 +23,13 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_HIP_ERROR; }
 
+// The prefill GEMM addresses an activation matrix (bf16, a_rows x a_cols) and
+// one expert's codes (w_rows x w_cols/2 bytes) with 32-bit buffer offsets that
+// stay below 2^31.
+bool gemm_extents_ok(long a_rows, long a_cols, long w_rows, long w_cols) {
+  return a_rows * a_cols * 2 < (1L << 31) && w_rows * (w_cols / 2) < (1L << 31);
+}
+
 bool weights_ok(const moe_nvfp4_weights *w) {
   return w && w->codes && w->scales && w->global && w->rows > 0 && w->cols > 0 && aligned(w->codes, 16) &&
          aligned(w->scales, 2) && aligned(w->global, 4);
@@ -197,6 +204,8 @@ moe_status nvfp4_expert_ffn(const void *xg, moe_dtype act_dtype, int n_rows, int
 
   const int dec_rows = gemv_max_rows < max_rows_per_expert ? gemv_max_rows : max_rows_per_expert;
   const bool use_gemm = max_rows_per_expert > gemv_max_rows;
+  if (use_gemm && (!gemm_extents_ok(n_rows, d, up->rows, d) || !gemm_extents_ok(n_rows, f, d_out, f)))
+    return MOE_UNSUPPORTED;
   const int max_active = n_experts < n_rows ? n_experts : n_rows;
   const int epi = (act == MOE_SWIGLU) ? EPI_SWIGLU : EPI_RELU2;
 
@@ -255,6 +264,7 @@ moe_status nvfp4_grouped_linear(const void *a_in, moe_dtype a_dtype, int n_rows,
 
   const int dec_rows = gemv_max_rows < max_rows_per_expert ? gemv_max_rows : max_rows_per_expert;
   const bool use_gemm = max_rows_per_expert > gemv_max_rows;
+  if (use_gemm && !gemm_extents_ok(n_rows, k, n_out, k)) return MOE_UNSUPPORTED;
   const int max_active = n_experts < n_rows ? n_experts : n_rows;
   const uint16_t *a = (const uint16_t *)a_in;
   int nt = 1;
@@ -318,6 +328,11 @@ bool plan_layer(const moe_layer_desc *dsc, LayerPlan *pl) {
   }
   if ((long)p.n * p.K >= (1L << 31)) return false;
   p.R = p.n * p.K;
+  if (p.n > dsc->gemv_max_rows) {  // some expert may take the prefill GEMM
+    if (!gemm_extents_ok(p.n, p.d, dsc->up.rows, p.d) || !gemm_extents_ok(p.R, p.f, p.d, p.f)) return false;
+    if (p.has_shared && (!gemm_extents_ok(p.n, p.d, p.fs, p.d) || !gemm_extents_ok(p.n, p.fs, p.d, p.fs)))
+      return false;
+  }
   p.f32 = dsc->x_dtype == MOE_F32;
   const size_t xb = p.f32 ? 4 : 2;
   size_t o = 0;

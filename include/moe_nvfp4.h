@@ -157,6 +157,10 @@ size_t nvfp4_grouped_linear_workspace_size(int n_rows, int k, moe_dtype a_dtype)
  *   out             device float [n_rows][down->rows]
  *   workspace       device scratch >= nvfp4_expert_ffn_workspace_size()
  * Alignment: xg, codes and the workspace 16-byte aligned, scales 2-byte.
+ * Limits: when the prefill path can run (max_rows_per_expert > gemv_max_rows),
+ * each activation matrix it reads as bf16 (n_rows x d, and h: n_rows x f) and
+ * one expert's codes of each projection must stay under 2 GiB (it addresses
+ * them with 32-bit offsets); otherwise MOE_UNSUPPORTED and nothing runs.
  * The shared expert is this call with n_experts = 1 and offsets {0, n}. */
 moe_status nvfp4_expert_ffn(const void *xg, moe_dtype act_dtype, int n_rows,
                             int max_rows_per_expert, const int32_t *expert_offsets,
@@ -202,7 +206,9 @@ moe_status nvfp4_unpack_bf16(const uint8_t *codes, const uint8_t *scales, int ro
  * This is the single NVFP4 matmul that gllm #91 "Testing" holds to the f32
  * tolerance when fed bf16-exact activations.
  *   a    device [n_rows][w->cols] of a_dtype; out device float [n_rows][w->rows]
- *   workspace  device scratch >= nvfp4_grouped_linear_workspace_size() */
+ *   workspace  device scratch >= nvfp4_grouped_linear_workspace_size()
+ * Limits: as nvfp4_expert_ffn's for the prefill path (a as bf16 and one
+ * expert's codes under 2 GiB), else MOE_UNSUPPORTED. */
 moe_status nvfp4_grouped_linear(const void *a, moe_dtype a_dtype, int n_rows,
                                 int max_rows_per_expert, const int32_t *expert_offsets,
                                 int n_experts, const moe_nvfp4_weights *w, int gemv_max_rows,
@@ -227,6 +233,10 @@ typedef struct {
   moe_nvfp4_weights up, down; /* routed: [E][f or 2f][d], [E][d][f] */
   moe_nvfp4_weights shared_up, shared_down; /* [1][fs][d], [1][d][fs] */
 } moe_layer_desc;
+/* A description is invalid (MOE_INVALID_ARG; workspace size 0) when, with
+ * n_tokens > gemv_max_rows, an activation matrix of the prefill GEMM (x as
+ * n x d; h as n*K x f; the shared h as n x fs, all bf16) or one expert's codes
+ * reach 2 GiB: that GEMM addresses them with 32-bit offsets. */
 
 /* Device pointers into a layer workspace where moe_layer_forward leaves the
  * intermediates of its last call (for inspection; computed on the host). */

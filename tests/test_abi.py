@@ -135,6 +135,11 @@ def test_ffn_argument_errors(lib):
     assert call(args(E=2000)) == 2
     assert call(args(xg=None)) == 1
     assert call(args(n=0, xg=None, off=None, out=None, ws=None)) == 0   # empty: nothing launched
+    # the prefill GEMM addresses each activation matrix with 32-bit offsets:
+    # 2^24 rows x 64 bf16 = 2 GiB is refused on the host before any launch
+    big = 1 << 24
+    big_ws = lib.nvfp4_expert_ffn_workspace_size(big, 64, 128, 1)
+    assert call(args(n=big, mx=big, dt=1, wsb=big_ws)) == 2
 
 
 def test_wrs_and_unpack_and_linear_argument_errors(lib):
@@ -149,3 +154,5 @@ def test_wrs_and_unpack_and_linear_argument_errors(lib):
     w = _w(64, 64)
     assert lib.nvfp4_grouped_linear(FAKE, 0, 8, 8, FAKE, 2, ctypes.byref(w), 32, None, 0, FAKE, None) == 1
     assert lib.nvfp4_grouped_linear(FAKE, 1, 8, 8, FAKE, 2, ctypes.byref(w), 40, None, 0, FAKE, None) == 2
+    # prefill path over a 2^25 x 64 bf16 activation matrix (4 GiB): refused
+    assert lib.nvfp4_grouped_linear(FAKE, 1, 1 << 25, 64, FAKE, 2, ctypes.byref(w), 32, None, 0, FAKE, None) == 2
