@@ -73,6 +73,7 @@ def copy_probe(mb: int):
 
 DECODE_KERNEL_SOURCES = ("dq_layer.hip", "nvfp4_device.hpp", "route_device.hpp")
 PREFILL_KERNEL_SOURCES = ("dq_gemm.hip", "nvfp4_device.hpp", "launch.hpp")
+GEMV_KERNEL_SOURCES = ("dq_gemv.hip", "nvfp4_device.hpp", "launch.hpp")
 
 
 def kernel_source_digest(files=DECODE_KERNEL_SOURCES) -> str:
@@ -273,7 +274,8 @@ def main():
         b = decode_step_bytes(inp, ids)
         achieved = b["weights"] / (ffn_us * 1e-6) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic("k_dq_gemv", inp.name, GEMV_KERNEL_SOURCES),
                     "kernel": "k_dq_gemv (decode dequant-GEMV: one up and one down launch per step, "
                               "shared + routed experts)",
                     "bytes_per_launch": b["weights"] // 2, "us_per_launch": round(ffn_us / 2, 3), "bytes": b}
