@@ -3,11 +3,11 @@
 // route + gather kernel).
 //
 // Each lane keeps PER_LANE of the token's logits in registers (expert
-// lane + 64*i).  K rounds of a wave-wide argmax pick the experts in
-// descending-logit order, equal logits going to the lower expert index.  The
-// argmax runs on DPP moves inside each 16-lane row (quad swaps, half-row and
-// row mirrors) and on readlane for the four row winners, so a round costs a
-// few dozen instructions and no LDS round trips.  Lane j ends with slot j's
+// lane + 64*i), each as a 64-bit key ordered like the routing rule.  K rounds
+// of a wave-wide maximum pick the experts in descending-logit order, equal
+// logits going to the lower expert index.  The maximum runs branch-free on DPP
+// moves inside each 16-lane row and two lane swaps across rows, so a round is
+// a few dozen instructions.  Lane j ends with slot j's
 // expert and weight w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), the sum taken
 // in slot order.
 #pragma once
@@ -19,74 +19,72 @@
 
 namespace moe {
 
-__device__ __forceinline__ bool route_beats(float v, int i, float bv, int bi) {
-  return (v > bv) || (v == bv && (unsigned)i < (unsigned)bi);
+// A candidate (logit v, expert i) as one unsigned 64-bit key whose order is
+// the routing order: larger logit first, equal logits to the lower index.  The
+// high word maps the float's bits monotonically to unsigned (-0 folded into +0,
+// so the two zeros tie as floats do); the low word is ~i.  Key 0 is "nothing"
+// (below every real key: a real key's high word is at least 0x007FFFFF, the
+// image of -inf).  NaN logits are not supported.
+__device__ __forceinline__ uint64_t route_key(float v, int i) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)i;
+}
+__device__ __forceinline__ int route_key_index(uint64_t k) { return (int)~(uint32_t)k; }
+__device__ __forceinline__ float route_key_logit(uint64_t k) {
+  uint32_t u = (uint32_t)(k >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+  return __uint_as_float(u);
 }
 
-// (bv, bi) <- the better of itself and the lane DPP_CTRL names.  An index of -1
-// means "nothing"; it never beats a real candidate.
+// k <- max(k, the key of the lane DPP_CTRL names), branch-free.
 template <int DPP_CTRL>
-__device__ __forceinline__ void dpp_take_best(float &bv, int &bi) {
-  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), DPP_CTRL, 0xF, 0xF, false));
-  const int oi = __builtin_amdgcn_update_dpp(-1, bi, DPP_CTRL, 0xF, 0xF, false);
-  if (oi >= 0 && (bi < 0 || route_beats(ov, oi, bv, bi))) {
-    bv = ov;
-    bi = oi;
-  }
+__device__ __forceinline__ void dpp_max_key(uint64_t &k) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)k, DPP_CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(k >> 32), DPP_CTRL, 0xF, 0xF, false);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  k = o > k ? o : k;
 }
 
-// Wave-wide argmax under route_beats; every lane returns the winner.
-__device__ __forceinline__ void wave_argmax(float &bv, int &bi) {
-  dpp_take_best<0xB1>(bv, bi);   // quad_perm [1,0,3,2]
-  dpp_take_best<0x4E>(bv, bi);   // quad_perm [2,3,0,1]
-  dpp_take_best<0x141>(bv, bi);  // row_half_mirror: quads 0 <-> 1 of each half-row
-  dpp_take_best<0x140>(bv, bi);  // row_mirror: half-rows 0 <-> 1 of each row
-  float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
-  int i = __builtin_amdgcn_readlane(bi, 0);
+// Wave-wide maximum key; every lane returns it.  DPP within each 16-lane row
+// (quad swaps, half-row and row mirrors), then lane swaps across rows.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  dpp_max_key<0xB1>(k);   // quad_perm [1,0,3,2]
+  dpp_max_key<0x4E>(k);   // quad_perm [2,3,0,1]
+  dpp_max_key<0x141>(k);  // row_half_mirror
+  dpp_max_key<0x140>(k);  // row_mirror
 #pragma unroll
-  for (int r = 1; r < 4; ++r) {
-    const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * r));
-    const int ri = __builtin_amdgcn_readlane(bi, 16 * r);
-    if (ri >= 0 && (i < 0 || route_beats(rv, ri, v, i))) {
-      v = rv;
-      i = ri;
-    }
+  for (int m = 16; m <= 32; m <<= 1) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)k, m, 64);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(k >> 32), m, 64);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    k = o > k ? o : k;
   }
-  bv = v;
-  bi = i;
+  return k;
 }
 
 template <int PER_LANE>
 __device__ __forceinline__ void route_one_token(const float *__restrict__ row, int n_experts, int top_k, int lane,
                                                 int &my_id, float &my_w) {
-  float v[PER_LANE];
-  bool taken[PER_LANE];
+  uint64_t key[PER_LANE];
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) {
     const int e = lane + i * 64;  // coalesced: consecutive lanes read consecutive experts
-    v[i] = (e < n_experts) ? row[e] : 0.0f;
-    taken[i] = !(e < n_experts);
+    key[i] = (e < n_experts) ? route_key(row[e], e) : 0ull;
   }
   float my_logit = 0.0f;
   my_id = 0;
   for (int j = 0; j < top_k; ++j) {
-    float bv = 0.0f;
-    int bi = -1;
+    uint64_t best = key[0];
 #pragma unroll
-    for (int i = 0; i < PER_LANE; ++i) {
-      const int e = lane + i * 64;
-      if (!taken[i] && (bi < 0 || route_beats(v[i], e, bv, bi))) {
-        bv = v[i];
-        bi = e;
-      }
-    }
-    wave_argmax(bv, bi);
+    for (int i = 1; i < PER_LANE; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_key(best);
 #pragma unroll
-    for (int i = 0; i < PER_LANE; ++i)
-      if (lane + i * 64 == bi) taken[i] = true;
+    for (int i = 0; i < PER_LANE; ++i) key[i] = key[i] == best ? 0ull : key[i];  // taken
     if (lane == j) {
-      my_logit = bv;
-      my_id = bi;
+      my_logit = route_key_logit(best);
+      my_id = route_key_index(best);
     }
   }
   const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_logit), 0));
