@@ -107,6 +107,12 @@ def test_route_edge_cases(ops):
     lg = rng.standard_normal((4, 77)).astype(np.float32)
     lg[:, ::3] = -np.inf                                                            # masked experts
     _route_case(ops, lg, 5)
+    lg = np.zeros((6, 40), dtype=np.float32)                                       # +0 and -0 tie
+    lg[:, 1::2] = np.float32(-0.0)
+    lg[1, 7] = 0.5
+    lg[2, 30] = -1.0
+    lg[3, ::5] = np.float32(-0.0)
+    _route_case(ops, lg, 7)
     ids, w = ops.moe_route_topk(torch.empty((0, 8), device=DEV), 2)                 # no tokens
     assert ids.shape == (0, 2)
 
