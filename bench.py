@@ -27,6 +27,8 @@ Prints ONE JSON line with the contract fields plus:
                 (FETCH_SIZE + WRITE_SIZE, scaled by what the counters read for
                 a plain copy), taken from profiles/ only while the kernel's
                 sources are the ones that were counted (else null).
+                `copy_gbs` is the HBM bandwidth a plain 1 GiB device copy
+                reaches on the same GPU (read + write bytes), for context.
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -61,6 +63,27 @@ def parse():
     return p.parse_args()
 
 
+def copy_bandwidth_gbs(mib: int = 1024, reps: int = 5) -> float:
+    """Measured HBM bandwidth of a plain device-to-device copy of `mib` MiB
+    (bytes read + bytes written over the best of `reps` event-timed copies):
+    context for the 8 TB/s spec peak, outside the timed region."""
+    import torch
+    src = torch.empty((mib << 20,), dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = None
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None or ms < best else best
+    del src, dst
+    return round(2 * (mib << 20) / (best * 1e-3) / 1e9, 1)
+
+
 def copy_probe(mb: int):
     import torch
     src = torch.empty((mb << 20,), dtype=torch.uint8, device="cuda:0")
@@ -71,7 +94,7 @@ def copy_probe(mb: int):
     print(json.dumps({"copy_probe_bytes": mb << 20, "launches": 5}))
 
 
-DECODE_KERNEL_SOURCES = ("dq_layer.hip", "nvfp4_device.hpp", "route_device.hpp")
+DECODE_KERNEL_SOURCES = ("dq_layer.hip", "nvfp4_device.hpp", "launch.hpp")
 PREFILL_KERNEL_SOURCES = ("dq_gemm.hip", "nvfp4_device.hpp", "launch.hpp")
 GEMV_KERNEL_SOURCES = ("dq_gemv.hip", "nvfp4_device.hpp", "launch.hpp")
 
@@ -289,6 +312,8 @@ def main():
                     "kernel": "k_dq_gemm (prefill grouped bf16 GEMM: one up and one down launch per step, "
                               "shared + routed experts)",
                     "flops_per_launch": flops // 2, "us_per_launch": round(ffn_us / 2, 3)}
+
+    roofline["copy_gbs"] = copy_bandwidth_gbs()
 
     cpu = None
     if not args.no_cpu_baseline:
