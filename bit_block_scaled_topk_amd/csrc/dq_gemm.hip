@@ -239,39 +239,81 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
 
-  // epilogue: lane holds D[m = 16 i + 4 q + r][column 16 j + nl of the wavefront]
+  // Epilogue: lane holds D[m = 16 i + 4 q + r][column 16 j + nl of the
+  // wavefront].  A bf16 h tile is staged in LDS (the activation buffers are
+  // free now) and written back as whole rows with 16-byte stores: 2-byte
+  // element stores of 16-column row pieces cost the up projection about a
+  // quarter of its time.  That takes 16-byte aligned rows whose width n_out is
+  // a whole number of chunks; other outputs get element stores.
   const float gl = p.global[e];
+  auto value = [&](int i, int j, int r) -> float {  // the output of accumulator (i, j, r)
+    if (EPI == EPI_F32) return gl * acc[i][j][r];
+    if (EPI == EPI_SWIGLU) {
+      const float a = gl * acc[i][j][r];
+      const float b = gl * acc[i][j + 2][r];
+      return (a / (1.0f + expf(-a))) * b;
+    }
+    float u = gl * acc[i][j][r];
+    u = u > 0.f ? u : 0.f;
+    return u * u;
+  };
+  constexpr int JN = (EPI == EPI_SWIGLU) ? 2 : 4;      // output column blocks per wavefront
+  constexpr int HC = (EPI == EPI_SWIGLU) ? 128 : BN;   // output columns of the tile
+  constexpr int EB = (EPI == EPI_F32) ? 4 : 2;         // output element bytes
+  constexpr int PER = 16 / EB;                         // elements per 16-byte chunk
+  const uintptr_t obase = EPI == EPI_F32 ? (uintptr_t)p.out_f32 : (uintptr_t)p.out_h;
+  // (f32 rows are staged only when it pays: measured, it does not for the
+  // down projection, whose 16-lane pieces are already 64 bytes)
+  const bool vec = EPI != EPI_F32 && ((obase | (uintptr_t)(p.ldo * EB)) & 15) == 0 && p.n_out % PER == 0;
+  const int c0 = nt * HC + wave * (16 * JN);  // first output column of this wavefront
+  if (!vec) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 16 * i + 4 * q + r;
-      if (m >= mrows) continue;
-      const size_t orow = (size_t)(r0 + m) * p.ldo;
-      if (EPI == EPI_SWIGLU) {
+      for (int r = 0; r < 4; ++r) {
+        const int m = 16 * i + 4 * q + r;
+        if (m >= mrows) continue;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = nt * 128 + wave * 32 + j * 16 + nl;
+        for (int j = 0; j < JN; ++j) {
+          const int col = c0 + 16 * j + nl;
           if (col >= p.n_out) continue;
-          const float a = gl * acc[i][j][r];
-          const float b = gl * acc[i][j + 2][r];
-          const float h = (a / (1.0f + expf(-a))) * b;
-          p.out_h[orow + col] = (uint16_t)f32_to_bf16_rne(h);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = nt * BN + wave * 64 + j * 16 + nl;
-          if (col >= p.n_out) continue;
-          float u = gl * acc[i][j][r];
-          if (EPI == EPI_F32) {
-            p.out_f32[orow + col] = u;
-          } else {
-            u = u > 0.f ? u : 0.f;
-            p.out_h[orow + col] = (uint16_t)f32_to_bf16_rne(u * u);
-          }
+          const size_t o = (size_t)(r0 + m) * p.ldo + col;
+          if (EPI == EPI_F32)
+            p.out_f32[o] = value(i, j, r);
+          else
+            p.out_h[o] = (uint16_t)f32_to_bf16_rne(value(i, j, r));
         }
       }
+    return;
+  }
+  // rows per LDS pass: the 64 KB activation buffers hold the whole bf16 tile, or 64 rows of f32
+  constexpr int RP = 65536 / (HC * EB) < BM ? 65536 / (HC * EB) : BM;
+  static_assert(BM % RP == 0 && RP % 16 == 0, "whole 16-row blocks per pass");
+  __syncthreads();  // every wavefront is done reading the activation buffers
+#pragma unroll
+  for (int pass = 0; pass < BM / RP; ++pass) {
+    if (pass) __syncthreads();  // the previous pass has been written back
+#pragma unroll
+    for (int i = pass * (RP / 16); i < (pass + 1) * (RP / 16); ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ml = 16 * i + 4 * q + r - pass * RP;
+#pragma unroll
+        for (int j = 0; j < JN; ++j) {
+          const int cl = wave * (16 * JN) + 16 * j + nl;
+          if (EPI == EPI_F32)
+            ((float *)sA)[ml * HC + cl] = value(i, j, r);
+          else
+            ((uint16_t *)sA)[ml * HC + cl] = (uint16_t)f32_to_bf16_rne(value(i, j, r));
+        }
+      }
+    __syncthreads();
+    constexpr int CPR = HC / PER;  // 16-byte chunks per row
+    for (int c = tid; c < RP * CPR; c += 256) {
+      const int ml = c / CPR, ch = c - ml * CPR;
+      const int m = pass * RP + ml, col = nt * HC + PER * ch;
+      if (m < mrows && col < p.n_out)
+        *(u32x4_t *)(obase + ((size_t)(r0 + m) * p.ldo + col) * EB) = *(const u32x4_t *)(sA + (ml * CPR + ch) * 16);
     }
   }
 }
