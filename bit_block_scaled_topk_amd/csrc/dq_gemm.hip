@@ -136,7 +136,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // Activation loads: instruction i of wavefront w fills rows 4g .. 4g + 3,
   // g = 8w + i; lane l takes row 4g + l/16, slot l%16, i.e. cell
   // (l%16) ^ (row & 15) of the row.
-  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.a, p.a_bytes);
   uint32_t a_off[8];
   int a_k[8];  // first k of the lane's cell
 #pragma unroll
@@ -168,6 +167,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // gate half of a partial SwiGLU tile -- rows whose results are not stored
   const uint32_t c_off0 = (uint32_t)wrow0 * (uint32_t)(K >> 1) + 16u * q;
   const uint32_t s_off0 = (uint32_t)wrow0 * (uint32_t)(K >> 4) + 2u * q;
+  // A wavefront whose output columns all lie past n_out (the last column tile
+  // of a ragged width, e.g. 1856 = 7 x 256 + 64) skips its MFMAs and decode:
+  // it still fills its share of the activation tile and meets every barrier,
+  // and its zero accumulators are never stored.
+  const int first_col = (EPI == EPI_SWIGLU) ? nt * 128 + wave * 32 : nt * BN + wave * 64;
+  const bool idle = __builtin_amdgcn_readfirstlane(first_col) >= p.n_out;
 
   f32x4_t acc[8][4];
 #pragma unroll
@@ -175,10 +180,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // The scales stay 16-bit until they are used after the next barrier:
+  // widened where they are loaded, the compiler waits for the loads just
+  // issued (s_waitcnt vmcnt) to zero-extend them, and the chunk-ahead
+  // prefetch is lost.
   u32x4_t rc[4];
-  uint32_t rs[4];
-  auto load = [&](int k0, int buf) {
-    uint8_t *dst = sA + buf * A_BYTES + wave * 8192;
+  uint16_t rs[4];
+  auto load = [&](int k0, uint8_t *abuf, __amdgpu_buffer_rsrc_t a_rsrc) {
+    uint8_t *dst = abuf + wave * 8192;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t off = (k0 + a_k[i] < K) ? a_off[i] + 2u * (uint32_t)k0 : OOB;
@@ -199,19 +208,28 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
   for (int s = 0; s < 4; ++s) fa[s] = nl * 256 + (((4 * q + s) ^ nl) << 4);
 
-  load(0, 0);
-  int buf = 0;
-  for (int k0 = 0; k0 < K; k0 += BK, buf ^= 1) {
+  // One chunk: wait for its operands, request the next chunk's into the other
+  // buffer, compute.  `cur` and `nxt` are declared non-aliasing so that the
+  // compiler does not make the LDS reads of `cur` wait for the buffer-to-LDS
+  // loads into `nxt` (it cannot tell them apart otherwise, and inserts a
+  // vmcnt wait that serialises every chunk's loads with its compute).  Across
+  // chunks the roles swap; the explicit vmcnt(0) and barrier at the top of
+  // each chunk order those accesses.  The activation resource is built here
+  // from a restrict pointer so that the loads carry their own alias scope.
+  auto chunk = [&](const uint8_t *__restrict__ cur, uint8_t *__restrict__ nxt, const void *__restrict__ a_src, int k0) {
     loads_done_barrier();
     u32x4_t cc[4];
-    float s0[4], s1[4];
+    uint16_t cs[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       cc[j] = rc[j];
-      e4m3x2_to_f32(rs[j], s0[j], s1[j]);
+      cs[j] = rs[j];
     }
-    if (k0 + BK < K) load(k0 + BK, buf ^ 1);
-    const uint8_t *sa = sA + buf * A_BYTES;
+    if (k0 + BK < K) load(k0 + BK, nxt, make_rsrc(a_src, p.a_bytes));
+    if (idle) return;
+    float s0[4], s1[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) e4m3x2_to_f32(cs[j], s0[j], s1[j]);
     // Software pipeline over the chunk's 32 groups g = 8 s + i (step s,
     // fragment i): group g issues the LDS read of fragment g + 2, its four
     // MFMAs, and a quarter of the next step's weight decode; sched_barriers
@@ -219,14 +237,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     u32x4_t bw[4], bn[4], af[3];
 #pragma unroll
     for (int j = 0; j < 4; ++j) bw[j] = dq8_bf16(cc[j][0], s0[j]);
-    af[0] = *(const u32x4_t *)(sa + fa[0]);
-    af[1] = *(const u32x4_t *)(sa + fa[0] + 4096);
+    af[0] = *(const u32x4_t *)(cur + fa[0]);
+    af[1] = *(const u32x4_t *)(cur + fa[0] + 4096);
 #pragma unroll
     for (int g = 0; g < 32; ++g) {
       const int st = g >> 3, i = g & 7;
       if (g + 2 < 32) {
         const int g2 = g + 2;
-        af[g2 % 3] = *(const u32x4_t *)(sa + fa[g2 >> 3] + (g2 & 7) * 4096);
+        af[g2 % 3] = *(const u32x4_t *)(cur + fa[g2 >> 3] + (g2 & 7) * 4096);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[g % 3], bw[j], acc[i][j]);
@@ -237,7 +255,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-  }
+  };
+
+  load(0, sA, make_rsrc(p.a, p.a_bytes));
+  for (int k0 = 0, buf = 0; k0 < K; k0 += BK, buf ^= 1) chunk(sA + buf * A_BYTES, sA + (buf ^ 1) * A_BYTES, p.a, k0);
 
   // Epilogue: lane holds D[m = 16 i + 4 q + r][column 16 j + nl of the
   // wavefront].  A bf16 h tile is staged in LDS (the activation buffers are
