@@ -27,6 +27,24 @@ struct GemmBatch {
   int count;
 };
 
+// Half of dq8_bf16: code bytes 2h and 2h + 1 of `w` (elements 4h .. 4h + 3)
+// into r[2h], r[2h + 1], exactly as dq8_bf16 decodes them.
+__device__ __forceinline__ void dq4_bf16(uint32_t w, float scale, int h, u32x4_t &r) {
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    f32x2_t v;
+    switch (2 * h + jj) {  // the byte selector must be an immediate
+      case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); break;
+      case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); break;
+      case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); break;
+      default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); break;
+    }
+    const uint32_t lo = __float_as_uint(v.x * scale);
+    const uint32_t hi = __float_as_uint(v.y * scale);
+    r[2 * h + jj] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);  // {hi[31:16], lo[31:16]}
+  }
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
@@ -232,8 +250,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int j = 0; j < 4; ++j) e4m3x2_to_f32(cs[j], s0[j], s1[j]);
     // Software pipeline over the chunk's 32 groups g = 8 s + i (step s,
     // fragment i): group g issues the LDS read of fragment g + 2, its four
-    // MFMAs, and a quarter of the next step's weight decode; sched_barriers
-    // keep that order, so LDS latency and the decode hide under the MFMAs.
+    // MFMAs, and an eighth of the next step's weight decode (half of one
+    // block's word); sched_barriers keep that order, so LDS latency and the
+    // decode hide under the MFMAs.
     u32x4_t bw[4], bn[4], af[3];
 #pragma unroll
     for (int j = 0; j < 4; ++j) bw[j] = dq8_bf16(cc[j][0], s0[j]);
@@ -248,7 +267,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[g % 3], bw[j], acc[i][j]);
-      if (st < 3 && i < 4) bn[i] = dq8_bf16(cc[i][st + 1], st + 1 < 2 ? s0[i] : s1[i]);
+      if (st < 3) dq4_bf16(cc[i >> 1][st + 1], st + 1 < 2 ? s0[i >> 1] : s1[i >> 1], i & 1, bn[i >> 1]);
       if (st < 3 && i == 7) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) bw[j] = bn[j];
