@@ -275,6 +275,22 @@ def test_grouped_linear(ops, a_dtype, path):
     assert normwise(got, ref) <= TOL_DECODE
 
 
+@pytest.mark.parametrize("counts", [[120, 128, 40, 200], [33, 202, 190, 215, 4]])
+def test_grouped_linear_prefill_row_mixes(ops, counts):
+    """The prefill GEMM over row counts around one and two 128-row m-tiles
+    (prefill4314 has about 202 rows per expert), with a k of 160 (a partial
+    128-wide chunk) and an expert of a few rows, against the oracle."""
+    rng = np.random.default_rng(31)
+    k, n_out = 160, 96
+    w = synth.random_nvfp4(32, len(counts), n_out, k)
+    a = synth.f32_to_bf16_bits(rng.standard_normal((sum(counts), k)).astype(np.float32))
+    off = _offsets(counts)
+    got = host(ops.nvfp4_grouped_linear(dev(a), dev(off), ops.DeviceNVFP4.from_host(w), max(counts),
+                                        gemv_max_rows=0))
+    ref = oracle.linear(oracle.bf16_bits_to_f64(a), off, w)
+    assert normwise(got, ref) <= TOL_DECODE
+
+
 def test_grouped_linear_mixed_paths(ops):
     """Experts on both sides of the 32-row threshold in one call."""
     rng = np.random.default_rng(13)
@@ -319,7 +335,9 @@ def test_layer_decode_workloads(ops, name):
 # 64-wide steps (d 96, d_ff 160, shared 224) and the gated FFN (SwiGLU gate
 # and up rows side by side in the weight tile).
 FORCED_PREFILL_CASES = [("tiny16", dict()), ("tiny16", dict(n=24, d=96, f=160, fs=224, seed=21)),
-                        ("gated2", dict(n=40, seed=22))]
+                        ("gated2", dict(n=40, seed=22)),
+                        # about 128 rows per expert, shared expert over four m-tiles
+                        ("tiny16", dict(n=512, seed=24))]
 
 
 @pytest.mark.parametrize("case", range(len(FORCED_PREFILL_CASES)))
