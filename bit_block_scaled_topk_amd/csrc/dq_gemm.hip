@@ -265,8 +265,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int g2 = g + 2;
         af[g2 % 3] = *(const u32x4_t *)(cur + fa[g2 >> 3] + (g2 & 7) * 4096);
       }
+      // f32 outputs: weights as the MFMA's A operand and activations as its
+      // B, so the product comes out transposed and each lane holds four
+      // consecutive columns of one row (16-byte output stores)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[g % 3], bw[j], acc[i][j]);
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = EPI == EPI_F32 ? mfma16x16x32(bw[j], af[g % 3], acc[i][j]) : mfma16x16x32(af[g % 3], bw[j], acc[i][j]);
       if (st < 3) dq4_bf16(cc[i >> 1][st + 1], st + 1 < 2 ? s0[i >> 1] : s1[i >> 1], i & 1, bn[i >> 1]);
       if (st < 3 && i == 7) {
 #pragma unroll
@@ -279,12 +283,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   load(0, sA, make_rsrc(p.a, p.a_bytes));
   for (int k0 = 0, buf = 0; k0 < K; k0 += BK, buf ^= 1) chunk(sA + buf * A_BYTES, sA + (buf ^ 1) * A_BYTES, p.a, k0);
 
-  // Epilogue: lane holds D[m = 16 i + 4 q + r][column 16 j + nl of the
+  // Epilogue.  f32 outputs (transposed product): lane holds D[m = 16 i + nl]
+  // [column 16 j + 4 q + r of the wavefront], r = 0..3, written with one
+  // 16-byte store per (i, j); four 4-byte element stores per lane, as the
+  // other order gives, cost the down projection about 9 % of its time.
+  // Other outputs: lane holds D[m = 16 i + 4 q + r][column 16 j + nl of the
   // wavefront].  A bf16 h tile is staged in LDS (the activation buffers are
   // free now) and written back as whole rows with 16-byte stores: 2-byte
   // element stores of 16-column row pieces cost the up projection about a
-  // quarter of its time.  That takes 16-byte aligned rows whose width n_out is
-  // a whole number of chunks; other outputs get element stores.
+  // quarter of its time.  Both take 16-byte aligned rows whose width n_out is
+  // a whole number of 16-byte chunks; other outputs get element stores.
   const float gl = p.global[e];
   auto value = [&](int i, int j, int r) -> float {  // the output of accumulator (i, j, r)
     if (EPI == EPI_F32) return gl * acc[i][j][r];
@@ -302,58 +310,72 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int EB = (EPI == EPI_F32) ? 4 : 2;         // output element bytes
   constexpr int PER = 16 / EB;                         // elements per 16-byte chunk
   const uintptr_t obase = EPI == EPI_F32 ? (uintptr_t)p.out_f32 : (uintptr_t)p.out_h;
-  // (f32 rows are staged only when it pays: measured, it does not for the
-  // down projection, whose 16-lane pieces are already 64 bytes)
-  const bool vec = EPI != EPI_F32 && ((obase | (uintptr_t)(p.ldo * EB)) & 15) == 0 && p.n_out % PER == 0;
-  const int c0 = nt * HC + wave * (16 * JN);  // first output column of this wavefront
-  if (!vec) {
+  if constexpr (EPI == EPI_F32) {
+    const bool aligned = (((uintptr_t)p.out_f32 | (uintptr_t)(p.ldo * 4)) & 15) == 0 && p.n_out % 4 == 0;
+    const int c0 = nt * BN + wave * 64;  // first output column of this wavefront
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = 16 * i + nl;
+      if (m >= mrows) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = c0 + 16 * j + 4 * q;  // a multiple of 4
+        if (col >= p.n_out) continue;
+        const size_t o = (size_t)(r0 + m) * p.ldo + col;
+        if (aligned) {  // n_out % 4 == 0: all four columns are in range
+          f32x4_t v;
+          v.x = value(i, j, 0);
+          v.y = value(i, j, 1);
+          v.z = value(i, j, 2);
+          v.w = value(i, j, 3);
+          *(f32x4_t *)(p.out_f32 + o) = v;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (col + r < p.n_out) p.out_f32[o + r] = value(i, j, r);
+        }
+      }
+    }
+  } else {
+    const bool vec = ((obase | (uintptr_t)(p.ldo * EB)) & 15) == 0 && p.n_out % PER == 0;
+    const int c0 = nt * HC + wave * (16 * JN);  // first output column of this wavefront
+    if (!vec) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = 16 * i + 4 * q + r;
+          if (m >= mrows) continue;
+#pragma unroll
+          for (int j = 0; j < JN; ++j) {
+            const int col = c0 + 16 * j + nl;
+            if (col >= p.n_out) continue;
+            p.out_h[(size_t)(r0 + m) * p.ldo + col] = (uint16_t)f32_to_bf16_rne(value(i, j, r));
+          }
+        }
+      return;
+    }
+    // the 64 KB activation buffers hold the whole bf16 tile
+    static_assert(BM * HC * EB <= 2 * A_BYTES, "the staged tile fits the activation buffers");
+    __syncthreads();  // every wavefront is done reading the activation buffers
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = 16 * i + 4 * q + r;
-        if (m >= mrows) continue;
-#pragma unroll
-        for (int j = 0; j < JN; ++j) {
-          const int col = c0 + 16 * j + nl;
-          if (col >= p.n_out) continue;
-          const size_t o = (size_t)(r0 + m) * p.ldo + col;
-          if (EPI == EPI_F32)
-            p.out_f32[o] = value(i, j, r);
-          else
-            p.out_h[o] = (uint16_t)f32_to_bf16_rne(value(i, j, r));
-        }
-      }
-    return;
-  }
-  // rows per LDS pass: the 64 KB activation buffers hold the whole bf16 tile, or 64 rows of f32
-  constexpr int RP = 65536 / (HC * EB) < BM ? 65536 / (HC * EB) : BM;
-  static_assert(BM % RP == 0 && RP % 16 == 0, "whole 16-row blocks per pass");
-  __syncthreads();  // every wavefront is done reading the activation buffers
-#pragma unroll
-  for (int pass = 0; pass < BM / RP; ++pass) {
-    if (pass) __syncthreads();  // the previous pass has been written back
-#pragma unroll
-    for (int i = pass * (RP / 16); i < (pass + 1) * (RP / 16); ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ml = 16 * i + 4 * q + r - pass * RP;
+        const int ml = 16 * i + 4 * q + r;
 #pragma unroll
         for (int j = 0; j < JN; ++j) {
           const int cl = wave * (16 * JN) + 16 * j + nl;
-          if (EPI == EPI_F32)
-            ((float *)sA)[ml * HC + cl] = value(i, j, r);
-          else
-            ((uint16_t *)sA)[ml * HC + cl] = (uint16_t)f32_to_bf16_rne(value(i, j, r));
+          ((uint16_t *)sA)[ml * HC + cl] = (uint16_t)f32_to_bf16_rne(value(i, j, r));
         }
       }
     __syncthreads();
     constexpr int CPR = HC / PER;  // 16-byte chunks per row
-    for (int c = tid; c < RP * CPR; c += 256) {
+    for (int c = tid; c < BM * CPR; c += 256) {
       const int ml = c / CPR, ch = c - ml * CPR;
-      const int m = pass * RP + ml, col = nt * HC + PER * ch;
-      if (m < mrows && col < p.n_out)
-        *(u32x4_t *)(obase + ((size_t)(r0 + m) * p.ldo + col) * EB) = *(const u32x4_t *)(sA + (ml * CPR + ch) * 16);
+      const int col = nt * HC + PER * ch;
+      if (ml < mrows && col < p.n_out)
+        *(u32x4_t *)(obase + ((size_t)(r0 + ml) * p.ldo + col) * EB) = *(const u32x4_t *)(sA + (ml * CPR + ch) * 16);
     }
   }
 }

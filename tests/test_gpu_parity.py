@@ -275,13 +275,16 @@ def test_grouped_linear(ops, a_dtype, path):
     assert normwise(got, ref) <= TOL_DECODE
 
 
+@pytest.mark.parametrize("n_out", [96, 90])
 @pytest.mark.parametrize("counts", [[120, 128, 40, 200], [33, 202, 190, 215, 4]])
-def test_grouped_linear_prefill_row_mixes(ops, counts):
+def test_grouped_linear_prefill_row_mixes(ops, counts, n_out):
     """The prefill GEMM over row counts around one and two 128-row m-tiles
     (prefill4314 has about 202 rows per expert), with a k of 160 (a partial
-    128-wide chunk) and an expert of a few rows, against the oracle."""
+    128-wide chunk) and an expert of a few rows, against the oracle.  An
+    output width that is not a multiple of 4 takes the element stores instead
+    of the 16-byte ones."""
     rng = np.random.default_rng(31)
-    k, n_out = 160, 96
+    k = 160
     w = synth.random_nvfp4(32, len(counts), n_out, k)
     a = synth.f32_to_bf16_bits(rng.standard_normal((sum(counts), k)).astype(np.float32))
     off = _offsets(counts)
