@@ -22,6 +22,11 @@ constexpr uint32_t OOB = 0x80000000u; // a buffer offset past every extent: the 
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
 struct GemmBatch {
   ProjProblem p[2];
   int count;
@@ -116,7 +121,14 @@ __device__ __forceinline__ void find_tile(const int32_t *offsets, int E, int n_r
 // contiguously.  Rows past the expert's and k past K load as zero (offsets
 // beyond the buffer's extent), so partial tiles need no branches.  One barrier
 // per chunk.
-template <int EPI>
+//
+// SP (K a multiple of 64, scales 4-byte aligned): the e4m3 scales are loaded
+// for a pair of chunks at a time -- lane (n, q) loads bytes 4q .. 4q + 3 of
+// the pair's 16 bytes of its weight row (chunk q >> 1, k-slices 2 (q & 1) and
+// 2 (q & 1) + 1) -- and handed to the lanes that use them with ds_bpermute.
+// One 2-byte load per chunk and block cost a third of the kernel's requests
+// to L2 (each its own cache line) and 10-17 % of its time.
+template <int EPI, bool SP>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) k_dq_gemm(GemmBatch batch) {
   __shared__ int s_info[3];
   __shared__ __attribute__((aligned(1024))) uint8_t sA[2 * A_BYTES];
@@ -184,7 +196,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // a column past n_out reads past the expert's rows (zero), or -- for the
   // gate half of a partial SwiGLU tile -- rows whose results are not stored
   const uint32_t c_off0 = (uint32_t)wrow0 * (uint32_t)(K >> 1) + 16u * q;
-  const uint32_t s_off0 = (uint32_t)wrow0 * (uint32_t)(K >> 4) + 2u * q;
+  const uint32_t s_off0 = (uint32_t)wrow0 * (uint32_t)(K >> 4) + (SP ? 4u : 2u) * q;
   // A wavefront whose output columns all lie past n_out (the last column tile
   // of a ragged width, e.g. 1856 = 7 x 256 + 64) skips its MFMAs and decode:
   // it still fills its share of the activation tile and meets every barrier,
@@ -198,13 +210,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // The scales stay 16-bit until they are used after the next barrier:
-  // widened where they are loaded, the compiler waits for the loads just
-  // issued (s_waitcnt vmcnt) to zero-extend them, and the chunk-ahead
-  // prefetch is lost.
   u32x4_t rc[4];
-  uint16_t rs[4];
-  auto load = [&](int k0, uint8_t *abuf, __amdgpu_buffer_rsrc_t a_rsrc) {
+  // Scales as loaded (SP: a chunk pair) and those of the chunk (pair) in use.
+  // The 2-byte loads stay 16-bit until they are used after the next barrier:
+  // widened where they are loaded, the compiler waits for the loads just
+  // issued (s_waitcnt vmcnt) to zero-extend them.
+  uint32_t rs32[4], cs[4];
+  uint16_t rs16[4];
+  auto load = [&](int k0, uint8_t *abuf, __amdgpu_buffer_rsrc_t a_rsrc, bool with_scales) {
     uint8_t *dst = abuf + wave * 8192;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -212,12 +225,18 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void *)(dst + i * 1024), 16, off, 0, 0, 0);
     }
     const bool b_in = k0 + 32 * q < K;
+    // SP: this lane's two k-slices of the pair (64 k, so whole or absent)
+    const bool s_in = SP ? k0 + 128 * (q >> 1) + 64 * (q & 1) < K : b_in;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t co = b_in ? c_off0 + (uint32_t)(dj[j] * (K >> 1)) + (uint32_t)(k0 >> 1) : OOB;
-      const uint32_t so = b_in ? s_off0 + (uint32_t)(dj[j] * (K >> 4)) + (uint32_t)(k0 >> 4) : OOB;
       rc[j] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, co, 0, 0);
-      rs[j] = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, so, 0, 0);
+      const uint32_t so = s_in ? s_off0 + (uint32_t)(dj[j] * (K >> 4)) + (uint32_t)(k0 >> 4) : OOB;
+      if constexpr (SP) {
+        if (with_scales) rs32[j] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, so, 0, 0);
+      } else {
+        rs16[j] = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, so, 0, 0);
+      }
     }
   };
 
@@ -235,19 +254,32 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // each chunk order those accesses.  The activation resource is built here
   // from a restrict pointer so that the loads carry their own alias scope.
   auto chunk = [&](const uint8_t *__restrict__ cur, uint8_t *__restrict__ nxt, const void *__restrict__ a_src, int k0) {
+    // SP: the chunk's place in its pair; the pair's scales (loaded with the
+    // pair's first chunk's codes) stay in rs32 through both of its chunks, and
+    // the next pair's are requested only after this copy
+    const int par = (k0 / BK) & 1;
     loads_done_barrier();
     u32x4_t cc[4];
-    uint16_t cs[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       cc[j] = rc[j];
-      cs[j] = rs[j];
+      if constexpr (SP)
+        cs[j] = rs32[j];
+      else
+        cs[j] = rs16[j];
     }
-    if (k0 + BK < K) load(k0 + BK, nxt, make_rsrc(a_src, p.a_bytes));
+    if (k0 + BK < K) load(k0 + BK, nxt, make_rsrc(a_src, p.a_bytes), !SP || par == 1);
     if (idle) return;
     float s0[4], s1[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) e4m3x2_to_f32(cs[j], s0[j], s1[j]);
+    for (int j = 0; j < 4; ++j) {
+      uint32_t two = cs[j];
+      if constexpr (SP) {  // slice q of chunk PAR: lane 2 PAR + (q >> 1) of this row, half q & 1
+        two = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (nl + 16 * (2 * par + (q >> 1))), (int)two);
+        two >>= 16 * (q & 1);
+      }
+      e4m3x2_to_f32(two, s0[j], s1[j]);
+    }
     // Software pipeline over the chunk's 32 groups g = 8 s + i (step s,
     // fragment i): group g issues the LDS read of fragment g + 2, its four
     // MFMAs, and an eighth of the next step's weight decode (half of one
@@ -280,7 +312,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
 
-  load(0, sA, make_rsrc(p.a, p.a_bytes));
+  load(0, sA, make_rsrc(p.a, p.a_bytes), true);
   for (int k0 = 0, buf = 0; k0 < K; k0 += BK, buf ^= 1) chunk(sA + buf * A_BYTES, sA + (buf ^ 1) * A_BYTES, p.a, k0);
 
   // Epilogue.  f32 outputs (transposed product): lane holds D[m = 16 i + nl]
@@ -412,11 +444,19 @@ hipError_t launch_dq_gemm(ProjProblem *probs, int count, int epi, hipStream_t st
   }
   if (b.count == 0) return hipSuccess;
   if (b.count == 1) b.p[1] = b.p[0];
+  // scales a chunk pair at a time when every problem's k is a multiple of 64
+  // and its scales are 4-byte aligned
+  bool sp = true;
+  for (int i = 0; i < b.count; ++i)
+    sp = sp && b.p[i].k % 64 == 0 && ((uintptr_t)b.p[i].scales & 3) == 0;
   dim3 grid((unsigned)total), block(256);
-  switch (epi) {
-    case EPI_F32: hipLaunchKernelGGL(k_dq_gemm<EPI_F32>, grid, block, 0, stream, b); break;
-    case EPI_RELU2: hipLaunchKernelGGL(k_dq_gemm<EPI_RELU2>, grid, block, 0, stream, b); break;
-    default: hipLaunchKernelGGL(k_dq_gemm<EPI_SWIGLU>, grid, block, 0, stream, b); break;
+  switch (epi * 2 + (sp ? 1 : 0)) {
+    case EPI_F32 * 2: hipLaunchKernelGGL((k_dq_gemm<EPI_F32, false>), grid, block, 0, stream, b); break;
+    case EPI_F32 * 2 + 1: hipLaunchKernelGGL((k_dq_gemm<EPI_F32, true>), grid, block, 0, stream, b); break;
+    case EPI_RELU2 * 2: hipLaunchKernelGGL((k_dq_gemm<EPI_RELU2, false>), grid, block, 0, stream, b); break;
+    case EPI_RELU2 * 2 + 1: hipLaunchKernelGGL((k_dq_gemm<EPI_RELU2, true>), grid, block, 0, stream, b); break;
+    case EPI_SWIGLU * 2: hipLaunchKernelGGL((k_dq_gemm<EPI_SWIGLU, false>), grid, block, 0, stream, b); break;
+    default: hipLaunchKernelGGL((k_dq_gemm<EPI_SWIGLU, true>), grid, block, 0, stream, b); break;
   }
   return hipGetLastError();
 }
