@@ -22,11 +22,6 @@ constexpr uint32_t OOB = 0x80000000u; // a buffer offset past every extent: the 
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int N>
-struct IntC {
-  static constexpr int value = N;
-};
-
 struct GemmBatch {
   ProjProblem p[2];
   int count;
@@ -126,8 +121,9 @@ __device__ __forceinline__ void find_tile(const int32_t *offsets, int E, int n_r
 // for a pair of chunks at a time -- lane (n, q) loads bytes 4q .. 4q + 3 of
 // the pair's 16 bytes of its weight row (chunk q >> 1, k-slices 2 (q & 1) and
 // 2 (q & 1) + 1) -- and handed to the lanes that use them with ds_bpermute.
-// One 2-byte load per chunk and block cost a third of the kernel's requests
-// to L2 (each its own cache line) and 10-17 % of its time.
+// The 2-byte loads, one per chunk and block, were a third of the kernel's
+// requests to L2 (each row's 8 bytes on its own cache line); a timing probe
+// without any scale loads ran 10-17 % faster.
 template <int EPI, bool SP>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) k_dq_gemm(GemmBatch batch) {
   __shared__ int s_info[3];
