@@ -218,6 +218,16 @@ def main():
         copies.append(tuple(None if w is None else ops.DeviceNVFP4(w.codes.clone(), w.scales.clone(),
                                                                    w.globals_.clone(), w.rows, w.cols)
                             for w in layer.weights()))
+    # the one-time scale repack of each copy (the prefill GEMM reads it), timed
+    # apart from the steps
+    torch.cuda.synchronize()
+    t_pack = time.perf_counter()
+    for c in copies[1:]:
+        for w in c:
+            if w is not None:
+                w.pack()
+    torch.cuda.synchronize()
+    prepack_ms = (time.perf_counter() - t_pack) * 1e3 / max(1, len(copies) - 1)
     xs = inp.x.view(np.int16) if inp.x.dtype == np.uint16 else inp.x
     x = torch.from_numpy(np.ascontiguousarray(xs)).to(dev)
     logits = torch.from_numpy(inp.logits).to(dev)
@@ -341,6 +351,7 @@ def main():
         "cpu_baseline": cpu,
         "step_breakdown_us": {k: round(v, 2) for k, v in breakdown.items()},
         "input_gen_s": round(gen_s, 1),
+        "prepack_ms_per_weight_set": round(prepack_ms, 3),
     }
     print(json.dumps(line))
 

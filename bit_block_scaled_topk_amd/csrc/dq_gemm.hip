@@ -117,15 +117,19 @@ __device__ __forceinline__ void find_tile(const int32_t *offsets, int E, int n_r
 // beyond the buffer's extent), so partial tiles need no branches.  One barrier
 // per chunk.
 //
-// SP (K a multiple of 64, scales 4-byte aligned): the e4m3 scales are loaded
+// SM, how the e4m3 scales are loaded: 0, one 2-byte load per chunk and block
+// from the canonical layout; 2, the same from the repacked layout (a block's
+// 16 rows of one chunk in one 128-byte line instead of 16 lines); 1 (K a
+// multiple of 64, scales 4-byte aligned, no repacked copy): loaded
 // for a pair of chunks at a time -- lane (n, q) loads bytes 4q .. 4q + 3 of
 // the pair's 16 bytes of its weight row (chunk q >> 1, k-slices 2 (q & 1) and
 // 2 (q & 1) + 1) -- and handed to the lanes that use them with ds_bpermute.
 // The 2-byte loads, one per chunk and block, were a third of the kernel's
 // requests to L2 (each row's 8 bytes on its own cache line); a timing probe
 // without any scale loads ran 10-17 % faster.
-template <int EPI, bool SP>
+template <int EPI, int SM>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) k_dq_gemm(GemmBatch batch) {
+  constexpr bool SP = SM == 1;
   __shared__ int s_info[3];
   __shared__ __attribute__((aligned(1024))) uint8_t sA[2 * A_BYTES];
 
@@ -178,7 +182,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int nl = lane & 15, q = lane >> 4;
   const size_t e_rows = (size_t)e * p.n_w;
   const __amdgpu_buffer_rsrc_t c_rsrc = make_rsrc(p.codes + e_rows * (size_t)(K >> 1), (uint32_t)p.n_w * (uint32_t)(K >> 1));
-  const __amdgpu_buffer_rsrc_t s_rsrc = make_rsrc(p.scales + e_rows * (size_t)(K >> 4), (uint32_t)p.n_w * (uint32_t)(K >> 4));
+  // repacked scales (SM 2): [16-row block][128-wide chunk][16 rows][8 bytes] per expert
+  const uint32_t nch = (uint32_t)(K + 127) >> 7, pk_bytes = (uint32_t)((p.n_w + 15) >> 4) * nch * 128u;
+  const __amdgpu_buffer_rsrc_t s_rsrc =
+      SM == 2 ? make_rsrc(p.scales_packed + (size_t)e * pk_bytes, pk_bytes)
+              : make_rsrc(p.scales + e_rows * (size_t)(K >> 4), (uint32_t)p.n_w * (uint32_t)(K >> 4));
   int wrow0, dj[4];
   if (EPI == EPI_SWIGLU) {  // blocks 0, 1: gate rows; 2, 3: the matching up rows
     wrow0 = nt * 128 + wave * 32 + nl;
@@ -192,7 +200,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // a column past n_out reads past the expert's rows (zero), or -- for the
   // gate half of a partial SwiGLU tile -- rows whose results are not stored
   const uint32_t c_off0 = (uint32_t)wrow0 * (uint32_t)(K >> 1) + 16u * q;
-  const uint32_t s_off0 = (uint32_t)wrow0 * (uint32_t)(K >> 4) + (SP ? 4u : 2u) * q;
+  const uint32_t s_off0 = SM == 2 ? 8u * (uint32_t)nl + 2u * q : (uint32_t)wrow0 * (uint32_t)(K >> 4) + (SP ? 4u : 2u) * q;
   // A wavefront whose output columns all lie past n_out (the last column tile
   // of a ragged width, e.g. 1856 = 7 x 256 + 64) skips its MFMAs and decode:
   // it still fills its share of the activation tile and meets every barrier,
@@ -227,7 +235,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int j = 0; j < 4; ++j) {
       const uint32_t co = b_in ? c_off0 + (uint32_t)(dj[j] * (K >> 1)) + (uint32_t)(k0 >> 1) : OOB;
       rc[j] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, co, 0, 0);
-      const uint32_t so = s_in ? s_off0 + (uint32_t)(dj[j] * (K >> 4)) + (uint32_t)(k0 >> 4) : OOB;
+      uint32_t so;
+      if constexpr (SM == 2)  // this lane's row's 16-row block, chunk k0 / 128
+        so = s_in ? s_off0 + ((uint32_t)((wrow0 - nl + dj[j]) >> 4) * nch + (uint32_t)(k0 >> 7)) * 128u : OOB;
+      else
+        so = s_in ? s_off0 + (uint32_t)(dj[j] * (K >> 4)) + (uint32_t)(k0 >> 4) : OOB;
       if constexpr (SP) {
         if (with_scales) rs32[j] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, so, 0, 0);
       } else {
@@ -440,20 +452,70 @@ hipError_t launch_dq_gemm(ProjProblem *probs, int count, int epi, hipStream_t st
   }
   if (b.count == 0) return hipSuccess;
   if (b.count == 1) b.p[1] = b.p[0];
-  // scales a chunk pair at a time when every problem's k is a multiple of 64
-  // and its scales are 4-byte aligned
-  bool sp = true;
-  for (int i = 0; i < b.count; ++i)
-    sp = sp && b.p[i].k % 64 == 0 && ((uintptr_t)b.p[i].scales & 3) == 0;
-  dim3 grid((unsigned)total), block(256);
-  switch (epi * 2 + (sp ? 1 : 0)) {
-    case EPI_F32 * 2: hipLaunchKernelGGL((k_dq_gemm<EPI_F32, false>), grid, block, 0, stream, b); break;
-    case EPI_F32 * 2 + 1: hipLaunchKernelGGL((k_dq_gemm<EPI_F32, true>), grid, block, 0, stream, b); break;
-    case EPI_RELU2 * 2: hipLaunchKernelGGL((k_dq_gemm<EPI_RELU2, false>), grid, block, 0, stream, b); break;
-    case EPI_RELU2 * 2 + 1: hipLaunchKernelGGL((k_dq_gemm<EPI_RELU2, true>), grid, block, 0, stream, b); break;
-    case EPI_SWIGLU * 2: hipLaunchKernelGGL((k_dq_gemm<EPI_SWIGLU, false>), grid, block, 0, stream, b); break;
-    default: hipLaunchKernelGGL((k_dq_gemm<EPI_SWIGLU, true>), grid, block, 0, stream, b); break;
+  // the repacked scales when every problem has them and whole 16-row blocks
+  // (SwiGLU: its gate and up halves too); else a chunk pair of scales at a
+  // time when every problem's k is a multiple of 64 and its scales are 4-byte
+  // aligned; else one chunk's at a time
+  bool pk = true, sp = true;
+  for (int i = 0; i < b.count; ++i) {
+    const ProjProblem &q = b.p[i];
+    pk = pk && q.scales_packed != nullptr && q.n_w % 16 == 0 && (epi != EPI_SWIGLU || q.n_out % 16 == 0);
+    sp = sp && q.k % 64 == 0 && ((uintptr_t)q.scales & 3) == 0;
   }
+  const int sm = pk ? 2 : sp ? 1 : 0;
+  dim3 grid((unsigned)total), block(256);
+  switch (epi * 3 + sm) {
+    case EPI_F32 * 3 + 0: hipLaunchKernelGGL((k_dq_gemm<EPI_F32, 0>), grid, block, 0, stream, b); break;
+    case EPI_F32 * 3 + 1: hipLaunchKernelGGL((k_dq_gemm<EPI_F32, 1>), grid, block, 0, stream, b); break;
+    case EPI_F32 * 3 + 2: hipLaunchKernelGGL((k_dq_gemm<EPI_F32, 2>), grid, block, 0, stream, b); break;
+    case EPI_RELU2 * 3 + 0: hipLaunchKernelGGL((k_dq_gemm<EPI_RELU2, 0>), grid, block, 0, stream, b); break;
+    case EPI_RELU2 * 3 + 1: hipLaunchKernelGGL((k_dq_gemm<EPI_RELU2, 1>), grid, block, 0, stream, b); break;
+    case EPI_RELU2 * 3 + 2: hipLaunchKernelGGL((k_dq_gemm<EPI_RELU2, 2>), grid, block, 0, stream, b); break;
+    case EPI_SWIGLU * 3 + 0: hipLaunchKernelGGL((k_dq_gemm<EPI_SWIGLU, 0>), grid, block, 0, stream, b); break;
+    case EPI_SWIGLU * 3 + 1: hipLaunchKernelGGL((k_dq_gemm<EPI_SWIGLU, 1>), grid, block, 0, stream, b); break;
+    default: hipLaunchKernelGGL((k_dq_gemm<EPI_SWIGLU, 2>), grid, block, 0, stream, b); break;
+  }
+  return hipGetLastError();
+}
+
+// One 8-byte unit u = ((e nrb + b) nch + c) 16 + r of the repacked scales per
+// thread: row 16 b + r of expert e, bytes 8 c .. 8 c + 7 of its kb scale bytes
+// (zero past the row count or past kb).
+__global__ void __launch_bounds__(256) k_pack_scales(const uint8_t *__restrict__ s, int rows, int kb, int nrb, int nch,
+                                                     long units, uint8_t *__restrict__ dst) {
+  const long u = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= units) return;
+  const int r = (int)(u & 15);
+  long t = u >> 4;
+  const int c = (int)(t % nch);
+  t /= nch;
+  const int blk = (int)(t % nrb);
+  const long e = t / nrb;
+  const int row = 16 * blk + r;
+  uint32_t w[2] = {0u, 0u};
+  if (row < rows) {
+    const uint8_t *src = s + (e * rows + row) * (long)kb + 8 * c;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (8 * c + i < kb) w[i >> 2] |= (uint32_t)src[i] << (8 * (i & 3));
+  }
+  uint2 v;
+  v.x = w[0];
+  v.y = w[1];
+  ((uint2 *)dst)[u] = v;
+}
+
+long packed_scales_bytes(long n_experts, int rows, int cols) {
+  return n_experts * (long)((rows + 15) / 16) * (long)((cols + 127) / 128) * 128L;
+}
+
+hipError_t launch_pack_scales(const uint8_t *scales, int n_experts, int rows, int cols, uint8_t *dst,
+                              hipStream_t stream) {
+  const int nrb = (rows + 15) / 16, nch = (cols + 127) / 128;
+  const long units = (long)n_experts * nrb * nch * 16;
+  if (units <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pack_scales, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream, scales, rows,
+                     cols / 16, nrb, nch, units, dst);
   return hipGetLastError();
 }
 

@@ -58,6 +58,7 @@ struct ProjProblem {
   int min_rows, max_rows; // experts with min_rows..max_rows rows are handled
   const uint8_t *codes;   // [n_experts][n_w][k/2]
   const uint8_t *scales;  // [n_experts][n_w][k/16]
+  const uint8_t *scales_packed;  // optional: the same scales as nvfp4_pack_scales orders them
   const float *global;    // [n_experts]
   int n_w, k, n_out;
   float *out_f32;         // EPI_F32 output [n_rows][ldo]
@@ -77,6 +78,10 @@ hipError_t launch_dq_gemv(ProjProblem *probs, const int *max_active, int count, 
                           hipStream_t stream);
 
 // Prefill path: up to two problems in one launch; bf16 activations (plane 0).
+// The one-time scale repack: dst[e][b][c][r][i] = scales[e][16 b + r][8 c + i].
+long packed_scales_bytes(long n_experts, int rows, int cols);
+hipError_t launch_pack_scales(const uint8_t *scales, int n_experts, int rows, int cols, uint8_t *dst,
+                              hipStream_t stream);
 hipError_t launch_dq_gemm(ProjProblem *probs, int count, int epi, hipStream_t stream);
 
 // A whole decode step (n_tokens <= 2) in one persistent launch: routing, the

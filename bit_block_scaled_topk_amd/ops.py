@@ -40,7 +40,7 @@ class MoeError(RuntimeError):
 class NVFP4Weights(ctypes.Structure):
     """moe_nvfp4_weights: device pointers of one projection for E experts."""
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("global_", ctypes.c_void_p),
-                ("rows", ctypes.c_int), ("cols", ctypes.c_int)]
+                ("rows", ctypes.c_int), ("cols", ctypes.c_int), ("scales_packed", ctypes.c_void_p)]
 
 
 _P = ctypes.c_void_p
@@ -70,6 +70,10 @@ _lib.nvfp4_unpack_bf16.restype = _I
 _lib.nvfp4_grouped_linear.argtypes = [_P, _I, _I, _I, _P, _I, ctypes.POINTER(NVFP4Weights), _I, _P, _SZ,
                                       _P, _P]
 _lib.nvfp4_grouped_linear.restype = _I
+_lib.nvfp4_packed_scales_bytes.argtypes = [_I, _I, _I]
+_lib.nvfp4_packed_scales_bytes.restype = _SZ
+_lib.nvfp4_pack_scales.argtypes = [ctypes.POINTER(NVFP4Weights), _I, _P, _SZ, _P]
+_lib.nvfp4_pack_scales.restype = _I
 
 class LayerDesc(ctypes.Structure):
     """moe_layer_desc."""
@@ -101,7 +105,8 @@ _lib.moe_layer_forward_profiled.restype = _I
 EXPORTED = ("moe_route_topk", "moe_gather_workspace_size", "moe_gather_rows",
             "nvfp4_expert_ffn_workspace_size", "nvfp4_grouped_linear_workspace_size",
             "nvfp4_expert_ffn", "moe_weighted_row_sum", "moe_weighted_row_sum_into", "nvfp4_unpack_bf16",
-            "nvfp4_grouped_linear", "moe_status_string", "moe_layer_workspace_size",
+            "nvfp4_grouped_linear", "nvfp4_packed_scales_bytes", "nvfp4_pack_scales", "moe_status_string",
+            "moe_layer_workspace_size",
             "moe_layer_workspace_init", "moe_layer_get_views",
             "moe_layer_forward", "moe_layer_forward_profiled")
 
@@ -136,6 +141,7 @@ class DeviceNVFP4:
     globals_: torch.Tensor  # float32 [E]
     rows: int
     cols: int
+    scales_packed: Optional[torch.Tensor] = None  # uint8, nvfp4_pack_scales order (optional)
 
     @classmethod
     def from_host(cls, t, device="cuda") -> "DeviceNVFP4":
@@ -144,7 +150,14 @@ class DeviceNVFP4:
 
     def struct(self) -> NVFP4Weights:
         return NVFP4Weights(self.codes.data_ptr(), self.scales.data_ptr(), self.globals_.data_ptr(),
-                            self.rows, self.cols)
+                            self.rows, self.cols,
+                            None if self.scales_packed is None else self.scales_packed.data_ptr())
+
+    def pack(self, stream=None) -> "DeviceNVFP4":
+        """Repack the scales once (nvfp4_pack_scales); the prefill GEMM then reads
+        them.  Returns self."""
+        self.scales_packed = nvfp4_pack_scales(self, stream=stream)
+        return self
 
     @property
     def n_experts(self) -> int:
@@ -234,6 +247,20 @@ def nvfp4_unpack_bf16(codes: torch.Tensor, scales: torch.Tensor, rows: int, cols
     _check("nvfp4_unpack_bf16", _lib.nvfp4_unpack_bf16(_ptr(codes), _ptr(scales), rows, cols, _ptr(out),
                                                        _stream(stream)))
     return out
+
+
+def nvfp4_packed_scales_bytes(n_experts: int, rows: int, cols: int) -> int:
+    return int(_lib.nvfp4_packed_scales_bytes(n_experts, rows, cols))
+
+
+def nvfp4_pack_scales(w: DeviceNVFP4, dst: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    nbytes = nvfp4_packed_scales_bytes(w.n_experts, w.rows, w.cols)
+    if dst is None:
+        dst = torch.empty(nbytes, dtype=torch.uint8, device=w.scales.device)
+    s = w.struct()
+    _check("nvfp4_pack_scales", _lib.nvfp4_pack_scales(ctypes.byref(s), w.n_experts, _ptr(dst), dst.numel(),
+                                                       _stream(stream)))
+    return dst
 
 
 def nvfp4_grouped_linear(a: torch.Tensor, offsets: torch.Tensor, w: DeviceNVFP4, max_rows_per_expert: int,
@@ -345,6 +372,9 @@ class MoELayer:
         self.down = DeviceNVFP4.from_host(inp.down, device)
         self.shared_up = DeviceNVFP4.from_host(inp.shared_up, device) if inp.fs > 0 else None
         self.shared_down = DeviceNVFP4.from_host(inp.shared_down, device) if inp.fs > 0 else None
+        for w in self.weights():
+            if w is not None:
+                w.pack()  # the one-time scale repack the prefill GEMM reads
         self.device = device
         self.layer_ws = None
         self._alloc(self.n)
@@ -374,7 +404,7 @@ class MoELayer:
 
     def desc(self, weights=None, n_tokens: Optional[int] = None) -> LayerDesc:
         up, down, sup, sdn = weights if weights is not None else self.weights()
-        empty = NVFP4Weights(None, None, None, 0, 0)
+        empty = NVFP4Weights(None, None, None, 0, 0, None)
         return LayerDesc(self.n if n_tokens is None else n_tokens, self.d, self.E, self.K, self.x_dtype, self.act,
                          self.gemv_max_rows, up.struct(), down.struct(),
                          sup.struct() if sup is not None else empty, sdn.struct() if sdn is not None else empty)

@@ -78,7 +78,33 @@ typedef struct {
   const float *global;
   int rows; /* out_features */
   int cols; /* in_features, a multiple of 32 */
+  /* Optional (NULL: absent): the same scales reordered by nvfp4_pack_scales.
+   * The prefill GEMM reads them when present and rows is a multiple of 16;
+   * every other path reads `scales`.  Both must hold the same weights. */
+  const uint8_t *scales_packed;
 } moe_nvfp4_weights;
+
+/* nvfp4_packed_scales_bytes -- bytes of the reordered scales of n_experts
+ * experts of rows x cols: n_experts * ceil(rows/16) * ceil(cols/128) * 128
+ * (0 for non-positive sizes). */
+size_t nvfp4_packed_scales_bytes(int n_experts, int rows, int cols);
+
+/* nvfp4_pack_scales -- the optional one-time repack of a projection's e4m3
+ * block scales into the order the prefill GEMM reads them in (the boundary's
+ * "prepack": same bytes, another order, no global):
+ *   dst[e][b][c][r][i] = scales[e][16 b + r][8 c + i]
+ * for 16-row block b, 128-column chunk c, row r < 16 and i < 8; entries past
+ * rows or past cols/16 are zero.  In that order one 16-row block's scales of
+ * one 128-wide k chunk are 128 contiguous bytes, one cache line, where the
+ * canonical layout spreads them over 16 (the GEMM's scale loads were a third
+ * of its requests to L2).
+ *   w       the projection (w->codes and w->global are not read)
+ *   dst     device, dst_bytes >= nvfp4_packed_scales_bytes(n_experts, rows, cols)
+ * Errors: MOE_INVALID_ARG for null pointers, n_experts < 1, rows < 1, cols not a
+ * positive multiple of 32, or dst_bytes too small; nothing is launched then.
+ * Stream-ordered on `stream`; allocates nothing. */
+moe_status nvfp4_pack_scales(const moe_nvfp4_weights *w, int n_experts, uint8_t *dst, size_t dst_bytes,
+                             hipStream_t stream);
 
 /* moe_route_topk -- per token, the top_k experts by router logit and their
  * weights, a softmax over the top_k picked logits only.

@@ -50,7 +50,7 @@ def test_binding_names_match_header():
 
 class W(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("global_", ctypes.c_void_p),
-                ("rows", ctypes.c_int), ("cols", ctypes.c_int)]
+                ("rows", ctypes.c_int), ("cols", ctypes.c_int), ("scales_packed", ctypes.c_void_p)]
 
 
 FAKE = ctypes.c_void_p(1 << 20)  # an aligned non-null address: never dereferenced on the host
@@ -71,6 +71,9 @@ def _setup(lib):
     lib.nvfp4_grouped_linear.argtypes = [P, I, I, I, P, I, ctypes.POINTER(W), I, P, SZ, P, P]
     lib.moe_status_string.argtypes = [I]
     lib.moe_status_string.restype = ctypes.c_char_p
+    lib.nvfp4_packed_scales_bytes.argtypes = [I, I, I]
+    lib.nvfp4_packed_scales_bytes.restype = SZ
+    lib.nvfp4_pack_scales.argtypes = [ctypes.POINTER(W), I, P, SZ, P]
 
 
 def test_status_strings(lib):
@@ -156,3 +159,21 @@ def test_wrs_and_unpack_and_linear_argument_errors(lib):
     assert lib.nvfp4_grouped_linear(FAKE, 1, 8, 8, FAKE, 2, ctypes.byref(w), 40, None, 0, FAKE, None) == 2
     # prefill path over a 2^25 x 64 bf16 activation matrix (4 GiB): refused
     assert lib.nvfp4_grouped_linear(FAKE, 1, 1 << 25, 64, FAKE, 2, ctypes.byref(w), 32, None, 0, FAKE, None) == 2
+
+
+def test_packed_scales_size_and_pack_argument_errors(lib):
+    """The repacked scale layout's size is n_experts * ceil(rows/16) *
+    ceil(cols/128) * 128 bytes (whole 16-row blocks and 128-wide chunks, 8 scale
+    bytes per row and chunk); bad arguments are refused before any launch."""
+    _setup(lib)
+    assert lib.nvfp4_packed_scales_bytes(128, 1856, 2688) == 128 * 116 * 21 * 128
+    assert lib.nvfp4_packed_scales_bytes(128, 2688, 1856) == 128 * 168 * 15 * 128
+    assert lib.nvfp4_packed_scales_bytes(3, 17, 32) == 3 * 2 * 1 * 128
+    assert lib.nvfp4_packed_scales_bytes(0, 16, 32) == 0
+    w = _w(64, 256)
+    need = lib.nvfp4_packed_scales_bytes(2, 64, 256)
+    assert lib.nvfp4_pack_scales(ctypes.byref(w), 2, FAKE, need - 1, None) == 1   # dst too small
+    assert lib.nvfp4_pack_scales(ctypes.byref(w), 0, FAKE, need, None) == 1       # no experts
+    assert lib.nvfp4_pack_scales(ctypes.byref(_w(64, 48)), 2, FAKE, need, None) == 1  # cols % 32
+    assert lib.nvfp4_pack_scales(ctypes.byref(w), 2, None, need, None) == 1       # null dst
+    assert lib.nvfp4_pack_scales(None, 2, FAKE, need, None) == 1                  # null weights

@@ -275,21 +275,46 @@ def test_grouped_linear(ops, a_dtype, path):
     assert normwise(got, ref) <= TOL_DECODE
 
 
+def test_pack_scales_layout(ops):
+    """nvfp4_pack_scales against the layout written out on the host: 16-row
+    blocks, 128-wide k chunks, 8 scale bytes per row and chunk, zeros past the
+    rows (40 = 2.5 blocks) and past the row's 14 scale bytes (224 columns)."""
+    E, rows, cols = 3, 40, 224
+    w = synth.random_bytes_nvfp4(41, E, rows, cols)
+    got = host(ops.nvfp4_pack_scales(ops.DeviceNVFP4.from_host(w)))
+    kb, nrb, nch = cols // 16, (rows + 15) // 16, (cols + 127) // 128
+    sc = np.asarray(w.scales).reshape(E, rows, kb)
+    ref = np.zeros((E, nrb, nch, 16, 8), dtype=np.uint8)
+    for b in range(nrb):
+        for r in range(16):
+            if 16 * b + r >= rows:
+                continue
+            for c in range(nch):
+                n = min(8, kb - 8 * c)
+                ref[:, b, c, r, :n] = sc[:, 16 * b + r, 8 * c:8 * c + n]
+    assert got.size == ops.nvfp4_packed_scales_bytes(E, rows, cols) == ref.size
+    assert np.array_equal(got.reshape(ref.shape), ref)
+
+
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("n_out", [96, 90])
 @pytest.mark.parametrize("counts", [[120, 128, 40, 200], [33, 202, 190, 215, 4]])
-def test_grouped_linear_prefill_row_mixes(ops, counts, n_out):
+def test_grouped_linear_prefill_row_mixes(ops, counts, n_out, packed):
     """The prefill GEMM over row counts around one and two 128-row m-tiles
     (prefill4314 has about 202 rows per expert), with a k of 160 (a partial
     128-wide chunk) and an expert of a few rows, against the oracle.  An
     output width that is not a multiple of 4 takes the element stores instead
-    of the 16-byte ones."""
+    of the 16-byte ones; with repacked scales (and 96 rows) the GEMM reads
+    those."""
     rng = np.random.default_rng(31)
     k = 160
     w = synth.random_nvfp4(32, len(counts), n_out, k)
     a = synth.f32_to_bf16_bits(rng.standard_normal((sum(counts), k)).astype(np.float32))
     off = _offsets(counts)
-    got = host(ops.nvfp4_grouped_linear(dev(a), dev(off), ops.DeviceNVFP4.from_host(w), max(counts),
-                                        gemv_max_rows=0))
+    dw = ops.DeviceNVFP4.from_host(w)
+    if packed:  # read by the GEMM when the row count is a whole number of 16-row blocks
+        dw.pack()
+    got = host(ops.nvfp4_grouped_linear(dev(a), dev(off), dw, max(counts), gemv_max_rows=0))
     ref = oracle.linear(oracle.bf16_bits_to_f64(a), off, w)
     assert normwise(got, ref) <= TOL_DECODE
 
