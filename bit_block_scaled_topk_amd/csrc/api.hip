@@ -61,6 +61,7 @@ ProjProblem make_problem(const uint16_t *a, long plane, long lda, const int32_t 
   p.codes = w->codes;
   p.scales = w->scales;
   p.scales_packed = w->scales_packed;
+  p.codes_packed = w->codes_packed;
   p.global = w->global;
   p.n_w = w->rows;
   p.k = w->cols;
@@ -114,6 +115,19 @@ moe_status nvfp4_pack_scales(const moe_nvfp4_weights *w, int n_experts, uint8_t 
     return MOE_INVALID_ARG;
   if (dst_bytes < (size_t)packed_scales_bytes(n_experts, w->rows, w->cols)) return MOE_INVALID_ARG;
   return hip_status(launch_pack_scales(w->scales, n_experts, w->rows, w->cols, dst, stream));
+}
+
+size_t nvfp4_packed_codes_bytes(int n_experts, int rows, int cols) {
+  if (n_experts < 1 || rows < 1 || cols < 1) return 0;
+  return (size_t)packed_codes_bytes(n_experts, rows, cols);
+}
+
+moe_status nvfp4_pack_codes(const moe_nvfp4_weights *w, int n_experts, uint8_t *dst, size_t dst_bytes,
+                            hipStream_t stream) {
+  if (!w || !w->codes || !dst || n_experts < 1 || w->rows < 1 || w->cols < 32 || w->cols % 32 != 0)
+    return MOE_INVALID_ARG;
+  if (dst_bytes < (size_t)packed_codes_bytes(n_experts, w->rows, w->cols)) return MOE_INVALID_ARG;
+  return hip_status(launch_pack_codes(w->codes, n_experts, w->rows, w->cols, dst, stream));
 }
 
 moe_status moe_route_topk(const float *logits, int n_tokens, int n_experts, int top_k, int32_t *topk_ids,

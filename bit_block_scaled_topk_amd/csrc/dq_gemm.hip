@@ -117,9 +117,11 @@ __device__ __forceinline__ void find_tile(const int32_t *offsets, int E, int n_r
 // beyond the buffer's extent), so partial tiles need no branches.  One barrier
 // per chunk.
 //
-// SM, how the e4m3 scales are loaded: 0, one 2-byte load per chunk and block
-// from the canonical layout; 2, the same from the repacked layout (a block's
-// 16 rows of one chunk in one 128-byte line instead of 16 lines); 1 (K a
+// SM, how the weights are loaded: 0, one 2-byte scale load per chunk and
+// block from the canonical layout; 2, the same from the repacked scales (a
+// block's 16 rows of one chunk in one 128-byte line instead of 16 lines); 3,
+// as 2 with the codes repacked too (a block's chunk, 16 rows x 64 bytes, is
+// 1 KB contiguous: one load reads 8 whole lines instead of 16 half lines); 1 (K a
 // multiple of 64, scales 4-byte aligned, no repacked copy): loaded
 // for a pair of chunks at a time -- lane (n, q) loads bytes 4q .. 4q + 3 of
 // the pair's 16 bytes of its weight row (chunk q >> 1, k-slices 2 (q & 1) and
@@ -181,11 +183,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // Weight loads: lane (nl, q), four 16-column blocks j of this wavefront.
   const int nl = lane & 15, q = lane >> 4;
   const size_t e_rows = (size_t)e * p.n_w;
-  const __amdgpu_buffer_rsrc_t c_rsrc = make_rsrc(p.codes + e_rows * (size_t)(K >> 1), (uint32_t)p.n_w * (uint32_t)(K >> 1));
+  const uint32_t nch_c = (uint32_t)(K + 127) >> 7, pkc_bytes = (uint32_t)((p.n_w + 15) >> 4) * nch_c * 1024u;
+  const __amdgpu_buffer_rsrc_t c_rsrc =
+      SM == 3 ? make_rsrc(p.codes_packed + (size_t)e * pkc_bytes, pkc_bytes)
+              : make_rsrc(p.codes + e_rows * (size_t)(K >> 1), (uint32_t)p.n_w * (uint32_t)(K >> 1));
   // repacked scales (SM 2): [16-row block][128-wide chunk][16 rows][8 bytes] per expert
   const uint32_t nch = (uint32_t)(K + 127) >> 7, pk_bytes = (uint32_t)((p.n_w + 15) >> 4) * nch * 128u;
   const __amdgpu_buffer_rsrc_t s_rsrc =
-      SM == 2 ? make_rsrc(p.scales_packed + (size_t)e * pk_bytes, pk_bytes)
+      SM >= 2 ? make_rsrc(p.scales_packed + (size_t)e * pk_bytes, pk_bytes)
               : make_rsrc(p.scales + e_rows * (size_t)(K >> 4), (uint32_t)p.n_w * (uint32_t)(K >> 4));
   int wrow0, dj[4];
   if (EPI == EPI_SWIGLU) {  // blocks 0, 1: gate rows; 2, 3: the matching up rows
@@ -200,7 +205,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // a column past n_out reads past the expert's rows (zero), or -- for the
   // gate half of a partial SwiGLU tile -- rows whose results are not stored
   const uint32_t c_off0 = (uint32_t)wrow0 * (uint32_t)(K >> 1) + 16u * q;
-  const uint32_t s_off0 = SM == 2 ? 8u * (uint32_t)nl + 2u * q : (uint32_t)wrow0 * (uint32_t)(K >> 4) + (SP ? 4u : 2u) * q;
+  const uint32_t s_off0 = SM >= 2 ? 8u * (uint32_t)nl + 2u * q : (uint32_t)wrow0 * (uint32_t)(K >> 4) + (SP ? 4u : 2u) * q;
   // A wavefront whose output columns all lie past n_out (the last column tile
   // of a ragged width, e.g. 1856 = 7 x 256 + 64) skips its MFMAs and decode:
   // it still fills its share of the activation tile and meets every barrier,
@@ -233,10 +238,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     const bool s_in = SP ? k0 + 128 * (q >> 1) + 64 * (q & 1) < K : b_in;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t co = b_in ? c_off0 + (uint32_t)(dj[j] * (K >> 1)) + (uint32_t)(k0 >> 1) : OOB;
+      uint32_t co;
+      if constexpr (SM == 3) {  // the block's chunk: 16 rows x 64 bytes
+        const uint32_t blk = (uint32_t)((wrow0 - nl + dj[j]) >> 4) * nch_c + (uint32_t)(k0 >> 7);
+        co = b_in ? (blk * 16u + (uint32_t)nl) * 64u + 16u * q : OOB;
+      } else
+        co = b_in ? c_off0 + (uint32_t)(dj[j] * (K >> 1)) + (uint32_t)(k0 >> 1) : OOB;
       rc[j] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, co, 0, 0);
       uint32_t so;
-      if constexpr (SM == 2)  // this lane's row's 16-row block, chunk k0 / 128
+      if constexpr (SM >= 2)  // this lane's row's 16-row block, chunk k0 / 128
         so = s_in ? s_off0 + ((uint32_t)((wrow0 - nl + dj[j]) >> 4) * nch + (uint32_t)(k0 >> 7)) * 128u : OOB;
       else
         so = s_in ? s_off0 + (uint32_t)(dj[j] * (K >> 4)) + (uint32_t)(k0 >> 4) : OOB;
@@ -462,18 +472,18 @@ hipError_t launch_dq_gemm(ProjProblem *probs, int count, int epi, hipStream_t st
     pk = pk && q.scales_packed != nullptr && q.n_w % 16 == 0 && (epi != EPI_SWIGLU || q.n_out % 16 == 0);
     sp = sp && q.k % 64 == 0 && ((uintptr_t)q.scales & 3) == 0;
   }
-  const int sm = pk ? 2 : sp ? 1 : 0;
+  bool pc = pk;
+  for (int i = 0; i < b.count; ++i) pc = pc && b.p[i].codes_packed != nullptr;
+  const int sm = pc ? 3 : pk ? 2 : sp ? 1 : 0;
   dim3 grid((unsigned)total), block(256);
-  switch (epi * 3 + sm) {
-    case EPI_F32 * 3 + 0: hipLaunchKernelGGL((k_dq_gemm<EPI_F32, 0>), grid, block, 0, stream, b); break;
-    case EPI_F32 * 3 + 1: hipLaunchKernelGGL((k_dq_gemm<EPI_F32, 1>), grid, block, 0, stream, b); break;
-    case EPI_F32 * 3 + 2: hipLaunchKernelGGL((k_dq_gemm<EPI_F32, 2>), grid, block, 0, stream, b); break;
-    case EPI_RELU2 * 3 + 0: hipLaunchKernelGGL((k_dq_gemm<EPI_RELU2, 0>), grid, block, 0, stream, b); break;
-    case EPI_RELU2 * 3 + 1: hipLaunchKernelGGL((k_dq_gemm<EPI_RELU2, 1>), grid, block, 0, stream, b); break;
-    case EPI_RELU2 * 3 + 2: hipLaunchKernelGGL((k_dq_gemm<EPI_RELU2, 2>), grid, block, 0, stream, b); break;
-    case EPI_SWIGLU * 3 + 0: hipLaunchKernelGGL((k_dq_gemm<EPI_SWIGLU, 0>), grid, block, 0, stream, b); break;
-    case EPI_SWIGLU * 3 + 1: hipLaunchKernelGGL((k_dq_gemm<EPI_SWIGLU, 1>), grid, block, 0, stream, b); break;
-    default: hipLaunchKernelGGL((k_dq_gemm<EPI_SWIGLU, 2>), grid, block, 0, stream, b); break;
+  switch (epi * 4 + sm) {
+#define MOE_GEMM_CASE(E, M) \
+  case E * 4 + M: hipLaunchKernelGGL((k_dq_gemm<E, M>), grid, block, 0, stream, b); break;
+    MOE_GEMM_CASE(EPI_F32, 0) MOE_GEMM_CASE(EPI_F32, 1) MOE_GEMM_CASE(EPI_F32, 2) MOE_GEMM_CASE(EPI_F32, 3)
+    MOE_GEMM_CASE(EPI_RELU2, 0) MOE_GEMM_CASE(EPI_RELU2, 1) MOE_GEMM_CASE(EPI_RELU2, 2) MOE_GEMM_CASE(EPI_RELU2, 3)
+    MOE_GEMM_CASE(EPI_SWIGLU, 0) MOE_GEMM_CASE(EPI_SWIGLU, 1) MOE_GEMM_CASE(EPI_SWIGLU, 2) MOE_GEMM_CASE(EPI_SWIGLU, 3)
+#undef MOE_GEMM_CASE
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -516,6 +526,49 @@ hipError_t launch_pack_scales(const uint8_t *scales, int n_experts, int rows, in
   if (units <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_pack_scales, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream, scales, rows,
                      cols / 16, nrb, nch, units, dst);
+  return hipGetLastError();
+}
+
+// One 16-byte piece u = (((e nrb + b) nch + c) 16 + r) 4 + i of the repacked
+// codes per thread: row 16 b + r of expert e, bytes 64 c + 16 i .. + 15 of its
+// kc code bytes (zero past the row count or past kc).
+__global__ void __launch_bounds__(256) k_pack_codes(const uint8_t *__restrict__ s, int rows, int kc, int nrb, int nch,
+                                                    long units, uint8_t *__restrict__ dst) {
+  const long u = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= units) return;
+  const int piece = (int)(u & 3);
+  const int r = (int)((u >> 2) & 15);
+  long t = u >> 6;
+  const int c = (int)(t % nch);
+  t /= nch;
+  const int blk = (int)(t % nrb);
+  const long e = t / nrb;
+  const int row = 16 * blk + r, col = 64 * c + 16 * piece;
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (row < rows && col < kc) {
+    const uint8_t *src = s + (e * rows + row) * (long)kc + col;
+    if (col + 16 <= kc && ((uintptr_t)src & 15) == 0) {
+      v = *(const u32x4_t *)src;
+    } else {
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+      for (int i = 0; i < 16 && col + i < kc; ++i) w[i >> 2] |= (uint32_t)src[i] << (8 * (i & 3));
+      v = u32x4_t{w[0], w[1], w[2], w[3]};
+    }
+  }
+  ((u32x4_t *)dst)[u] = v;
+}
+
+long packed_codes_bytes(long n_experts, int rows, int cols) {
+  return n_experts * (long)((rows + 15) / 16) * (long)((cols + 127) / 128) * 1024L;
+}
+
+hipError_t launch_pack_codes(const uint8_t *codes, int n_experts, int rows, int cols, uint8_t *dst,
+                             hipStream_t stream) {
+  const int nrb = (rows + 15) / 16, nch = (cols + 127) / 128;
+  const long units = (long)n_experts * nrb * nch * 64;
+  if (units <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pack_codes, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream, codes, rows,
+                     cols / 2, nrb, nch, units, dst);
   return hipGetLastError();
 }
 

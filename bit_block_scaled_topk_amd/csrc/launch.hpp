@@ -59,6 +59,7 @@ struct ProjProblem {
   const uint8_t *codes;   // [n_experts][n_w][k/2]
   const uint8_t *scales;  // [n_experts][n_w][k/16]
   const uint8_t *scales_packed;  // optional: the same scales as nvfp4_pack_scales orders them
+  const uint8_t *codes_packed;   // optional: the same codes as nvfp4_pack_codes orders them
   const float *global;    // [n_experts]
   int n_w, k, n_out;
   float *out_f32;         // EPI_F32 output [n_rows][ldo]
@@ -82,6 +83,10 @@ hipError_t launch_dq_gemv(ProjProblem *probs, const int *max_active, int count, 
 long packed_scales_bytes(long n_experts, int rows, int cols);
 hipError_t launch_pack_scales(const uint8_t *scales, int n_experts, int rows, int cols, uint8_t *dst,
                               hipStream_t stream);
+// The one-time code repack: dst[e][b][c][r][i] = codes[e][16 b + r][64 c + i].
+long packed_codes_bytes(long n_experts, int rows, int cols);
+hipError_t launch_pack_codes(const uint8_t *codes, int n_experts, int rows, int cols, uint8_t *dst,
+                             hipStream_t stream);
 hipError_t launch_dq_gemm(ProjProblem *probs, int count, int epi, hipStream_t stream);
 
 // A whole decode step (n_tokens <= 2) in one persistent launch: routing, the

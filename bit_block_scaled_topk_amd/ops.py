@@ -40,7 +40,8 @@ class MoeError(RuntimeError):
 class NVFP4Weights(ctypes.Structure):
     """moe_nvfp4_weights: device pointers of one projection for E experts."""
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("global_", ctypes.c_void_p),
-                ("rows", ctypes.c_int), ("cols", ctypes.c_int), ("scales_packed", ctypes.c_void_p)]
+                ("rows", ctypes.c_int), ("cols", ctypes.c_int), ("scales_packed", ctypes.c_void_p),
+                ("codes_packed", ctypes.c_void_p)]
 
 
 _P = ctypes.c_void_p
@@ -74,6 +75,10 @@ _lib.nvfp4_packed_scales_bytes.argtypes = [_I, _I, _I]
 _lib.nvfp4_packed_scales_bytes.restype = _SZ
 _lib.nvfp4_pack_scales.argtypes = [ctypes.POINTER(NVFP4Weights), _I, _P, _SZ, _P]
 _lib.nvfp4_pack_scales.restype = _I
+_lib.nvfp4_packed_codes_bytes.argtypes = [_I, _I, _I]
+_lib.nvfp4_packed_codes_bytes.restype = _SZ
+_lib.nvfp4_pack_codes.argtypes = [ctypes.POINTER(NVFP4Weights), _I, _P, _SZ, _P]
+_lib.nvfp4_pack_codes.restype = _I
 
 class LayerDesc(ctypes.Structure):
     """moe_layer_desc."""
@@ -105,7 +110,8 @@ _lib.moe_layer_forward_profiled.restype = _I
 EXPORTED = ("moe_route_topk", "moe_gather_workspace_size", "moe_gather_rows",
             "nvfp4_expert_ffn_workspace_size", "nvfp4_grouped_linear_workspace_size",
             "nvfp4_expert_ffn", "moe_weighted_row_sum", "moe_weighted_row_sum_into", "nvfp4_unpack_bf16",
-            "nvfp4_grouped_linear", "nvfp4_packed_scales_bytes", "nvfp4_pack_scales", "moe_status_string",
+            "nvfp4_grouped_linear", "nvfp4_packed_scales_bytes", "nvfp4_pack_scales",
+            "nvfp4_packed_codes_bytes", "nvfp4_pack_codes", "moe_status_string",
             "moe_layer_workspace_size",
             "moe_layer_workspace_init", "moe_layer_get_views",
             "moe_layer_forward", "moe_layer_forward_profiled")
@@ -142,6 +148,7 @@ class DeviceNVFP4:
     rows: int
     cols: int
     scales_packed: Optional[torch.Tensor] = None  # uint8, nvfp4_pack_scales order (optional)
+    codes_packed: Optional[torch.Tensor] = None   # uint8, nvfp4_pack_codes order (optional)
 
     @classmethod
     def from_host(cls, t, device="cuda") -> "DeviceNVFP4":
@@ -151,12 +158,14 @@ class DeviceNVFP4:
     def struct(self) -> NVFP4Weights:
         return NVFP4Weights(self.codes.data_ptr(), self.scales.data_ptr(), self.globals_.data_ptr(),
                             self.rows, self.cols,
-                            None if self.scales_packed is None else self.scales_packed.data_ptr())
+                            None if self.scales_packed is None else self.scales_packed.data_ptr(),
+                            None if self.codes_packed is None else self.codes_packed.data_ptr())
 
     def pack(self, stream=None) -> "DeviceNVFP4":
-        """Repack the scales once (nvfp4_pack_scales); the prefill GEMM then reads
-        them.  Returns self."""
+        """Repack the scales and codes once (nvfp4_pack_scales, nvfp4_pack_codes);
+        the prefill GEMM then reads them.  Returns self."""
         self.scales_packed = nvfp4_pack_scales(self, stream=stream)
+        self.codes_packed = nvfp4_pack_codes(self, stream=stream)
         return self
 
     @property
@@ -260,6 +269,20 @@ def nvfp4_pack_scales(w: DeviceNVFP4, dst: Optional[torch.Tensor] = None, stream
     s = w.struct()
     _check("nvfp4_pack_scales", _lib.nvfp4_pack_scales(ctypes.byref(s), w.n_experts, _ptr(dst), dst.numel(),
                                                        _stream(stream)))
+    return dst
+
+
+def nvfp4_packed_codes_bytes(n_experts: int, rows: int, cols: int) -> int:
+    return int(_lib.nvfp4_packed_codes_bytes(n_experts, rows, cols))
+
+
+def nvfp4_pack_codes(w: DeviceNVFP4, dst: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    nbytes = nvfp4_packed_codes_bytes(w.n_experts, w.rows, w.cols)
+    if dst is None:
+        dst = torch.empty(nbytes, dtype=torch.uint8, device=w.codes.device)
+    s = w.struct()
+    _check("nvfp4_pack_codes", _lib.nvfp4_pack_codes(ctypes.byref(s), w.n_experts, _ptr(dst), dst.numel(),
+                                                     _stream(stream)))
     return dst
 
 
@@ -404,7 +427,7 @@ class MoELayer:
 
     def desc(self, weights=None, n_tokens: Optional[int] = None) -> LayerDesc:
         up, down, sup, sdn = weights if weights is not None else self.weights()
-        empty = NVFP4Weights(None, None, None, 0, 0, None)
+        empty = NVFP4Weights(None, None, None, 0, 0, None, None)
         return LayerDesc(self.n if n_tokens is None else n_tokens, self.d, self.E, self.K, self.x_dtype, self.act,
                          self.gemv_max_rows, up.struct(), down.struct(),
                          sup.struct() if sup is not None else empty, sdn.struct() if sdn is not None else empty)

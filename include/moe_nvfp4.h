@@ -82,6 +82,9 @@ typedef struct {
    * The prefill GEMM reads them when present and rows is a multiple of 16;
    * every other path reads `scales`.  Both must hold the same weights. */
   const uint8_t *scales_packed;
+  /* Optional (NULL: absent): the codes reordered by nvfp4_pack_codes.  Read
+   * by the prefill GEMM together with scales_packed (both must be present). */
+  const uint8_t *codes_packed;
 } moe_nvfp4_weights;
 
 /* nvfp4_packed_scales_bytes -- bytes of the reordered scales of n_experts
@@ -105,6 +108,25 @@ size_t nvfp4_packed_scales_bytes(int n_experts, int rows, int cols);
  * Stream-ordered on `stream`; allocates nothing. */
 moe_status nvfp4_pack_scales(const moe_nvfp4_weights *w, int n_experts, uint8_t *dst, size_t dst_bytes,
                              hipStream_t stream);
+
+/* nvfp4_packed_codes_bytes -- bytes of the reordered codes of n_experts
+ * experts of rows x cols: n_experts * ceil(rows/16) * ceil(cols/128) * 1024
+ * (0 for non-positive sizes). */
+size_t nvfp4_packed_codes_bytes(int n_experts, int rows, int cols);
+
+/* nvfp4_pack_codes -- the optional one-time repack of a projection's e2m1
+ * codes into the order the prefill GEMM reads them in (same bytes, another
+ * order):
+ *   dst[e][b][c][r][i] = codes[e][16 b + r][64 c + i]
+ * for 16-row block b, 128-column chunk c, row r < 16 and i < 64; entries past
+ * rows or past cols/2 are zero.  One 16-row block's codes of one 128-wide k
+ * chunk are then 1 KB contiguous, which one 16-byte-per-lane load reads as 8
+ * whole cache lines (16 half lines in the canonical layout).
+ *   w       the projection (w->scales and w->global are not read)
+ *   dst     device, dst_bytes >= nvfp4_packed_codes_bytes(n_experts, rows, cols)
+ * Errors as nvfp4_pack_scales.  Stream-ordered on `stream`; allocates nothing. */
+moe_status nvfp4_pack_codes(const moe_nvfp4_weights *w, int n_experts, uint8_t *dst, size_t dst_bytes,
+                            hipStream_t stream);
 
 /* moe_route_topk -- per token, the top_k experts by router logit and their
  * weights, a softmax over the top_k picked logits only.

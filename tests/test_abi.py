@@ -50,7 +50,8 @@ def test_binding_names_match_header():
 
 class W(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("global_", ctypes.c_void_p),
-                ("rows", ctypes.c_int), ("cols", ctypes.c_int), ("scales_packed", ctypes.c_void_p)]
+                ("rows", ctypes.c_int), ("cols", ctypes.c_int), ("scales_packed", ctypes.c_void_p),
+                ("codes_packed", ctypes.c_void_p)]
 
 
 FAKE = ctypes.c_void_p(1 << 20)  # an aligned non-null address: never dereferenced on the host
@@ -74,6 +75,9 @@ def _setup(lib):
     lib.nvfp4_packed_scales_bytes.argtypes = [I, I, I]
     lib.nvfp4_packed_scales_bytes.restype = SZ
     lib.nvfp4_pack_scales.argtypes = [ctypes.POINTER(W), I, P, SZ, P]
+    lib.nvfp4_packed_codes_bytes.argtypes = [I, I, I]
+    lib.nvfp4_packed_codes_bytes.restype = SZ
+    lib.nvfp4_pack_codes.argtypes = [ctypes.POINTER(W), I, P, SZ, P]
 
 
 def test_status_strings(lib):
@@ -177,3 +181,17 @@ def test_packed_scales_size_and_pack_argument_errors(lib):
     assert lib.nvfp4_pack_scales(ctypes.byref(_w(64, 48)), 2, FAKE, need, None) == 1  # cols % 32
     assert lib.nvfp4_pack_scales(ctypes.byref(w), 2, None, need, None) == 1       # null dst
     assert lib.nvfp4_pack_scales(None, 2, FAKE, need, None) == 1                  # null weights
+
+
+def test_packed_codes_size_and_pack_argument_errors(lib):
+    """The repacked code layout's size: n_experts * ceil(rows/16) *
+    ceil(cols/128) * 1024 bytes (64 code bytes per row and 128-wide chunk)."""
+    _setup(lib)
+    assert lib.nvfp4_packed_codes_bytes(128, 1856, 2688) == 128 * 116 * 21 * 1024
+    assert lib.nvfp4_packed_codes_bytes(3, 17, 160) == 3 * 2 * 2 * 1024
+    assert lib.nvfp4_packed_codes_bytes(1, 0, 64) == 0
+    w = _w(64, 256)
+    need = lib.nvfp4_packed_codes_bytes(2, 64, 256)
+    assert lib.nvfp4_pack_codes(ctypes.byref(w), 2, FAKE, need - 1, None) == 1   # dst too small
+    assert lib.nvfp4_pack_codes(ctypes.byref(_w(64, 40)), 2, FAKE, need, None) == 1  # cols % 32
+    assert lib.nvfp4_pack_codes(ctypes.byref(w), 2, None, need, None) == 1       # null dst

@@ -296,6 +296,27 @@ def test_pack_scales_layout(ops):
     assert np.array_equal(got.reshape(ref.shape), ref)
 
 
+def test_pack_codes_layout(ops):
+    """nvfp4_pack_codes against the layout written out on the host: 16-row
+    blocks, 128-wide k chunks, 64 code bytes per row and chunk, zeros past the
+    rows (40) and past the row's 112 code bytes (224 columns)."""
+    E, rows, cols = 3, 40, 224
+    w = synth.random_bytes_nvfp4(42, E, rows, cols)
+    got = host(ops.nvfp4_pack_codes(ops.DeviceNVFP4.from_host(w)))
+    kc, nrb, nch = cols // 2, (rows + 15) // 16, (cols + 127) // 128
+    cd = np.asarray(w.codes).reshape(E, rows, kc)
+    ref = np.zeros((E, nrb, nch, 16, 64), dtype=np.uint8)
+    for b in range(nrb):
+        for r in range(16):
+            if 16 * b + r >= rows:
+                continue
+            for c in range(nch):
+                n = min(64, kc - 64 * c)
+                ref[:, b, c, r, :n] = cd[:, 16 * b + r, 64 * c:64 * c + n]
+    assert got.size == ops.nvfp4_packed_codes_bytes(E, rows, cols) == ref.size
+    assert np.array_equal(got.reshape(ref.shape), ref)
+
+
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("n_out", [96, 90])
 @pytest.mark.parametrize("counts", [[120, 128, 40, 200], [33, 202, 190, 215, 4]])
@@ -304,8 +325,8 @@ def test_grouped_linear_prefill_row_mixes(ops, counts, n_out, packed):
     (prefill4314 has about 202 rows per expert), with a k of 160 (a partial
     128-wide chunk) and an expert of a few rows, against the oracle.  An
     output width that is not a multiple of 4 takes the element stores instead
-    of the 16-byte ones; with repacked scales (and 96 rows) the GEMM reads
-    those."""
+    of the 16-byte ones; with repacked scales and codes (and 96 rows) the
+    GEMM reads those."""
     rng = np.random.default_rng(31)
     k = 160
     w = synth.random_nvfp4(32, len(counts), n_out, k)
