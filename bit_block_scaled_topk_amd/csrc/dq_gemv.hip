@@ -104,7 +104,11 @@ __device__ __forceinline__ void find_expert(const int32_t *__restrict__ offsets,
   }
 }
 
-template <int WAVES, int MT, int NT, int EPI, int CT>
+// PK: the weights are read from their repacked copies (nvfp4_pack_codes and
+// nvfp4_pack_scales: [16-row block][128-wide k chunk][16 rows][64 or 8 bytes]),
+// where the 16 rows of a round's k-groups are contiguous (one 1 KB piece of
+// codes and one 128-byte line of scales per tile) instead of 16 row segments.
+template <int WAVES, int MT, int NT, int EPI, int CT, bool PK>
 __global__ void __launch_bounds__(64 * WAVES) k_dq_gemv(GemvBatch batch) {
   constexpr int NB = (EPI == EPI_SWIGLU) ? 2 : 1;
   constexpr int kNI = kNIT / CT > 0 ? kNIT / CT : 1;  // k-group iterations per round
@@ -151,6 +155,14 @@ __global__ void __launch_bounds__(64 * WAVES) k_dq_gemv(GemvBatch batch) {
     const int col = min((tile0 + ct) * 16 + nl, p.n_out - 1);
     return base + ((size_t)e * p.n_w + (size_t)col + (size_t)b * p.n_out) * pitch;
   };
+  // repacked: byte offset of k-group g of weight row `row` (codes: 16 bytes
+  // per k-group, scales: 2), inside this expert's copy
+  const int nch = (p.k + 127) >> 7;
+  const size_t pk_rows = (size_t)((p.n_w + 15) >> 4) * (size_t)nch * 16;  // 16-row slots of one expert
+  auto pk_slot = [&](int ct, int b, int g) -> size_t {
+    const int row = min((tile0 + ct) * 16 + nl, p.n_out - 1) + b * p.n_out;
+    return (size_t)e * pk_rows + ((size_t)(row >> 4) * nch + (g >> 2)) * 16 + (row & 15);
+  };
   const uint16_t *arow[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -178,6 +190,13 @@ __global__ void __launch_bounds__(64 * WAVES) k_dq_gemv(GemvBatch batch) {
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
+          if constexpr (PK) {
+            const size_t slot = pk_slot(ct, b, gc);
+            wq[ct][b][i] = *(const u32x4_t *)(p.codes_packed + slot * 64 + (gc & 3) * 16);
+            const uint32_t s2 = *(const uint16_t *)(p.scales_packed + slot * 8 + (gc & 3) * 2);
+            sc[ct][b][i] = (g < ge) ? s2 : 0u;  // a zero scale neutralises a clamped group
+            continue;
+          }
           wq[ct][b][i] = *(const u32x4_t *)(wrow_of(ct, b, p.codes, crow) + (size_t)gc * 16);
           const uint32_t s2 = *(const uint16_t *)(wrow_of(ct, b, p.scales, srow) + (size_t)gc * 2);
           sc[ct][b][i] = (g < ge) ? s2 : 0u;  // a zero scale neutralises a clamped group
@@ -304,10 +323,21 @@ k_split3(const float *__restrict__ a, long n_elems, uint16_t *__restrict__ plane
 template <int WAVES, int MT, int NT>
 hipError_t dispatch_epi(const GemvBatch &b, int epi, dim3 grid, hipStream_t s) {
   dim3 block(64 * WAVES);
-  switch (epi) {
-    case EPI_F32: hipLaunchKernelGGL((k_dq_gemv<WAVES, MT, NT, EPI_F32, kCT>), grid, block, 0, s, b); break;
-    case EPI_RELU2: hipLaunchKernelGGL((k_dq_gemv<WAVES, MT, NT, EPI_RELU2, kCT>), grid, block, 0, s, b); break;
-    default: hipLaunchKernelGGL((k_dq_gemv<WAVES, MT, NT, EPI_SWIGLU, kCT>), grid, block, 0, s, b); break;
+  bool pk = true;  // every problem carries both repacked copies
+  for (int i = 0; i < b.count; ++i) pk = pk && b.p[i].codes_packed && b.p[i].scales_packed;
+  switch (epi * 2 + (pk ? 1 : 0)) {
+    case EPI_F32 * 2: hipLaunchKernelGGL((k_dq_gemv<WAVES, MT, NT, EPI_F32, kCT, false>), grid, block, 0, s, b); break;
+    case EPI_F32 * 2 + 1: hipLaunchKernelGGL((k_dq_gemv<WAVES, MT, NT, EPI_F32, kCT, true>), grid, block, 0, s, b); break;
+    case EPI_RELU2 * 2:
+      hipLaunchKernelGGL((k_dq_gemv<WAVES, MT, NT, EPI_RELU2, kCT, false>), grid, block, 0, s, b);
+      break;
+    case EPI_RELU2 * 2 + 1:
+      hipLaunchKernelGGL((k_dq_gemv<WAVES, MT, NT, EPI_RELU2, kCT, true>), grid, block, 0, s, b);
+      break;
+    case EPI_SWIGLU * 2:
+      hipLaunchKernelGGL((k_dq_gemv<WAVES, MT, NT, EPI_SWIGLU, kCT, false>), grid, block, 0, s, b);
+      break;
+    default: hipLaunchKernelGGL((k_dq_gemv<WAVES, MT, NT, EPI_SWIGLU, kCT, true>), grid, block, 0, s, b); break;
   }
   return hipGetLastError();
 }
