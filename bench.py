@@ -1,35 +1,36 @@
 """MoE-layer benchmark on one MI355X.
 
 A step is one pass of the whole layer -- topK routing, gather, shared expert,
-routed experts (NVFP4 up -> relu^2 -> down), WeightedRowSum -- over one batch
-of seeded synthetic input (bit_block_scaled_topk_amd.synth), all inputs and
-weights resident in HBM before the timed region starts.
+routed experts (NVFP4 up -> relu^2 / SwiGLU -> down), WeightedRowSum -- over
+one batch of seeded synthetic input (bit_block_scaled_topk_amd.synth), with
+every input and weight resident in HBM before the timed region starts.
 
-The default workload is the batch-1 decode layer (1 token, d_model 2688, 128
-experts, topK 6, relu^2 d_ff 1856, shared d_ff 3712, bf16 activations).  The
-timed loop walks 16 device-resident copies of the layer's weights, one per
-step, as consecutive MoE layers of a model would, so no step finds its
-weights in the 256 MB Infinity Cache.  Steps are replayed from a HIP graph
-(the layer allocates and synchronises nothing, so it captures whole).
+The parsed line is the largest workload, the 4314-token prefill layer (d_model
+2688, 128 experts, topK 6, relu^2 d_ff 1856, shared d_ff 3712, bf16
+activations): every expert takes the bf16 MFMA GEMM.  Exactly --steps eager
+steps are timed between two device synchronisations; `value` is tokens per
+second of wall time over them.
 
-Prints ONE JSON line with the contract fields plus:
-  roofline      the step's dominant kernel against its roofline.  A decode
-                step of one or two tokens is one launch (k_decode_layer):
-                its average duration is the timed region measured with HIP
-                events on the launch stream, divided by the launches in it,
-                and it is held against 8 TB/s with the step's algorithmic
-                bytes (the picked experts' and the shared expert's NVFP4
-                weights once, x, the logits, the output).  A prefill step's
-                dominant kernel is the grouped GEMM (k_dq_gemm: one up and one
-                down launch), timed with HIP events between the library's
-                launch phases, against the dense bf16 matrix-core peak.
-                `traffic` is the HBM bytes per launch that rocprofv3 counted
-                (FETCH_SIZE + WRITE_SIZE, scaled by what the counters read for
-                a plain copy), taken from profiles/ only while the kernel's
-                sources are the ones that were counted (else null).
-                `copy_gbs` is the HBM bandwidth a plain 1 GiB device copy
-                reaches on the same GPU (read + write bytes), for context.
+Fields beyond the contract:
+  roofline      the dominant kernel, k_dq_gemm (one up and one down launch
+                per step), against the dense bf16 matrix-core peak: the step's
+                algorithmic flops (2 per multiply-add over real rows, no tile
+                padding) over the two launches' durations, which the library
+                brackets with HIP events recorded on the launch stream
+                (moe_layer_forward_profiled).  Median over --kernel-steps
+                steps after the timed region; the timed region's own mean is
+                reported beside it.  `traffic` is the HBM bytes per launch
+                rocprofv3 counted (FETCH_SIZE + WRITE_SIZE, scaled by what the
+                counters read for a plain copy), taken from profiles/ only
+                while the kernel's sources are the ones that were counted.
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
+  decode        the three decode workloads (1 token; 32 tokens with a skewed
+                router; 2 tokens with SwiGLU experts), each timed as the median
+                of --decode-replays replays of a HIP graph of 16 steps that
+                walk 16 device copies of the weights (as 16 layers would, so no
+                step finds its weights in the 256 MB Infinity Cache), with its
+                own HBM roofline: the touched NVFP4 weights' bytes over the
+                duration of the step's weight-streaming kernels.
 """
 from __future__ import annotations
 
@@ -45,22 +46,30 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 N_COPIES = 16
+METRIC = "MoE-layer tokens/s; decode HBM GB/s & prefill TFLOPS as % of MI355X peak"
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=3200)
-    p.add_argument("--warmup", type=int, default=320)
-    p.add_argument("--workload", default="decode1")
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="prefill4314")
+    p.add_argument("--kernel-steps", type=int, default=50, help="profiled steps for the kernel medians")
+    p.add_argument("--decode", default="decode1,decode32_zipf,gated2",
+                   help="decode workloads benchmarked beside the main line ('' for none)")
+    p.add_argument("--decode-replays", type=int, default=50)
     p.add_argument("--copies", type=int, default=N_COPIES)
-    p.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
     p.add_argument("--copy-probe-mb", type=int, default=0,
                    help="only run a plain device-to-device copy of this many MiB, 5 times (the "
                         "reference for scaling FETCH_SIZE / WRITE_SIZE), then exit")
     return p.parse_args()
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def copy_bandwidth_gbs(mib: int = 1024, reps: int = 5) -> float:
@@ -99,7 +108,7 @@ PREFILL_KERNEL_SOURCES = ("dq_gemm.hip", "nvfp4_device.hpp", "launch.hpp")
 GEMV_KERNEL_SOURCES = ("dq_gemv.hip", "nvfp4_device.hpp", "launch.hpp")
 
 
-def kernel_source_digest(files=DECODE_KERNEL_SOURCES) -> str:
+def kernel_source_digest(files) -> str:
     import hashlib
     h = hashlib.sha256()
     for f in files:
@@ -151,23 +160,27 @@ def decode_step_bytes(inp, ids) -> dict:
     return dict(weights=w, activations=act, total=w + act, distinct_experts=distinct)
 
 
-def layer_ffn_flops(inp) -> int:
-    """2 flops per multiply-add over real rows (no tile padding), shared + routed."""
+def layer_ffn_flops(inp) -> dict:
+    """2 flops per multiply-add over real rows (no tile padding): the up and the
+    down launch, shared + routed."""
     R = inp.n * inp.K
     up_rows = 2 * inp.f if inp.act == "swiglu" else inp.f
-    fl = 2 * R * inp.d * up_rows + 2 * R * inp.f * inp.d
+    up = 2 * R * inp.d * up_rows
+    down = 2 * R * inp.f * inp.d
     if inp.fs > 0:
-        fl += 2 * inp.n * inp.d * inp.fs * 2
-    return fl
+        up += 2 * inp.n * inp.d * inp.fs
+        down += 2 * inp.n * inp.fs * inp.d
+    return {"up": up, "down": down, "total": up + down}
 
 
 def cpu_baseline(inp, budget_s: float) -> dict:
+    import numpy as np
+
     import oracle
     threads = oracle.default_threads()
-    sample_tokens = list(range(inp.n))
     t0 = time.perf_counter()
-    calls = 0
     if inp.n <= 64:
+        calls = 0
         while True:
             oracle.layer(inp, threads=threads)
             calls += 1
@@ -177,166 +190,218 @@ def cpu_baseline(inp, budget_s: float) -> dict:
         tokens = calls * inp.n
         sample = f"{calls} full oracle layer calls on the {inp.name} inputs ({tokens} tokens)"
     else:
-        import numpy as np
         ids, w = oracle.route_topk(inp.logits, inp.K)
         rng = np.random.default_rng(0)
         tokens = 0
-        sample_tokens = []
         while time.perf_counter() - t0 < budget_s:
             t = int(rng.integers(0, inp.n))
             oracle.layer_sampled(inp, [t], ids, w, threads=threads)
             tokens += 1
-            sample_tokens.append(t)
         dt = time.perf_counter() - t0
-        sample = f"{tokens} sampled tokens of the {inp.name} layer (routing, shared + 6 experts each)"
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle", "sample": sample,
-            "seconds": round(dt, 2)}
+        sample = (f"{tokens} tokens of the {inp.name} layer drawn at random, one oracle call each "
+                  f"(shared expert + {inp.K} picked experts + WeightedRowSum; routing once for the batch)")
+    return {"value": round(tokens / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 2)}
+
+
+def median(v):
+    import numpy as np
+    return float(np.median(np.asarray(v, dtype=np.float64)))
+
+
+# ---------------------------------------------------------------------------
+# the main line: eager steps of one layer (prefill)
+# ---------------------------------------------------------------------------
+
+def bench_main(args, ops, synth):
+    import numpy as np
+    import torch
+
+    dev = "cuda:0"
+    t_gen = time.perf_counter()
+    inp = synth.make_layer(args.workload)
+    gen_s = time.perf_counter() - t_gen
+    layer = ops.MoELayer(inp, device=dev)
+    x = torch.from_numpy(np.ascontiguousarray(inp.x.view(np.int16) if inp.x.dtype == np.uint16 else inp.x)).to(dev)
+    logits = torch.from_numpy(inp.logits).to(dev)
+    stream = torch.cuda.Stream()
+    E8 = ops.PROFILE_EVENTS
+    torch.cuda.synchronize()
+    log(f"{inp.name}: inputs in {gen_s:.1f} s; warmup {args.warmup} steps")
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, args.warmup)):
+            layer.forward_fused(x, logits, stream=stream, check=False)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly args.steps steps, the library recording HIP
+    # events between its launches on the launch stream ----
+    K = args.steps
+    ev = ops.HipEvents(E8 * K)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(K):
+            layer.forward_profiled(x, logits, ev.slice(E8 * i), stream=stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    region = [[ev.elapsed_ms(E8 * i + j, E8 * i + j + 1) * 1e3 for j in range(E8 - 1)] for i in range(K)]
+    ev.close()
+    log(f"{inp.name}: {K} timed steps in {elapsed * 1e3:.1f} ms")
+
+    # ---- kernel medians: a further profiled pass ----
+    KS = max(1, args.kernel_steps)
+    ev = ops.HipEvents(E8 * KS)
+    with torch.cuda.stream(stream):
+        for i in range(KS):
+            layer.forward_profiled(x, logits, ev.slice(E8 * i), stream=stream)
+    torch.cuda.synchronize()
+    prof = [[ev.elapsed_ms(E8 * i + j, E8 * i + j + 1) * 1e3 for j in range(E8 - 1)] for i in range(KS)]
+    ev.close()
+    names = ["route_gather", "split", "decode_up", "gemm_up", "decode_down", "gemm_down", "combine"]
+    phase_med = {nm: median([r[j] for r in prof]) for j, nm in enumerate(names)}
+    step_med = median([sum(r) for r in prof])
+
+    fl = layer_ffn_flops(inp)
+    gemm_us = [r[3] + r[5] for r in prof]
+    g_med = median(gemm_us)
+    tf = fl["total"] / (g_med * 1e-6) / 1e12
+    region_gemm = float(np.mean([r[3] + r[5] for r in region]))
+    roofline = {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic("k_dq_gemm", inp.name, PREFILL_KERNEL_SOURCES),
+                "kernel": "k_dq_gemm (grouped bf16 MFMA GEMM with the NVFP4 unpack fused; one up and one down "
+                          "launch per step, shared + routed experts)",
+                "flops_per_launch": fl["total"] // 2, "flops": fl,
+                "us_per_launch": round(g_med / 2, 3),
+                "us_up_down_median": [round(phase_med["gemm_up"], 2), round(phase_med["gemm_down"], 2)],
+                "timed_region_us_per_launch_mean": round(region_gemm / 2, 3),
+                "kernel_steps": KS, "timing": "HIP events recorded by the library on the launch stream"}
+    ids = layer.views()["ids"].cpu().numpy()
+    counts = np.diff(layer.views()["offsets"].cpu().numpy())
+    return inp, gen_s, elapsed, roofline, {k: round(v, 2) for k, v in phase_med.items()}, step_med, counts, ids
+
+
+# ---------------------------------------------------------------------------
+# decode workloads: HIP-graph replays over 16 weight copies
+# ---------------------------------------------------------------------------
+
+def bench_decode(name, args, ops, synth):
+    import numpy as np
+    import torch
+
+    dev = "cuda:0"
+    inp = synth.make_layer(name)
+    layer = ops.MoELayer(inp, device=dev, single_launch=True)
+    copies = [layer.weights()]
+    for _ in range(args.copies - 1):
+        copies.append(tuple(None if w is None else ops.DeviceNVFP4(w.codes.clone(), w.scales.clone(),
+                                                                   w.globals_.clone(), w.rows, w.cols).pack()
+                            for w in layer.weights()))
+    x = torch.from_numpy(np.ascontiguousarray(inp.x.view(np.int16) if inp.x.dtype == np.uint16 else inp.x)).to(dev)
+    logits = torch.from_numpy(inp.logits).to(dev)
+    L = len(copies)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(2 * L):
+            layer.forward_fused(x, logits, weights=copies[i % L], stream=stream, check=False)
+    torch.cuda.synchronize()
+    layer.check_wait_error()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for c in copies:
+            layer.forward_fused(x, logits, weights=c, stream=stream, check=False)
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    v = layer.views()
+    launches0 = int(v["decode_launch"].cpu()[0])
+    R = max(1, args.decode_replays)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for a, b in evs:
+            a.record(stream)
+            graph.replay()
+            b.record(stream)
+    torch.cuda.synchronize()
+    layer.check_wait_error()
+    rep_us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    single = int(v["decode_launch"].cpu()[0]) - launches0 == R * L
+    step_us = median(rep_us) / L
+    ids = v["ids"].cpu().numpy()
+    b = decode_step_bytes(inp, ids)
+    out = {"tokens": inp.n, "d_model": inp.d, "experts": inp.E, "top_k": inp.K, "d_ff": inp.f,
+           "shared_d_ff": inp.fs, "activation": inp.act, "weight_copies": L, "replays": R,
+           "tokens_per_s": round(inp.n / (step_us * 1e-6), 1), "us_per_step_median": round(step_us, 3)}
+    if single:
+        # one launch per step: the graph replay's event time over its launches
+        ach = b["total"] / (step_us * 1e-6) / 1e9
+        out["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(ach / HBM_PEAK_GBS, 4),
+                           "traffic": measured_traffic("k_decode_layer", name, DECODE_KERNEL_SOURCES),
+                           "kernel": "k_decode_layer (the whole decode step in one persistent launch)",
+                           "bytes_per_launch": b["total"], "us_per_launch": round(step_us, 3), "bytes": b}
+    else:
+        # the weight-streaming launches of k_dq_gemv (one up, one down), timed
+        # with the library's events in an eager pass over the same copies
+        E8 = ops.PROFILE_EVENTS
+        n = 2 * L
+        ev = ops.HipEvents(E8 * n)
+        with torch.cuda.stream(stream):
+            for i in range(n):
+                layer.forward_profiled(x, logits, ev.slice(E8 * i), weights=copies[i % L], stream=stream)
+        torch.cuda.synchronize()
+        up = median([ev.elapsed_ms(E8 * i + 2, E8 * i + 3) * 1e3 for i in range(n)])
+        dn = median([ev.elapsed_ms(E8 * i + 4, E8 * i + 5) * 1e3 for i in range(n)])
+        ev.close()
+        ach = b["weights"] / ((up + dn) * 1e-6) / 1e9
+        out["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(ach / HBM_PEAK_GBS, 4),
+                           "traffic": measured_traffic("k_dq_gemv", name, GEMV_KERNEL_SOURCES),
+                           "kernel": "k_dq_gemv (decode dequant-GEMV: one up and one down launch per step, "
+                                     "shared + routed experts)",
+                           "bytes_per_launch": b["weights"] // 2, "us_per_launch": round((up + dn) / 2, 3),
+                           "us_up_down_median": [round(up, 2), round(dn, 2)], "bytes": b}
+    del copies, layer, graph
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                          "(the sharded design is described, not built)"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1 (the sharded "
+                                   "design is described in DESIGN.md, not built)"}))
         sys.exit(2)
     if args.copy_probe_mb > 0:
         copy_probe(args.copy_probe_mb)
         return
-    import numpy as np
     import torch
 
     from bit_block_scaled_topk_amd import ops, synth
 
-    dev = "cuda:0"
     torch.cuda.set_device(0)
-    t_gen = time.perf_counter()
-    inp = synth.make_layer(args.workload)
-    gen_s = time.perf_counter() - t_gen
-    layer = ops.MoELayer(inp, device=dev)
-    copies = [layer.weights()]
-    for _ in range(args.copies - 1):
-        copies.append(tuple(None if w is None else ops.DeviceNVFP4(w.codes.clone(), w.scales.clone(),
-                                                                   w.globals_.clone(), w.rows, w.cols)
-                            for w in layer.weights()))
-    # the one-time scale repack of each copy (the prefill GEMM reads it), timed
-    # apart from the steps
-    torch.cuda.synchronize()
-    t_pack = time.perf_counter()
-    for c in copies[1:]:
-        for w in c:
-            if w is not None:
-                w.pack()
-    torch.cuda.synchronize()
-    prepack_ms = (time.perf_counter() - t_pack) * 1e3 / max(1, len(copies) - 1)
-    xs = inp.x.view(np.int16) if inp.x.dtype == np.uint16 else inp.x
-    x = torch.from_numpy(np.ascontiguousarray(xs)).to(dev)
-    logits = torch.from_numpy(inp.logits).to(dev)
-    L = len(copies)
-    stream = torch.cuda.Stream()
-    torch.cuda.synchronize()
-
-    def one_pass():
-        for c in copies:
-            layer.forward_fused(x, logits, weights=c)
-
-    # warmup (eager) on the bench stream
-    with torch.cuda.stream(stream):
-        for i in range(max(1, args.warmup)):
-            layer.forward_fused(x, logits, weights=copies[i % L])
-    torch.cuda.synchronize()
-
-    steps = max(L, (args.steps // L) * L)
-    graph = None
-    if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            one_pass()
-        for _ in range(2):
-            graph.replay()
-        torch.cuda.synchronize()
-
-    # ---- timed region: exactly `steps` layer steps ----
-    launches0 = int(layer.views()["decode_launch"].cpu()[0])
-    ev_start, ev_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        ev_start.record()  # on `stream`, the launch stream
-        if graph is not None:
-            for _ in range(steps // L):
-                graph.replay()
-        else:
-            for i in range(steps):
-                layer.forward_fused(x, logits, weights=copies[i % L])
-        ev_end.record()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    region_us = ev_start.elapsed_time(ev_end) * 1e3
-    single_launch = int(layer.views()["decode_launch"].cpu()[0]) - launches0 == steps
-    tokens_per_s = inp.n * steps / elapsed
-
-    # ---- kernel timing: HIP events recorded by the library between its launch
-    # phases (moe_layer_forward_profiled), on the launch stream, same copies ----
-    k_steps = min(steps, 20 * L)
-    ev = ops.HipEvents(6 * k_steps)
-    with torch.cuda.stream(stream):
-        for i in range(k_steps):
-            layer.forward_profiled(x, logits, ev.slice(6 * i), weights=copies[i % L])
-    torch.cuda.synchronize()
-    names = ["route_gather", "split", "up", "down", "combine"]
-    phase = {nm: [ev.elapsed_ms(6 * i + j, 6 * i + j + 1) * 1e3 for i in range(k_steps)]
-             for j, nm in enumerate(names)}
-    ev.close()
-    breakdown = {k: float(np.mean(v)) for k, v in phase.items()}
-    v = layer.views()
-    ids = v["ids"].cpu().numpy()
-    if single_launch:
-        # one launch per step: the timed region's event time over its launches
-        us = region_us / steps
-        b = decode_step_bytes(inp, ids)
-        achieved = b["total"] / (us * 1e-6) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": measured_traffic("k_decode_layer", inp.name, DECODE_KERNEL_SOURCES),
-                    "kernel": "k_decode_layer (the whole decode step in one persistent launch)",
-                    "bytes_per_launch": b["total"], "us_per_launch": round(us, 3), "bytes": b}
-        breakdown = {"decode_layer_eager": breakdown["route_gather"]}
-    elif np.diff(v["offsets"].cpu().numpy()).max() <= layer.gemv_max_rows:
-        # every expert on the decode GEMV: one up and one down launch of k_dq_gemv
-        ffn_us = breakdown["up"] + breakdown["down"]
-        b = decode_step_bytes(inp, ids)
-        achieved = b["weights"] / (ffn_us * 1e-6) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": measured_traffic("k_dq_gemv", inp.name, GEMV_KERNEL_SOURCES),
-                    "kernel": "k_dq_gemv (decode dequant-GEMV: one up and one down launch per step, "
-                              "shared + routed experts)",
-                    "bytes_per_launch": b["weights"] // 2, "us_per_launch": round(ffn_us / 2, 3), "bytes": b}
-    else:
-        flops = layer_ffn_flops(inp)
-        ffn_us = breakdown["up"] + breakdown["down"]
-        tf = flops / (ffn_us * 1e-6) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                    "traffic": measured_traffic("k_dq_gemm", inp.name, PREFILL_KERNEL_SOURCES),
-                    "kernel": "k_dq_gemm (prefill grouped bf16 GEMM: one up and one down launch per step, "
-                              "shared + routed experts)",
-                    "flops_per_launch": flops // 2, "us_per_launch": round(ffn_us / 2, 3)}
-
+    inp, gen_s, elapsed, roofline, phases, step_med, counts, ids = bench_main(args, ops, synth)
     roofline["copy_gbs"] = copy_bandwidth_gbs()
-
+    decode = {}
+    for name in [w for w in args.decode.split(",") if w]:
+        log(f"decode workload {name}")
+        decode[name] = bench_decode(name, args, ops, synth)
     cpu = None
     if not args.no_cpu_baseline:
+        log("cpu baseline")
         cpu = cpu_baseline(inp, args.cpu_seconds)
-
+    K = args.steps
     line = {
-        "metric": "MoE-layer tokens/s; decode HBM GB/s & prefill TFLOPS as % of MI355X peak",
-        "value": round(tokens_per_s, 1),
+        "metric": METRIC,
+        "value": round(inp.n * K / elapsed, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": steps,
+        "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(elapsed / steps * 1e3, 5),
+        "ms_per_step": round(elapsed / K * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -345,13 +410,14 @@ def main():
         "config": {"workload": inp.name, "tokens": inp.n, "d_model": inp.d, "experts": inp.E, "top_k": inp.K,
                    "d_ff": inp.f, "shared_d_ff": inp.fs, "activation": inp.act,
                    "activations_dtype": inp.x_dtype, "weights": "nvfp4 (e2m1, e4m3/16, fp32 global)",
-                   "weight_copies": L, "launch": "hipgraph" if graph is not None else "eager",
-                   "parallelism": "none (1 GPU)"},
+                   "routed_rows": int(counts.sum()), "rows_per_expert": [int(counts.min()), int(counts.max())],
+                   "launch": "eager", "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "step_breakdown_us": {k: round(v, 2) for k, v in breakdown.items()},
+        "step_median_us": round(step_med, 2),
+        "step_breakdown_us_median": phases,
         "input_gen_s": round(gen_s, 1),
-        "prepack_ms_per_weight_set": round(prepack_ms, 3),
+        "decode": decode,
     }
     print(json.dumps(line))
 

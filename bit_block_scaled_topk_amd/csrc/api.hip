@@ -30,10 +30,24 @@ bool gemm_extents_ok(long a_rows, long a_cols, long w_rows, long w_cols) {
   return a_rows * a_cols * 2 < (1L << 31) && w_rows * (w_cols / 2) < (1L << 31);
 }
 
+// The repacked copies: both or neither, 16-byte aligned, and one expert's
+// repacked codes addressable with 32-bit offsets below 2^31 (the GEMM marks
+// skipped loads with offset 2^31).
+bool packed_ok(const moe_nvfp4_weights *w) {
+  if (!w->codes_packed && !w->scales_packed) return true;
+  if (!w->codes_packed || !w->scales_packed) return false;
+  if (!aligned(w->codes_packed, 16) || !aligned(w->scales_packed, 16)) return false;
+  return packed_codes_bytes(1, w->rows, w->cols) < (1L << 31);
+}
+
 bool weights_ok(const moe_nvfp4_weights *w) {
   return w && w->codes && w->scales && w->global && w->rows > 0 && w->cols > 0 && aligned(w->codes, 16) &&
-         aligned(w->scales, 2) && aligned(w->global, 4);
+         aligned(w->scales, 2) && aligned(w->global, 4) && packed_ok(w);
 }
+
+// Every workspace of nvfp4_expert_ffn and moe_gather_rows starts with 256
+// bytes reserved for its error word (the int32 at offset 0).
+constexpr size_t kErrBytes = 256;
 
 // Planes of the fp32-activation split: three bf16 planes of n_rows*k.
 size_t split_bytes(long n_rows, long k) { return align_up((size_t)3 * n_rows * k * sizeof(uint16_t)); }
@@ -143,7 +157,7 @@ moe_status moe_route_topk(const float *logits, int n_tokens, int n_experts, int 
 
 size_t moe_gather_workspace_size(int n_tokens, int n_experts) {
   if (n_tokens < 0 || n_experts < 1 || n_experts > MOE_MAX_EXPERTS) return 0;
-  return align_up(gather_workspace_bytes(n_tokens, n_experts));
+  return kErrBytes + align_up(gather_workspace_bytes(n_tokens, n_experts));
 }
 
 moe_status moe_gather_rows(const void *x, moe_dtype x_dtype, int n_tokens, int d_model, const int32_t *topk_ids,
@@ -161,30 +175,44 @@ moe_status moe_gather_rows(const void *x, moe_dtype x_dtype, int n_tokens, int d
   if (ws_bytes < moe_gather_workspace_size(n_tokens, n_experts)) return MOE_WORKSPACE_TOO_SMALL;
   int elem = (x_dtype == MOE_F32) ? 4 : 2;
   return hip_status(launch_gather(x, elem, n_tokens, d_model, topk_ids, top_k, n_experts, xg, expert_offsets,
-                                  row_token, rows, workspace, stream));
+                                  row_token, rows, (char *)workspace + kErrBytes, (int32_t *)workspace, stream));
 }
 
 static moe_status wrs_common(float *dst, const float *src, int n_src_rows, const int32_t *rows,
                              const float *weights, int n_tokens, int top_k, int d_model, bool accumulate,
-                             hipStream_t stream) {
+                             int32_t *error_word, hipStream_t stream) {
   if (n_src_rows < 0 || n_tokens < 0 || top_k < 1 || d_model < 0) return MOE_INVALID_ARG;
   if ((long)n_tokens * d_model >= (1L << 40)) return MOE_UNSUPPORTED;
   if (n_tokens == 0 || d_model == 0) return MOE_OK;
   if (!dst || !rows || !weights || (n_src_rows > 0 && !src)) return MOE_INVALID_ARG;
   if (src && (const void *)src == (const void *)dst) return MOE_INVALID_ARG;
+  if (error_word && !aligned(error_word, 4)) return MOE_INVALID_ARG;
   return hip_status(launch_weighted_row_sum(dst, src, n_src_rows, rows, weights, n_tokens, top_k, d_model,
-                                            accumulate, stream));
+                                            accumulate, error_word, stream));
 }
 
 moe_status moe_weighted_row_sum(float *dst, const float *src, int n_src_rows, const int32_t *rows,
-                                const float *weights, int n_tokens, int top_k, int d_model, hipStream_t stream) {
-  return wrs_common(dst, src, n_src_rows, rows, weights, n_tokens, top_k, d_model, true, stream);
+                                const float *weights, int n_tokens, int top_k, int d_model, int32_t *error_word,
+                                hipStream_t stream) {
+  return wrs_common(dst, src, n_src_rows, rows, weights, n_tokens, top_k, d_model, true, error_word, stream);
 }
 
 moe_status moe_weighted_row_sum_into(float *dst, const float *src, int n_src_rows, const int32_t *rows,
                                      const float *weights, int n_tokens, int top_k, int d_model,
-                                     hipStream_t stream) {
-  return wrs_common(dst, src, n_src_rows, rows, weights, n_tokens, top_k, d_model, false, stream);
+                                     int32_t *error_word, hipStream_t stream) {
+  return wrs_common(dst, src, n_src_rows, rows, weights, n_tokens, top_k, d_model, false, error_word, stream);
+}
+
+moe_status moe_error_word_clear(int32_t *word, hipStream_t stream) {
+  if (!word || !aligned(word, 4)) return MOE_INVALID_ARG;
+  return hip_status(launch_error_word_clear(word, stream));
+}
+
+moe_status moe_error_word_read(const int32_t *word, int32_t *value, hipStream_t stream) {
+  if (!word || !value || !aligned(word, 4)) return MOE_INVALID_ARG;
+  if (hipMemcpyAsync(value, word, sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return MOE_HIP_ERROR;
+  return hip_status(hipStreamSynchronize(stream));
 }
 
 moe_status nvfp4_unpack_bf16(const uint8_t *codes, const uint8_t *scales, int rows, int cols, uint16_t *out,
@@ -200,9 +228,23 @@ moe_status nvfp4_unpack_bf16(const uint8_t *codes, const uint8_t *scales, int ro
 size_t nvfp4_expert_ffn_workspace_size(int n_rows, int d_model, int d_ff, moe_dtype act_dtype) {
   if (n_rows < 0 || d_model < 0 || d_ff < 0) return 0;
   if (act_dtype != MOE_F32 && act_dtype != MOE_BF16) return 0;
-  size_t s = h_bytes(n_rows, d_ff);
+  size_t s = kErrBytes + h_bytes(n_rows, d_ff);
   if (act_dtype == MOE_F32) s += split_bytes(n_rows, d_model);
-  return s > 0 ? s : kAlign;
+  return s;
+}
+
+size_t moe_workspace_size(int n_tokens, int top_k, int n_experts, int d_model, int d_ff_max, moe_act act) {
+  if (n_tokens < 0 || top_k < 1 || n_experts < 1 || d_model < 0 || d_ff_max < 0) return 0;
+  if (act != MOE_RELU2 && act != MOE_SWIGLU) return 0;
+  if (top_k > n_experts || n_experts > MOE_MAX_EXPERTS || top_k > MOE_MAX_TOPK) return 0;
+  if ((long)n_tokens * top_k >= (1L << 31)) return 0;
+  const int R = n_tokens * top_k;
+  size_t s = moe_gather_workspace_size(n_tokens, n_experts);
+  const size_t routed = nvfp4_expert_ffn_workspace_size(R, d_model, d_ff_max, MOE_F32);
+  const size_t shared = nvfp4_expert_ffn_workspace_size(n_tokens, d_model, d_ff_max, MOE_F32);
+  if (routed > s) s = routed;
+  if (shared > s) s = shared;
+  return s;
 }
 
 size_t nvfp4_grouped_linear_workspace_size(int n_rows, int k, moe_dtype a_dtype) {
@@ -237,7 +279,7 @@ moe_status nvfp4_expert_ffn(const void *xg, moe_dtype act_dtype, int n_rows, int
   const int max_active = n_experts < n_rows ? n_experts : n_rows;
   const int epi = (act == MOE_SWIGLU) ? EPI_SWIGLU : EPI_RELU2;
 
-  char *ws = (char *)workspace;
+  char *ws = (char *)workspace + kErrBytes;
   uint16_t *h = (uint16_t *)ws;
   const long h_plane = (long)n_rows * f;
   ws += h_bytes(n_rows, f);
@@ -341,6 +383,7 @@ bool plan_layer(const moe_layer_desc *dsc, LayerPlan *pl) {
   if (dsc->x_dtype != MOE_F32 && dsc->x_dtype != MOE_BF16) return false;
   if (dsc->act != MOE_RELU2 && dsc->act != MOE_SWIGLU) return false;
   if (dsc->gemv_max_rows < 0 || dsc->gemv_max_rows > MOE_MAX_GEMV_ROWS) return false;
+  if (dsc->flags & ~MOE_LAYER_SINGLE_LAUNCH) return false;
   if (!weights_ok(&dsc->up) || !weights_ok(&dsc->down)) return false;
   p.f = dsc->down.cols;
   if (dsc->up.cols != p.d || dsc->down.rows != p.d) return false;
@@ -453,8 +496,9 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, 
   const int max_active = p.E < p.R ? p.E : p.R;
   const int epi = dsc->act == MOE_SWIGLU ? EPI_SWIGLU : EPI_RELU2;
   // 1-5 in one persistent launch for a decode step (at most two tokens, every
-  //     expert on the decode path)
-  if (p.n <= gmax && decode_layer_takes(p.n, p.K, p.d)) {
+  //     expert on the decode path), when the caller has promised the device
+  //     to this call alone
+  if ((dsc->flags & MOE_LAYER_SINGLE_LAUNCH) && p.n <= gmax && decode_layer_takes(p.n, p.K, p.d)) {
     DecodeLayerProblem lp{};
     lp.up[1] = make_problem(nullptr, 0, p.d, nullptr, p.E, p.R, -1, &dsc->up, p.f, nullptr, nullptr, 0, 0);
     lp.down[1] = make_problem(nullptr, 0, p.f, nullptr, p.E, p.R, -1, &dsc->down, p.d, nullptr, nullptr, 0, 0);
@@ -488,7 +532,7 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, 
     lp.sync = sync;
     const hipError_t e = launch_decode_layer(lp, stream);
     if (e == hipSuccess) {
-      for (int i = 1; i <= 5; ++i)
+      for (int i = 1; i <= 7; ++i)
         if (mark(i) != hipSuccess) return MOE_HIP_ERROR;
       return MOE_OK;
     }
@@ -509,7 +553,7 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, 
   } else {
     if (launch_route_topk(logits, p.n, p.E, p.K, ids, w, stream) != hipSuccess) return MOE_HIP_ERROR;
     if (launch_gather(x, elem, p.n, p.d, ids, p.K, p.E, nullptr, offsets, row_token, rows, ws + p.off_gather,
-                      stream) != hipSuccess)
+                      nullptr, stream) != hipSuccess)
       return MOE_HIP_ERROR;
   }
   if (mark(1) != hipSuccess) return MOE_HIP_ERROR;
@@ -562,6 +606,7 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, 
       int one = 1;
       if (launch_dq_gemv(&s1, &one, 1, nt, EPI_RELU2, stream) != hipSuccess) return MOE_HIP_ERROR;
     }
+    if (mark(3) != hipSuccess) return MOE_HIP_ERROR;
     ProjProblem gem[2];
     int g = 0;
     const bool gjoin = shared_gemm && epi == EPI_RELU2;
@@ -574,7 +619,7 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, 
     }
   }
 
-  if (mark(3) != hipSuccess) return MOE_HIP_ERROR;
+  if (mark(4) != hipSuccess) return MOE_HIP_ERROR;
   // 4. down projections: shared -> out, routed -> yg
   {
     ProjProblem dec[2];
@@ -587,6 +632,7 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, 
     dec[c] = as_decode(rd, dec_rows);
     act[c++] = max_active;
     if (launch_dq_gemv(dec, act, c, 3, EPI_F32, stream) != hipSuccess) return MOE_HIP_ERROR;
+    if (mark(5) != hipSuccess) return MOE_HIP_ERROR;
     ProjProblem gem[2];
     int g = 0;
     if (shared_gemm) gem[g++] = as_prefill(sd, gmax);
@@ -594,11 +640,11 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, 
     if (g > 0 && launch_dq_gemm(gem, g, EPI_F32, stream) != hipSuccess) return MOE_HIP_ERROR;
   }
 
-  if (mark(4) != hipSuccess) return MOE_HIP_ERROR;
+  if (mark(6) != hipSuccess) return MOE_HIP_ERROR;
   // 5. combine: out += sum_j w * yg[rows]  (onto zero without a shared expert)
-  if (launch_weighted_row_sum(out, yg, p.R, rows, w, p.n, p.K, p.d, p.has_shared, stream) != hipSuccess)
+  if (launch_weighted_row_sum(out, yg, p.R, rows, w, p.n, p.K, p.d, p.has_shared, nullptr, stream) != hipSuccess)
     return MOE_HIP_ERROR;
-  if (mark(5) != hipSuccess) return MOE_HIP_ERROR;
+  if (mark(7) != hipSuccess) return MOE_HIP_ERROR;
   return MOE_OK;
 }
 

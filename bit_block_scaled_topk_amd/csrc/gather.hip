@@ -136,7 +136,7 @@ template <bool ROUTE>
 __global__ void __launch_bounds__(kSmallThreads)
 k_gather_small(const float *__restrict__ logits, float *__restrict__ topk_w, int32_t *ids, int n, int K, int E,
                int32_t *__restrict__ offsets, int32_t *__restrict__ row_token, int32_t *__restrict__ rows,
-               const void *x, int row_bytes, void *xg) {
+               const void *x, int row_bytes, void *xg, int32_t *err) {
   __shared__ uint32_t s_bits[kSmallWords];
   __shared__ int32_t s_ids[kSmallPicks];
   __shared__ int32_t s_rt[kSmallPicks];
@@ -178,7 +178,10 @@ k_gather_small(const float *__restrict__ logits, float *__restrict__ topk_w, int
   for (int p = tid; p < picks; p += blockDim.x) {
     const int e = s_ids[p];
     const int t = p / K;
-    if (e >= 0 && e < E) atomicOr(&bits[e * W + (t >> 5)], 1u << (t & 31));
+    if (e >= 0 && e < E)
+      atomicOr(&bits[e * W + (t >> 5)], 1u << (t & 31));
+    else if (err)
+      atomicOr(err, MOE_DEVERR_EXPERT_ID);
   }
   __syncthreads();
 
@@ -258,7 +261,7 @@ k_gather_small(const float *__restrict__ logits, float *__restrict__ topk_w, int
 // bitmap words for every expert and its per-expert pick counts.
 __global__ void __launch_bounds__(256)
 k_gather_bits(const int32_t *__restrict__ ids, int n, int K, int E, int W, uint32_t *__restrict__ bitmap,
-              int32_t *__restrict__ chunk_count, int n_chunks) {
+              int32_t *__restrict__ chunk_count, int n_chunks, int32_t *err) {
   __shared__ uint32_t s_bits[MOE_MAX_EXPERTS * kChunkWords];
   const int c = blockIdx.x, tid = threadIdx.x;
   const int t0 = c * kChunkTokens;
@@ -268,7 +271,10 @@ k_gather_bits(const int32_t *__restrict__ ids, int n, int K, int E, int W, uint3
   for (long p = (long)t0 * K + tid; p < (long)t1 * K; p += blockDim.x) {
     int e = ids[p];
     int t = (int)(p / K) - t0;
-    if (e >= 0 && e < E) atomicOr(&s_bits[e * kChunkWords + (t >> 5)], 1u << (t & 31));
+    if (e >= 0 && e < E)
+      atomicOr(&s_bits[e * kChunkWords + (t >> 5)], 1u << (t & 31));
+    else if (err)
+      atomicOr(err, MOE_DEVERR_EXPERT_ID);
   }
   __syncthreads();
   const int w0 = c * kChunkWords;
@@ -384,12 +390,12 @@ bool gather_is_single_launch(int n_tokens, int top_k, int n_experts, int elem_by
 
 hipError_t launch_gather(const void *x, int elem_bytes, int n_tokens, int d_model, const int32_t *ids, int top_k,
                          int n_experts, void *xg, int32_t *offsets, int32_t *row_token, int32_t *rows,
-                         void *workspace, hipStream_t stream) {
+                         void *workspace, int32_t *err, hipStream_t stream) {
   const int row_bytes = elem_bytes * d_model;
   if (small_path(n_tokens, top_k, n_experts, row_bytes)) {
     hipLaunchKernelGGL(k_gather_small<false>, dim3(1), dim3(kSmallThreads), 0, stream, nullptr, nullptr,
                        const_cast<int32_t *>(ids), n_tokens, top_k, n_experts, offsets, row_token, rows, x,
-                       row_bytes, xg);
+                       row_bytes, xg, err);
     return hipGetLastError();
   }
   const int W = (n_tokens + 31) / 32;
@@ -397,13 +403,13 @@ hipError_t launch_gather(const void *x, int elem_bytes, int n_tokens, int d_mode
   uint32_t *bitmap = (uint32_t *)workspace;
   int32_t *chunk_count = (int32_t *)(bitmap + (size_t)n_experts * W);
   hipLaunchKernelGGL(k_gather_bits, dim3(n_chunks), dim3(256), 0, stream, ids, n_tokens, top_k, n_experts, W, bitmap,
-                     chunk_count, n_chunks);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+                     chunk_count, n_chunks, err);
+  hipError_t he = hipGetLastError();
+  if (he != hipSuccess) return he;
   hipLaunchKernelGGL(k_gather_place, dim3(n_chunks), dim3(256), 0, stream, ids, n_tokens, top_k, n_experts, W,
                      bitmap, chunk_count, n_chunks, offsets, row_token, rows);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  he = hipGetLastError();
+  if (he != hipSuccess) return he;
   long R = (long)n_tokens * top_k;
   long chunks = R * (row_bytes / 16);
   long blocks = (chunks + 255) / 256;
@@ -418,7 +424,7 @@ hipError_t launch_route_gather_small(const float *logits, int n_tokens, int n_ex
                                      float *weights, const void *x, int elem_bytes, int d_model, void *xg,
                                      int32_t *offsets, int32_t *row_token, int32_t *rows, hipStream_t stream) {
   hipLaunchKernelGGL(k_gather_small<true>, dim3(1), dim3(kSmallThreads), 0, stream, logits, weights, ids, n_tokens,
-                     top_k, n_experts, offsets, row_token, rows, x, elem_bytes * d_model, xg);
+                     top_k, n_experts, offsets, row_token, rows, x, elem_bytes * d_model, xg, nullptr);
   return hipGetLastError();
 }
 

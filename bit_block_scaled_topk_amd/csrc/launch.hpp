@@ -22,14 +22,23 @@ bool gather_is_single_launch(int n_tokens, int top_k, int n_experts, int elem_by
 hipError_t launch_route_gather_small(const float *logits, int n_tokens, int n_experts, int top_k, int32_t *ids,
                                      float *weights, const void *x, int elem_bytes, int d_model, void *xg,
                                      int32_t *offsets, int32_t *row_token, int32_t *rows, hipStream_t stream);
+// err (optional): MOE_DEVERR_EXPERT_ID is OR-ed into it for an id outside
+// [0, n_experts); that pick is dropped (row -1, not counted).
 hipError_t launch_gather(const void *x, int elem_bytes, int n_tokens, int d_model,
                          const int32_t *ids, int top_k, int n_experts, void *xg,
                          int32_t *offsets, int32_t *row_token, int32_t *rows, void *workspace,
-                         hipStream_t stream);
+                         int32_t *err, hipStream_t stream);
 
+// error_word (optional): MOE_DEVERR_ROW is OR-ed into it for a row outside
+// [0, n_src_rows); that entry contributes nothing.
 hipError_t launch_weighted_row_sum(float *dst, const float *src, int n_src_rows,
                                    const int32_t *rows, const float *weights, int n_tokens,
-                                   int top_k, int d_model, bool accumulate, hipStream_t stream);
+                                   int top_k, int d_model, bool accumulate, int32_t *error_word,
+                                   hipStream_t stream);
+
+// A device error word: cleared by a one-thread kernel (no memset, so the call
+// may sit in a captured graph).
+hipError_t launch_error_word_clear(int32_t *word, hipStream_t stream);
 
 hipError_t launch_unpack_bf16(const uint8_t *codes, const uint8_t *scales, long rows, int cols,
                               uint16_t *out, hipStream_t stream);

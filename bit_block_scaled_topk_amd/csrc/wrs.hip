@@ -3,7 +3,8 @@
 // in a fixed j order: one thread per output element (four adjacent elements
 // per thread when the row width allows 16-byte access), no atomics.  The j-sum
 // runs in fused multiply-adds from a zero accumulator and is added to dst once.
-// A row index outside [0, n_src) is skipped, so nothing is read out of bounds.
+// A row index outside [0, n_src) is skipped, so nothing is read out of bounds,
+// and MOE_DEVERR_ROW is OR-ed into the caller's error word (when one is given).
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
@@ -14,7 +15,7 @@ namespace {
 template <bool ACCUM>
 __global__ void __launch_bounds__(256)
 k_wrs_vec4(float *__restrict__ dst, const float *__restrict__ src, int n_src,
-           const int32_t *__restrict__ rows, const float *__restrict__ w, int n, int K, int d4) {
+           const int32_t *__restrict__ rows, const float *__restrict__ w, int n, int K, int d4, int32_t *err) {
   long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long)n * d4) return;
   int i = (int)(idx / d4);
@@ -23,7 +24,10 @@ k_wrs_vec4(float *__restrict__ dst, const float *__restrict__ src, int n_src,
   for (int j = 0; j < K; ++j) {
     int r = rows[(size_t)i * K + j];
     float wt = w[(size_t)i * K + j];
-    if (r < 0 || r >= n_src) continue;
+    if (r < 0 || r >= n_src) {
+      if (err && c4 == 0) atomicOr(err, MOE_DEVERR_ROW);
+      continue;
+    }
     f32x4_t s = ((const f32x4_t *)src)[(size_t)r * d4 + c4];
     acc.x = fmaf(wt, s.x, acc.x);
     acc.y = fmaf(wt, s.y, acc.y);
@@ -45,7 +49,7 @@ k_wrs_vec4(float *__restrict__ dst, const float *__restrict__ src, int n_src,
 template <bool ACCUM>
 __global__ void __launch_bounds__(256)
 k_wrs_scalar(float *__restrict__ dst, const float *__restrict__ src, int n_src,
-             const int32_t *__restrict__ rows, const float *__restrict__ w, int n, int K, int d) {
+             const int32_t *__restrict__ rows, const float *__restrict__ w, int n, int K, int d, int32_t *err) {
   long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long)n * d) return;
   int i = (int)(idx / d);
@@ -53,7 +57,10 @@ k_wrs_scalar(float *__restrict__ dst, const float *__restrict__ src, int n_src,
   float acc = 0.f;
   for (int j = 0; j < K; ++j) {
     int r = rows[(size_t)i * K + j];
-    if (r < 0 || r >= n_src) continue;
+    if (r < 0 || r >= n_src) {
+      if (err && c == 0) atomicOr(err, MOE_DEVERR_ROW);
+      continue;
+    }
     acc = fmaf(w[(size_t)i * K + j], src[(size_t)r * d + c], acc);
   }
   if (ACCUM)
@@ -66,23 +73,32 @@ k_wrs_scalar(float *__restrict__ dst, const float *__restrict__ src, int n_src,
 
 hipError_t launch_weighted_row_sum(float *dst, const float *src, int n_src_rows, const int32_t *rows,
                                    const float *weights, int n_tokens, int top_k, int d_model, bool accumulate,
-                                   hipStream_t stream) {
+                                   int32_t *error_word, hipStream_t stream) {
   bool vec = (d_model % 4 == 0) && ((uintptr_t)dst % 16 == 0) && ((uintptr_t)src % 16 == 0);
   long elems = (long)n_tokens * (vec ? d_model / 4 : d_model);
   long blocks = (elems + 255) / 256;
   dim3 grid((unsigned)blocks), block(256);
   if (vec && accumulate)
     hipLaunchKernelGGL(k_wrs_vec4<true>, grid, block, 0, stream, dst, src, n_src_rows, rows, weights, n_tokens,
-                       top_k, d_model / 4);
+                       top_k, d_model / 4, error_word);
   else if (vec)
     hipLaunchKernelGGL(k_wrs_vec4<false>, grid, block, 0, stream, dst, src, n_src_rows, rows, weights, n_tokens,
-                       top_k, d_model / 4);
+                       top_k, d_model / 4, error_word);
   else if (accumulate)
     hipLaunchKernelGGL(k_wrs_scalar<true>, grid, block, 0, stream, dst, src, n_src_rows, rows, weights,
-                       n_tokens, top_k, d_model);
+                       n_tokens, top_k, d_model, error_word);
   else
     hipLaunchKernelGGL(k_wrs_scalar<false>, grid, block, 0, stream, dst, src, n_src_rows, rows, weights,
-                       n_tokens, top_k, d_model);
+                       n_tokens, top_k, d_model, error_word);
+  return hipGetLastError();
+}
+
+namespace {
+__global__ void k_error_word_clear(int32_t *word) { *word = 0; }
+}  // namespace
+
+hipError_t launch_error_word_clear(int32_t *word, hipStream_t stream) {
+  hipLaunchKernelGGL(k_error_word_clear, dim3(1), dim3(1), 0, stream, word);
   return hipGetLastError();
 }
 

@@ -15,12 +15,12 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# MOE_NVFP4_LIB may name another build of the same library (e.g. a tuning variant)
-LIB_PATH = os.environ.get("MOE_NVFP4_LIB", os.path.join(_HERE, "libmoe_nvfp4.so"))
+LIB_PATH = os.path.join(_HERE, "libmoe_nvfp4.so")
 
 MOE_OK, MOE_INVALID_ARG, MOE_UNSUPPORTED, MOE_HIP_ERROR, MOE_WORKSPACE_TOO_SMALL = 0, 1, 2, 3, 4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_RELU2, MOE_SWIGLU = 0, 1
+MOE_DEVERR_EXPERT_ID, MOE_DEVERR_ROW = 1, 2
 MAX_GEMV_ROWS = 32
 
 if not os.path.exists(LIB_PATH):
@@ -62,10 +62,16 @@ _lib.nvfp4_grouped_linear_workspace_size.restype = _SZ
 _lib.nvfp4_expert_ffn.argtypes = [_P, _I, _I, _I, _P, _I, ctypes.POINTER(NVFP4Weights),
                                   ctypes.POINTER(NVFP4Weights), _I, _I, _P, _SZ, _P, _P]
 _lib.nvfp4_expert_ffn.restype = _I
-_lib.moe_weighted_row_sum.argtypes = [_P, _P, _I, _P, _P, _I, _I, _I, _P]
+_lib.moe_weighted_row_sum.argtypes = [_P, _P, _I, _P, _P, _I, _I, _I, _P, _P]
 _lib.moe_weighted_row_sum.restype = _I
-_lib.moe_weighted_row_sum_into.argtypes = [_P, _P, _I, _P, _P, _I, _I, _I, _P]
+_lib.moe_weighted_row_sum_into.argtypes = [_P, _P, _I, _P, _P, _I, _I, _I, _P, _P]
 _lib.moe_weighted_row_sum_into.restype = _I
+_lib.moe_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I]
+_lib.moe_workspace_size.restype = _SZ
+_lib.moe_error_word_clear.argtypes = [_P, _P]
+_lib.moe_error_word_clear.restype = _I
+_lib.moe_error_word_read.argtypes = [_P, ctypes.POINTER(ctypes.c_int32), _P]
+_lib.moe_error_word_read.restype = _I
 _lib.nvfp4_unpack_bf16.argtypes = [_P, _P, _I, _I, _P, _P]
 _lib.nvfp4_unpack_bf16.restype = _I
 _lib.nvfp4_grouped_linear.argtypes = [_P, _I, _I, _I, _P, _I, ctypes.POINTER(NVFP4Weights), _I, _P, _SZ,
@@ -85,7 +91,11 @@ class LayerDesc(ctypes.Structure):
     _fields_ = [("n_tokens", ctypes.c_int), ("d_model", ctypes.c_int), ("n_experts", ctypes.c_int),
                 ("top_k", ctypes.c_int), ("x_dtype", ctypes.c_int), ("act", ctypes.c_int),
                 ("gemv_max_rows", ctypes.c_int), ("up", NVFP4Weights), ("down", NVFP4Weights),
-                ("shared_up", NVFP4Weights), ("shared_down", NVFP4Weights)]
+                ("shared_up", NVFP4Weights), ("shared_down", NVFP4Weights), ("flags", ctypes.c_int)]
+
+
+MOE_LAYER_SINGLE_LAUNCH = 1
+PROFILE_EVENTS = 8  # events moe_layer_forward_profiled records per call
 
 
 class LayerViews(ctypes.Structure):
@@ -109,7 +119,8 @@ _lib.moe_layer_forward_profiled.restype = _I
 
 EXPORTED = ("moe_route_topk", "moe_gather_workspace_size", "moe_gather_rows",
             "nvfp4_expert_ffn_workspace_size", "nvfp4_grouped_linear_workspace_size",
-            "nvfp4_expert_ffn", "moe_weighted_row_sum", "moe_weighted_row_sum_into", "nvfp4_unpack_bf16",
+            "nvfp4_expert_ffn", "moe_weighted_row_sum", "moe_weighted_row_sum_into", "moe_workspace_size",
+            "moe_error_word_clear", "moe_error_word_read", "nvfp4_unpack_bf16",
             "nvfp4_grouped_linear", "nvfp4_packed_scales_bytes", "nvfp4_pack_scales",
             "nvfp4_packed_codes_bytes", "nvfp4_pack_codes", "moe_status_string",
             "moe_layer_workspace_size",
@@ -234,19 +245,38 @@ def nvfp4_expert_ffn(xg: torch.Tensor, offsets: torch.Tensor, up: DeviceNVFP4, d
 
 
 def moe_weighted_row_sum(dst: torch.Tensor, src: torch.Tensor, rows: torch.Tensor, weights: torch.Tensor,
-                         stream=None) -> torch.Tensor:
+                         error_word: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     n, K = rows.shape
     _check("moe_weighted_row_sum", _lib.moe_weighted_row_sum(
-        _ptr(dst), _ptr(src), src.shape[0], _ptr(rows), _ptr(weights), n, K, dst.shape[1], _stream(stream)))
+        _ptr(dst), _ptr(src), src.shape[0], _ptr(rows), _ptr(weights), n, K, dst.shape[1], _ptr(error_word),
+        _stream(stream)))
     return dst
 
 
 def moe_weighted_row_sum_into(dst: torch.Tensor, src: torch.Tensor, rows: torch.Tensor, weights: torch.Tensor,
-                              stream=None) -> torch.Tensor:
+                              error_word: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     n, K = rows.shape
     _check("moe_weighted_row_sum_into", _lib.moe_weighted_row_sum_into(
-        _ptr(dst), _ptr(src), src.shape[0], _ptr(rows), _ptr(weights), n, K, dst.shape[1], _stream(stream)))
+        _ptr(dst), _ptr(src), src.shape[0], _ptr(rows), _ptr(weights), n, K, dst.shape[1], _ptr(error_word),
+        _stream(stream)))
     return dst
+
+
+def moe_workspace_size(n_tokens: int, top_k: int, n_experts: int, d_model: int, d_ff_max: int, act: int) -> int:
+    return int(_lib.moe_workspace_size(n_tokens, top_k, n_experts, d_model, d_ff_max, act))
+
+
+def moe_error_word_clear(word: torch.Tensor, stream=None) -> None:
+    """``word``: an int32 device tensor whose first element is the error word
+    (e.g. a workspace viewed as int32)."""
+    _check("moe_error_word_clear", _lib.moe_error_word_clear(_ptr(word), _stream(stream)))
+
+
+def moe_error_word_read(word: torch.Tensor, stream=None) -> int:
+    """Test and debugging helper: waits for the stream, returns the word."""
+    v = ctypes.c_int32(0)
+    _check("moe_error_word_read", _lib.moe_error_word_read(_ptr(word), ctypes.byref(v), _stream(stream)))
+    return int(v.value)
 
 
 def nvfp4_unpack_bf16(codes: torch.Tensor, scales: torch.Tensor, rows: int, cols: int,
@@ -328,7 +358,7 @@ def moe_layer_forward(desc: LayerDesc, x: torch.Tensor, logits: torch.Tensor, ou
 
 def moe_layer_forward_profiled(desc: LayerDesc, x: torch.Tensor, logits: torch.Tensor, out: torch.Tensor,
                                workspace: torch.Tensor, events, stream=None) -> torch.Tensor:
-    """``events``: a ctypes array of 6 hipEvent_t handles (see HipEvents)."""
+    """``events``: PROFILE_EVENTS hipEvent_t handles (see HipEvents.slice)."""
     _check("moe_layer_forward_profiled", _lib.moe_layer_forward_profiled(
         ctypes.byref(desc), _ptr(x), _ptr(logits), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), events, _stream(stream)))
@@ -383,21 +413,25 @@ class MoELayer:
     experts -> WeightedRowSum on the current stream and returns the [n, d]
     float32 output (gllm PR #91, "What changes").  Buffers are allocated once
     at construction for n_tokens tokens, so a forward pass allocates nothing.
+    ``single_launch`` sets MOE_LAYER_SINGLE_LAUNCH in the layer description:
+    only for callers that run nothing else on the device during a step.
     """
 
-    def __init__(self, inp, device="cuda", gemv_max_rows: int = MAX_GEMV_ROWS, n_tokens: Optional[int] = None):
+    def __init__(self, inp, device="cuda", gemv_max_rows: int = MAX_GEMV_ROWS, n_tokens: Optional[int] = None,
+                 single_launch: bool = False):
         self.n = int(n_tokens if n_tokens is not None else inp.n)
         self.d, self.E, self.K, self.f, self.fs = inp.d, inp.E, inp.K, inp.f, inp.fs
         self.act = MOE_SWIGLU if inp.act == "swiglu" else MOE_RELU2
         self.x_dtype = MOE_F32 if inp.x_dtype == "f32" else MOE_BF16
         self.gemv_max_rows = gemv_max_rows
+        self.flags = MOE_LAYER_SINGLE_LAUNCH if single_launch else 0
         self.up = DeviceNVFP4.from_host(inp.up, device)
         self.down = DeviceNVFP4.from_host(inp.down, device)
         self.shared_up = DeviceNVFP4.from_host(inp.shared_up, device) if inp.fs > 0 else None
         self.shared_down = DeviceNVFP4.from_host(inp.shared_down, device) if inp.fs > 0 else None
         for w in self.weights():
             if w is not None:
-                w.pack()  # the one-time scale repack the prefill GEMM reads
+                w.pack()  # the one-time repack the prefill GEMM and the decode GEMV read
         self.device = device
         self.layer_ws = None
         self._alloc(self.n)
@@ -419,6 +453,7 @@ class MoELayer:
                  nvfp4_expert_ffn_workspace_size(R, d, self.f, self.x_dtype),
                  nvfp4_expert_ffn_workspace_size(n, d, max(self.fs, 32), self.x_dtype))
         self.workspace = torch.empty((ws,), dtype=torch.uint8, device=dev)
+        moe_error_word_clear(self.workspace.view(torch.int32))  # the gather's error word
         self.layer_ws = torch.empty((moe_layer_workspace_size(self.desc(None, n)),), dtype=torch.uint8, device=dev)
         moe_layer_workspace_init(self.desc(None, n), self.layer_ws)
 
@@ -430,16 +465,38 @@ class MoELayer:
         empty = NVFP4Weights(None, None, None, 0, 0, None, None)
         return LayerDesc(self.n if n_tokens is None else n_tokens, self.d, self.E, self.K, self.x_dtype, self.act,
                          self.gemv_max_rows, up.struct(), down.struct(),
-                         sup.struct() if sup is not None else empty, sdn.struct() if sdn is not None else empty)
+                         sup.struct() if sup is not None else empty, sdn.struct() if sdn is not None else empty,
+                         self.flags)
 
-    def forward_fused(self, x: torch.Tensor, logits: torch.Tensor, stream=None, weights=None) -> torch.Tensor:
+    def forward_fused(self, x: torch.Tensor, logits: torch.Tensor, stream=None, weights=None,
+                      check: bool = True) -> torch.Tensor:
         """The whole layer through moe_layer_forward (the fewest launches);
-        intermediates stay in the layer workspace (see views())."""
+        intermediates stay in the layer workspace (see views()).  With
+        ``check`` (and outside graph capture) the call waits for the stream and
+        raises if a bounded wait of the single-launch step expired, i.e. the
+        output is invalid; pass check=False in timed or captured loops and call
+        check_wait_error() afterwards."""
         d = self.desc(weights, x.shape[0])
         need = moe_layer_workspace_size(d)
         if self.layer_ws is None or self.layer_ws.numel() < need:
             raise MoeError("moe_layer_forward", MOE_WORKSPACE_TOO_SMALL)
-        return moe_layer_forward(d, x, logits, self.out, self.layer_ws, stream=stream)
+        out = moe_layer_forward(d, x, logits, self.out, self.layer_ws, stream=stream)
+        if check and self.flags and not torch.cuda.is_current_stream_capturing():
+            self.check_wait_error(stream)
+        return out
+
+    def check_wait_error(self, stream=None) -> None:
+        """Raise if the single-launch step's wait_error word is set (waits for
+        the stream)."""
+        v = moe_layer_get_views(self.desc(None, self.n), self.layer_ws)
+        word = self.layer_ws[v.wait_error - self.layer_ws.data_ptr():][:4].view(torch.int32)
+        if moe_error_word_read(word, stream) != 0:
+            raise RuntimeError("moe_layer_forward: a bounded wait of the single-launch decode step expired; "
+                               "the output of that call is invalid (was another kernel running on the device?)")
+
+    def gather_error(self, stream=None) -> int:
+        """The gather workspace's error word (MOE_DEVERR_* bits; waits for the stream)."""
+        return moe_error_word_read(self.workspace.view(torch.int32), stream)
 
     def forward_profiled(self, x: torch.Tensor, logits: torch.Tensor, events, stream=None,
                          weights=None) -> torch.Tensor:

@@ -27,6 +27,13 @@
  *   - Entry points are stateless and may be called from several host threads.
  *   - Results are deterministic: the same inputs give the same output bits,
  *     whatever else runs on the GPU (no floating-point atomics anywhere).
+ *   - Index errors found on the device are reported, never trapped on: a
+ *     kernel that meets an index outside its range skips that entry and ORs a
+ *     MOE_DEVERR_* bit into a device error word (the first int32 of the
+ *     workspace of moe_gather_rows and nvfp4_expert_ffn, whose first 256 bytes
+ *     are reserved for it; an argument of moe_weighted_row_sum).  The word is
+ *     sticky: kernels only set bits; moe_error_word_clear resets it and
+ *     moe_error_word_read (a test and debugging helper) copies it to the host.
  *
  * NVFP4 tensor layout (one projection of n_experts experts):
  *   codes   uint8 [n_experts][rows][cols/2]: e2m1 codes (OCP MX E2M1: sign bit 3,
@@ -57,6 +64,10 @@ typedef int moe_status;
 #define MOE_HIP_ERROR 3            /* a kernel launch failed (hipGetLastError) */
 #define MOE_WORKSPACE_TOO_SMALL 4  /* ws_bytes below the size query's answer */
 
+/* Bits of a device error word. */
+#define MOE_DEVERR_EXPERT_ID 1  /* moe_gather_rows: a topk_id outside [0, n_experts) */
+#define MOE_DEVERR_ROW 2        /* moe_weighted_row_sum: a rows entry outside [0, n_src_rows) */
+
 typedef int moe_dtype;
 #define MOE_F32 0   /* IEEE binary32 */
 #define MOE_BF16 1  /* bfloat16, stored as uint16 bit patterns */
@@ -78,12 +89,14 @@ typedef struct {
   const float *global;
   int rows; /* out_features */
   int cols; /* in_features, a multiple of 32 */
-  /* Optional (NULL: absent): the same scales reordered by nvfp4_pack_scales.
-   * The prefill GEMM reads them when present and rows is a multiple of 16;
-   * every other path reads `scales`.  Both must hold the same weights. */
+  /* Optional: the same scales and codes reordered by nvfp4_pack_scales and
+   * nvfp4_pack_codes -- both present or both NULL, 16-byte aligned, holding
+   * the same weights as `codes` / `scales`.  When both are present the decode
+   * GEMV reads them, and so does the prefill GEMM when rows is a multiple of
+   * 16 (SwiGLU: f too); the single-launch decode step and the standalone
+   * unpack read the canonical layout.  With them, one expert's repacked codes
+   * (ceil(rows/16) * ceil(cols/128) KB) must stay under 2 GiB. */
   const uint8_t *scales_packed;
-  /* Optional (NULL: absent): the codes reordered by nvfp4_pack_codes.  Read
-   * by the prefill GEMM together with scales_packed (both must be present). */
   const uint8_t *codes_packed;
 } moe_nvfp4_weights;
 
@@ -144,7 +157,8 @@ moe_status moe_route_topk(const float *logits, int n_tokens, int n_experts, int 
                           int32_t *topk_ids, float *topk_weights, hipStream_t stream);
 
 /* Workspace bytes moe_gather_rows needs for n_tokens tokens and n_experts
- * experts (0 for invalid arguments). */
+ * experts, the 256 reserved bytes of the error word included (0 for invalid
+ * arguments). */
 size_t moe_gather_workspace_size(int n_tokens, int n_experts);
 
 /* moe_gather_rows -- the MoE gather (gllm #91 "What changes": each (token,
@@ -160,11 +174,15 @@ size_t moe_gather_workspace_size(int n_tokens, int n_experts);
  *                   [expert_offsets[e], expert_offsets[e+1])
  *   row_token       device int32 [n_tokens*top_k] (out): token of each row
  *   rows            device int32 [n_tokens][top_k] (out): row of pick (t, j)
- *   workspace       device scratch of ws_bytes >= moe_gather_workspace_size()
+ *   workspace       device scratch of ws_bytes >= moe_gather_workspace_size();
+ *                   its first int32 is the error word (clear it once with
+ *                   moe_error_word_clear before reading it)
  * Rows inside an expert's group are in ascending token order, so the layout is
- * unique.  A pick whose id is outside [0, n_experts) is dropped: its rows[t][j]
- * is -1, it is not counted, and the unused tail rows (from
- * expert_offsets[n_experts] on) get row_token -1 and are not written in xg.
+ * unique.  A pick whose id is outside [0, n_experts) is dropped -- its
+ * rows[t][j] is -1, it is not counted, and the unused tail rows (from
+ * expert_offsets[n_experts] on) get row_token -1 and are not written in xg --
+ * and MOE_DEVERR_EXPERT_ID is set in the workspace's error word (the
+ * oracle of the tests rejects such ids: gllm #91 "Testing" checks bounds).
  * Limits: n_tokens*top_k < 2^31, d_model a multiple of 16, x and xg 16-byte
  * aligned. */
 moe_status moe_gather_rows(const void *x, moe_dtype x_dtype, int n_tokens, int d_model,
@@ -174,9 +192,9 @@ moe_status moe_gather_rows(const void *x, moe_dtype x_dtype, int n_tokens, int d
 
 /* Workspace bytes nvfp4_expert_ffn needs for n_rows packed rows of d_model
  * activations of act_dtype and an intermediate h of width d_ff (up->rows is
- * d_ff, or 2*d_ff for SwiGLU); 0 for invalid arguments.  It holds h as three
- * bf16 planes (hi + mid + lo) and, for fp32 activations, the activations split
- * the same way. */
+ * d_ff, or 2*d_ff for SwiGLU); 0 for invalid arguments.  After the 256 bytes
+ * reserved for the error word it holds h as three bf16 planes (hi + mid + lo)
+ * and, for fp32 activations, the activations split the same way. */
 size_t nvfp4_expert_ffn_workspace_size(int n_rows, int d_model, int d_ff, moe_dtype act_dtype);
 
 /* Workspace bytes nvfp4_grouped_linear needs (fp32 activations only; 0 for bf16). */
@@ -225,10 +243,13 @@ moe_status nvfp4_expert_ffn(const void *xg, moe_dtype act_dtype, int n_rows,
  *   src      device float [n_src_rows][d_model]
  *   rows     device int32 [n_tokens][top_k]; an entry outside [0, n_src_rows)
  *            contributes nothing (it is skipped, never read out of bounds)
- *   weights  device float [n_tokens][top_k] */
+ *            and sets MOE_DEVERR_ROW in *error_word
+ *   weights  device float [n_tokens][top_k]
+ *   error_word  device int32, or NULL (not reported); the call has no
+ *            workspace, so the caller passes the word (sticky, see above) */
 moe_status moe_weighted_row_sum(float *dst, const float *src, int n_src_rows,
                                 const int32_t *rows, const float *weights, int n_tokens,
-                                int top_k, int d_model, hipStream_t stream);
+                                int top_k, int d_model, int32_t *error_word, hipStream_t stream);
 
 /* moe_weighted_row_sum_into -- the same sum written onto a zero destination,
  *   dst[i][c] = sum_{j=0..top_k-1} weights[i][j] * src[rows[i][j]][c]
@@ -236,7 +257,28 @@ moe_status moe_weighted_row_sum(float *dst, const float *src, int n_src_rows,
  * without a shared expert. */
 moe_status moe_weighted_row_sum_into(float *dst, const float *src, int n_src_rows,
                                      const int32_t *rows, const float *weights, int n_tokens,
-                                     int top_k, int d_model, hipStream_t stream);
+                                     int top_k, int d_model, int32_t *error_word, hipStream_t stream);
+
+/* moe_workspace_size -- one workspace that serves every call of a layer made
+ * with the four calls in order: moe_gather_rows for n_tokens tokens and
+ * n_experts experts, nvfp4_expert_ffn over the n_tokens*top_k routed rows and
+ * over the n_tokens rows of a shared expert, with any d_ff up to d_ff_max and
+ * either activation dtype (the largest of their sizes).  act is accepted for
+ * SwiGLU's sake: h has d_ff columns for both activations, so the size does
+ * not depend on it.  The calls run one after another on one stream, so they
+ * may share the bytes; the first int32 (the error word) is left to the
+ * gather.  0 for invalid arguments. */
+size_t moe_workspace_size(int n_tokens, int top_k, int n_experts, int d_model, int d_ff_max, moe_act act);
+
+/* moe_error_word_clear -- set a device error word to 0 (a one-thread kernel on
+ * `stream`, no memset, so it may be captured in a graph). */
+moe_status moe_error_word_clear(int32_t *word, hipStream_t stream);
+
+/* moe_error_word_read -- test and debugging helper: waits for `stream`, then
+ * copies the device error word to *value (host).  It is the one entry point
+ * that synchronises and reads device memory on the host; the product path
+ * never calls it. */
+moe_status moe_error_word_read(const int32_t *word, int32_t *value, hipStream_t stream);
 
 /* nvfp4_unpack_bf16 -- exact unpack of NVFP4 codes and scales to bf16 without
  * the per-tensor global (gllm #91 "bf16 NVFP4 GEMM (CUDA)": an e2m1 code times
@@ -280,7 +322,17 @@ typedef struct {
   int gemv_max_rows;          /* 0..32, as in nvfp4_expert_ffn */
   moe_nvfp4_weights up, down; /* routed: [E][f or 2f][d], [E][d][f] */
   moe_nvfp4_weights shared_up, shared_down; /* [1][fs][d], [1][d][fs] */
+  int flags;                  /* 0, or MOE_LAYER_SINGLE_LAUNCH */
 } moe_layer_desc;
+
+/* Allows the single-launch decode step (see moe_layer_forward).  Its
+ * workgroups wait on one another, so they must all be resident at once: the
+ * caller promises that no other kernel -- on any stream, this library's
+ * included -- runs on the device while the call's kernel does (e.g. one
+ * decode loop on one stream).  Without the flag every step is made of
+ * kernels that never wait on each other, which is safe under any
+ * concurrency. */
+#define MOE_LAYER_SINGLE_LAUNCH 1
 /* A description is invalid (MOE_INVALID_ARG; workspace size 0) when, with
  * n_tokens > gemv_max_rows, an activation matrix of the prefill GEMM (x as
  * n x d; h as n*K x f; the shared h as n x fs, all bf16) or one expert's codes
@@ -327,13 +379,14 @@ moe_status moe_layer_get_views(const moe_layer_desc *desc, void *workspace, moe_
  * workgroup for small batches, the shared and the routed experts share each
  * up and each down launch, and nothing synchronises or allocates (Glq v0.2.13
  * "Remaining gap to bf16-native": fewer launches per layer).  For a decode
- * step -- n_tokens <= min(2, gemv_max_rows), d_model <= 16384 and the weights
- * fit the LDS of the CUs -- the whole layer (routing, gather layout, up and
- * down projections, combine) is ONE persistent launch whose workgroups hand
- * results to each other through flags and counters in the workspace (waits
- * are bounded; see moe_layer_views.wait_error); its dot products run in fp32
- * on the vector ALUs, so it agrees with the four calls to fp32 rounding rather
- * than bit for bit.  The workspace must have been prepared by
+ * step -- desc->flags has MOE_LAYER_SINGLE_LAUNCH, n_tokens <= min(2,
+ * gemv_max_rows), d_model <= 16384 and the weights fit the LDS of the CUs --
+ * the whole layer (routing, gather layout, up and down projections, combine)
+ * is ONE persistent launch whose workgroups hand results to each other
+ * through flags and counters in the workspace (waits are bounded; see
+ * moe_layer_views.wait_error); its dot products run in fp32 on the vector
+ * ALUs, so it agrees with the four calls to fp32 rounding rather than bit for
+ * bit.  The workspace must have been prepared by
  * moe_layer_workspace_init.  Calls that overlap on one workspace race.
  *   x       device [n][d] of desc->x_dtype (16-byte aligned)
  *   logits  device float [n][E]
@@ -343,12 +396,14 @@ moe_status moe_layer_get_views(const moe_layer_desc *desc, void *workspace, moe_
 moe_status moe_layer_forward(const moe_layer_desc *desc, const void *x, const float *logits, float *out,
                              void *workspace, size_t ws_bytes, hipStream_t stream);
 
-/* moe_layer_forward with timing: events[0..5] (created by the caller, timing
+/* moe_layer_forward with timing: events[0..7] (created by the caller, timing
  * enabled) are recorded on `stream` before routing, after routing + gather,
- * after the activation split, after the up projections, after the down
- * projections and after the combine, so each phase's GPU time can be read
- * with hipEventElapsedTime.  With the single-launch decode step, events 1..5
- * are all recorded after that launch.  events == NULL records nothing. */
+ * after the activation split, after the decode-path up launch, after the
+ * prefill up launch (the grouped GEMM; nothing runs between events 3 and 4
+ * when no expert can take it), after the decode-path down launch, after the
+ * prefill down launch, and after the combine, so each launch's GPU time can be
+ * read with hipEventElapsedTime.  With the single-launch decode step, events
+ * 1..7 are all recorded after that launch.  events == NULL records nothing. */
 moe_status moe_layer_forward_profiled(const moe_layer_desc *desc, const void *x, const float *logits,
                                       float *out, void *workspace, size_t ws_bytes, hipEvent_t *events,
                                       hipStream_t stream);

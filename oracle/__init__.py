@@ -2,8 +2,11 @@
 
 Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  It wraps ``moe_oracle.c`` (plain C,
-IEEE double, fixed summation orders; see that file for the passages each
-function follows) and composes the layer from its pieces in plain Python.
+fixed summation orders; see that file for the passages each function follows)
+and composes the layer from its pieces in plain Python.  Two arithmetics are
+offered: IEEE double (the exact values, up to rounding far below binary32's;
+the default) and binary32 with fused multiply-adds in one fixed order (the
+``*_f32`` functions, ``layer(..., arith="f32")``).
 
 It shares no code with the HIP library: bf16 decoding of activations, the
 NVFP4 decode and every sum are its own.
@@ -61,6 +64,11 @@ def lib():
         L.orc_expert_ffn.restype = I
         L.orc_linear.argtypes = [P, I, I, P, I, P, P, P, I, I, P]; L.orc_linear.restype = I
         L.orc_weighted_row_sum.argtypes = [P, P, I, P, P, I, I, I]; L.orc_weighted_row_sum.restype = I
+        L.orc_expert_ffn_f32.argtypes = [P, I, I, P, I, P, P, P, P, P, P, I, I, I, I, P]
+        L.orc_expert_ffn_f32.restype = I
+        L.orc_linear_f32.argtypes = [P, I, I, P, I, P, P, P, I, I, P]; L.orc_linear_f32.restype = I
+        L.orc_weighted_row_sum_f32.argtypes = [P, P, I, P, P, I, I, I]
+        L.orc_weighted_row_sum_f32.restype = I
         _lib = L
     return _lib
 
@@ -79,7 +87,8 @@ def _check(rc: int, what: str):
 
 
 def default_threads() -> int:
-    return max(1, min(64, os.cpu_count() or 1))
+    # at most 16: the share of host cores one GPU's job gets on a shared machine
+    return max(1, min(16, os.cpu_count() or 1))
 
 
 # ----------------------------------------------------------------------------
@@ -206,16 +215,76 @@ def weighted_row_sum(dst: np.ndarray, src: np.ndarray, rows: np.ndarray, w: np.n
     return out
 
 
+def activations_f32(x: np.ndarray, x_dtype: str) -> np.ndarray:
+    """Activations as binary32 (a bf16 value is exact in binary32)."""
+    if x_dtype == "bf16":
+        b = np.ascontiguousarray(x, dtype=np.uint16).astype(np.uint32) << 16
+        return b.view(np.float32)
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def expert_ffn_f32(x32: np.ndarray, offsets: np.ndarray, up, down, f: int, act: str,
+                   threads: Optional[int] = None) -> np.ndarray:
+    """expert_ffn in binary32: each dot product a chain of fmaf in k order, the
+    global applied after it, relu^2 / SwiGLU in binary32.  Returns float32."""
+    x32 = np.ascontiguousarray(x32, dtype=np.float32)
+    n_rows, d = x32.shape
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    E = offsets.shape[0] - 1
+    d_out = down.rows
+    out = np.zeros((n_rows, d_out), dtype=np.float32)
+    a = ACT_SWIGLU if act == "swiglu" else ACT_RELU2
+    uc, us, ug = (np.ascontiguousarray(up.codes), np.ascontiguousarray(up.scales),
+                  np.ascontiguousarray(up.globals_, dtype=np.float32))
+    dc, ds, dg = (np.ascontiguousarray(down.codes), np.ascontiguousarray(down.scales),
+                  np.ascontiguousarray(down.globals_, dtype=np.float32))
+    _check(lib().orc_expert_ffn_f32(_p(x32), n_rows, d, _p(offsets), E, _p(uc), _p(us), _p(ug),
+                                    _p(dc), _p(ds), _p(dg), f, d_out, a, threads or default_threads(),
+                                    _p(out)), "expert_ffn_f32")
+    return out
+
+
+def linear_f32(a32: np.ndarray, offsets: np.ndarray, w, threads: Optional[int] = None) -> np.ndarray:
+    """linear in binary32 (fmaf chain in k order, then times the global)."""
+    a32 = np.ascontiguousarray(a32, dtype=np.float32)
+    n_rows, k = a32.shape
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    E = offsets.shape[0] - 1
+    out = np.zeros((n_rows, w.rows), dtype=np.float32)
+    c, s, g = (np.ascontiguousarray(w.codes), np.ascontiguousarray(w.scales),
+               np.ascontiguousarray(w.globals_, dtype=np.float32))
+    _check(lib().orc_linear_f32(_p(a32), n_rows, k, _p(offsets), E, _p(c), _p(s), _p(g), w.rows,
+                                threads or default_threads(), _p(out)), "linear_f32")
+    return out
+
+
+def weighted_row_sum_f32(dst: np.ndarray, src: np.ndarray, rows: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """WeightedRowSum in binary32: per element a chain of fmaf over j from a zero
+    accumulator, then one add onto dst.  Returns a new float32 array."""
+    out = np.array(dst, dtype=np.float32, order="C", copy=True)
+    src = np.ascontiguousarray(src, dtype=np.float32)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, K = rows.shape
+    d = out.shape[1] if out.ndim == 2 else 0
+    _check(lib().orc_weighted_row_sum_f32(_p(out), _p(src), src.shape[0], _p(rows), _p(w), n, K, d),
+           "weighted_row_sum_f32")
+    return out
+
+
 # ----------------------------------------------------------------------------
 # the layer
 # ----------------------------------------------------------------------------
 
-def layer(inp, bf16_act: bool = False, threads: Optional[int] = None, routing=None) -> dict:
+def layer(inp, bf16_act: bool = False, threads: Optional[int] = None, routing=None,
+          arith: str = "f64") -> dict:
     """The whole layer: route -> gather -> experts -> shared expert -> combine.
 
     ``routing`` (ids, weights) may be supplied to run the experts and combine on
-    a given routing; by default the oracle routes itself.  Returns every
-    intermediate in a dict."""
+    a given routing; by default the oracle routes itself.  ``arith`` is "f64"
+    (exact values) or "f32" (binary32, fixed-order fmaf chains; the routing
+    weights are then rounded to binary32 before the combine, and ``bf16_act``
+    is not available).  Returns every intermediate in a dict."""
     if routing is None:
         ids, w = route_topk(inp.logits, inp.K)
     else:
@@ -224,6 +293,22 @@ def layer(inp, bf16_act: bool = False, threads: Optional[int] = None, routing=No
         w = np.ascontiguousarray(w, dtype=np.float64)
     offsets, row_token, rows = gather_layout(ids, inp.E)
     xg = gather_copy(inp.x, row_token)
+    if arith == "f32":
+        if bf16_act:
+            raise ValueError("the bf16-activation mode is a double-precision mode")
+        w32 = w.astype(np.float32)
+        yg = expert_ffn_f32(activations_f32(xg, inp.x_dtype), offsets, inp.up, inp.down, inp.f, inp.act,
+                            threads)
+        if inp.fs > 0:
+            shared = expert_ffn_f32(activations_f32(inp.x, inp.x_dtype), np.array([0, inp.n], dtype=np.int32),
+                                    inp.shared_up, inp.shared_down, inp.fs, "relu2", threads)
+        else:
+            shared = np.zeros((inp.n, inp.d), dtype=np.float32)
+        out = weighted_row_sum_f32(shared, yg, rows, w32)
+        return dict(ids=ids, weights=w, offsets=offsets, row_token=row_token, rows=rows, xg=xg,
+                    yg=yg, shared=shared, out=out)
+    if arith != "f64":
+        raise ValueError(f"unknown arithmetic {arith!r}")
     x64 = activations_f64(inp.x, inp.x_dtype)
     xg64 = activations_f64(xg, inp.x_dtype)
     yg = expert_ffn(xg64, offsets, inp.up, inp.down, inp.f, inp.act, bf16_act, threads)
@@ -239,33 +324,35 @@ def layer(inp, bf16_act: bool = False, threads: Optional[int] = None, routing=No
 
 def layer_sampled(inp, tokens, ids: np.ndarray, w: np.ndarray, bf16_act_of_expert=None,
                   threads: Optional[int] = None) -> np.ndarray:
-    """Layer output for a few tokens only, on a given routing (ids, w).
+    """Layer output (double) for a few tokens only, on a given routing (ids, w).
 
-    Each sampled token's picked experts run over that token's activation row;
-    ``bf16_act_of_expert(e)`` (optional) says which experts are evaluated in the
-    bf16-activation mode.  Returns [len(tokens), d] float64."""
-    tokens = list(tokens)
-    x64 = activations_f64(inp.x, inp.x_dtype)
-    out = np.zeros((len(tokens), inp.d), dtype=np.float64)
-    for i, t in enumerate(tokens):
-        if inp.fs > 0:
-            s = expert_ffn(x64[t:t + 1], np.array([0, 1], dtype=np.int32), inp.shared_up,
-                           inp.shared_down, inp.fs, "relu2",
-                           bool(bf16_act_of_expert and bf16_act_of_expert(-1)), threads)[0]
-        else:
-            s = np.zeros((inp.d,), dtype=np.float64)
-        ys = []
-        for j in range(inp.K):
-            e = int(ids[t, j])
-            sub_up = _one_expert(inp.up, e)
-            sub_dn = _one_expert(inp.down, e)
-            mode = bool(bf16_act_of_expert and bf16_act_of_expert(e))
-            ys.append(expert_ffn(x64[t:t + 1], np.array([0, 1], dtype=np.int32), sub_up, sub_dn,
-                                 inp.f, inp.act, mode, threads)[0])
-        src = np.stack(ys)
-        out[i] = weighted_row_sum(s[None, :], src, np.arange(inp.K, dtype=np.int32)[None, :],
-                                  np.asarray(w[t:t + 1], dtype=np.float64))[0]
-    return out
+    The same steps as ``layer`` restricted to the sampled tokens: the shared
+    expert over their rows, each picked expert over the rows of the sampled
+    tokens that picked it (expert by expert, so each expert's weights are
+    decoded once), then WeightedRowSum in slot order onto the shared output.
+    Every output row is computed alone, so the values equal ``layer``'s rows.
+    ``bf16_act_of_expert(e)`` (optional) says which experts run in the
+    bf16-activation mode; e = -1 is the shared expert.  Returns
+    [len(tokens), d] float64."""
+    tokens = [int(t) for t in tokens]
+    m = len(tokens)
+    x64 = activations_f64(inp.x, inp.x_dtype)[tokens]
+    if inp.fs > 0:
+        shared = expert_ffn(x64, np.array([0, m], dtype=np.int32), inp.shared_up, inp.shared_down, inp.fs,
+                            "relu2", bool(bf16_act_of_expert and bf16_act_of_expert(-1)), threads)
+    else:
+        shared = np.zeros((m, inp.d), dtype=np.float64)
+    sub_ids = np.ascontiguousarray(np.asarray(ids)[tokens], dtype=np.int32)
+    src = np.zeros((m * inp.K, inp.d), dtype=np.float64)  # row i*K + j: token i's pick j
+    for e in sorted(set(sub_ids.ravel().tolist())):
+        picks = [(i, j) for i in range(m) for j in range(inp.K) if sub_ids[i, j] == e]
+        mode = bool(bf16_act_of_expert and bf16_act_of_expert(e))
+        y = expert_ffn(x64[[i for i, _ in picks]], np.array([0, len(picks)], dtype=np.int32),
+                       _one_expert(inp.up, e), _one_expert(inp.down, e), inp.f, inp.act, mode, threads)
+        for (i, j), row in zip(picks, y):
+            src[i * inp.K + j] = row
+    rows = np.arange(m * inp.K, dtype=np.int32).reshape(m, inp.K)
+    return weighted_row_sum(shared, src, rows, np.asarray(w, dtype=np.float64)[tokens])
 
 
 class _Slice:

@@ -17,6 +17,9 @@
  * Arithmetic: every floating-point value is carried in IEEE double and every sum
  * runs in one fixed, documented order, so the result does not depend on the
  * number of threads.  Each output element is produced by exactly one thread.
+ * The functions ending in _f32 (at the end of the file) evaluate the same steps
+ * in binary32 with fused multiply-adds in one fixed order instead; the double
+ * ones are the exact values those round towards.
  *
  * Readings of points the pages leave open (each is stated where it is used):
  *   - e2m1 value set: OCP Microscaling spec, E2M1 (sign, 2 exponent bits with
@@ -399,6 +402,166 @@ int orc_weighted_row_sum(double *dst, const double *src, int n_src, const int32_
       for (int j = 0; j < K; ++j)
         acc += w[(size_t)i * K + j] * src[(size_t)rows[(size_t)i * K + j] * d + c];
       dst[(size_t)i * d + c] += acc;
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* The same steps in binary32, each sum in one fixed order                     */
+/* ------------------------------------------------------------------------- */
+
+/* The workload describes its CPU reference as fp32 accumulation in a fixed
+ * order.  These functions are that evaluation, written out step by step:
+ *   q = e4m3(scale) * e2m1(code)      exact in binary32 (at most 6 significant
+ *                                     bits, [gllm#91] "bf16 NVFP4 GEMM (CUDA)")
+ *   F(a, b): acc = 0; for k ascending: acc = fmaf(a_k, b_k, acc)
+ *   projection  out = global * F(a_row, q_row)   (the global applied once,
+ *                                     after the dot product, as alpha)
+ *   relu^2      h = max(u, 0); h = h * h
+ *   swiglu      h = (a / (1 + expf(-a))) * b
+ *   WeightedRowSum  acc = 0; for j ascending: acc = fmaf(w_ij, src_rj, acc);
+ *                   dst = dst + acc          ([gllm#91] "What changes")
+ * The file is built with -ffp-contract=off, so every other multiply and add
+ * rounds on its own; fmaf is the C library's correctly rounded one. */
+
+static float orc_q32(const uint8_t *codes, const uint8_t *scales, int cols, int r, int k) {
+  uint8_t byte = codes[(size_t)r * (cols / 2) + k / 2];
+  unsigned code = (k % 2 == 0) ? (byte & 15u) : (byte >> 4);
+  return (float)(orc_e4m3(scales[(size_t)r * (cols / 16) + k / 16]) * orc_e2m1(code));
+}
+
+static float orc_dot32(const float *a, const float *b, int k) {
+  float acc = 0.0f;
+  for (int i = 0; i < k; ++i) acc = fmaf(a[i], b[i], acc);
+  return acc;
+}
+
+typedef struct {
+  const uint8_t *codes, *scales;
+  int rows, cols;
+  float *out;
+} orc_deq32_ctx;
+
+static void orc_deq32_rows(void *p, long i0, long i1) {
+  orc_deq32_ctx *c = (orc_deq32_ctx *)p;
+  for (long r = i0; r < i1; ++r)
+    for (int k = 0; k < c->cols; ++k) c->out[(size_t)r * c->cols + k] = orc_q32(c->codes, c->scales, c->cols, (int)r, k);
+}
+
+typedef struct {
+  const float *x; const int32_t *row_list; const float *qu, *qd;
+  float gu, gd; int d, f, d_out, act; float *out;
+} orc_ffn32_ctx;
+
+static void orc_ffn32_rows(void *p, long i0, long i1) {
+  orc_ffn32_ctx *c = (orc_ffn32_ctx *)p;
+  int up_rows = (c->act == ORC_ACT_SWIGLU) ? 2 * c->f : c->f;
+  float *u = (float *)malloc(sizeof(float) * (size_t)up_rows);
+  float *h = (float *)malloc(sizeof(float) * (size_t)c->f);
+  if (!u || !h) { free(u); free(h); return; }
+  for (long i = i0; i < i1; ++i) {
+    int r = c->row_list[i];
+    const float *xr = c->x + (size_t)r * c->d;
+    for (int nn = 0; nn < up_rows; ++nn) u[nn] = c->gu * orc_dot32(xr, c->qu + (size_t)nn * c->d, c->d);
+    for (int nn = 0; nn < c->f; ++nn) {
+      if (c->act == ORC_ACT_SWIGLU) {
+        float a = u[nn], b = u[c->f + nn];
+        float s = a / (1.0f + expf(-a));
+        h[nn] = s * b;
+      } else {
+        float a = u[nn] > 0.0f ? u[nn] : 0.0f;
+        h[nn] = a * a;
+      }
+    }
+    for (int m = 0; m < c->d_out; ++m)
+      c->out[(size_t)r * c->d_out + m] = c->gd * orc_dot32(h, c->qd + (size_t)m * c->f, c->f);
+  }
+  free(u); free(h);
+}
+
+/* orc_expert_ffn in binary32 (arguments as there, x and out in float). */
+int orc_expert_ffn_f32(const float *x, int n_rows, int d, const int32_t *offsets, int E,
+                       const uint8_t *up_codes, const uint8_t *up_scales, const float *up_global,
+                       const uint8_t *dn_codes, const uint8_t *dn_scales, const float *dn_global,
+                       int f, int d_out, int act, int threads, float *out) {
+  if (n_rows < 0 || d < 16 || f < 16 || d_out < 1 || E < 1 || (d % 16) || (f % 16)) return ORC_EINVAL;
+  if (act != ORC_ACT_RELU2 && act != ORC_ACT_SWIGLU) return ORC_EINVAL;
+  if (offsets[0] != 0 || offsets[E] != n_rows) return ORC_EINVAL;
+  for (int e = 0; e < E; ++e)
+    if (offsets[e + 1] < offsets[e]) return ORC_EINVAL;
+  int up_rows = (act == ORC_ACT_SWIGLU) ? 2 * f : f;
+  float *qu = (float *)malloc(sizeof(float) * (size_t)up_rows * d);
+  float *qd = (float *)malloc(sizeof(float) * (size_t)d_out * f);
+  int32_t *row_list = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n_rows > 0 ? n_rows : 1));
+  if (!qu || !qd || !row_list) { free(qu); free(qd); free(row_list); return ORC_ENOMEM; }
+  for (int r = 0; r < n_rows; ++r) row_list[r] = r;
+  for (int e = 0; e < E; ++e) {
+    int r0 = offsets[e], r1 = offsets[e + 1];
+    if (r1 == r0) continue;
+    orc_deq32_ctx du = {up_codes + (size_t)e * up_rows * (d / 2), up_scales + (size_t)e * up_rows * (d / 16),
+                        up_rows, d, qu};
+    orc_parallel_for(up_rows, threads, orc_deq32_rows, &du);
+    orc_deq32_ctx dd = {dn_codes + (size_t)e * d_out * (f / 2), dn_scales + (size_t)e * d_out * (f / 16),
+                        d_out, f, qd};
+    orc_parallel_for(d_out, threads, orc_deq32_rows, &dd);
+    orc_ffn32_ctx c = {x, row_list + r0, qu, qd, up_global[e], dn_global[e], d, f, d_out, act, out};
+    orc_parallel_for(r1 - r0, threads, orc_ffn32_rows, &c);
+  }
+  free(qu); free(qd); free(row_list);
+  return ORC_OK;
+}
+
+typedef struct {
+  const float *a; const float *q; float g; int k, nout; const int32_t *row_list; float *out;
+} orc_lin32_ctx;
+
+static void orc_lin32_rows(void *p, long i0, long i1) {
+  orc_lin32_ctx *c = (orc_lin32_ctx *)p;
+  for (long i = i0; i < i1; ++i) {
+    int r = c->row_list[i];
+    for (int nn = 0; nn < c->nout; ++nn)
+      c->out[(size_t)r * c->nout + nn] = c->g * orc_dot32(c->a + (size_t)r * c->k, c->q + (size_t)nn * c->k, c->k);
+  }
+}
+
+/* orc_linear in binary32. */
+int orc_linear_f32(const float *a, int n_rows, int k, const int32_t *offsets, int E,
+                   const uint8_t *codes, const uint8_t *scales, const float *global, int nout,
+                   int threads, float *out) {
+  if (n_rows < 0 || k < 16 || (k % 16) || nout < 1 || E < 1) return ORC_EINVAL;
+  if (offsets[0] != 0 || offsets[E] != n_rows) return ORC_EINVAL;
+  float *q = (float *)malloc(sizeof(float) * (size_t)nout * k);
+  int32_t *row_list = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n_rows > 0 ? n_rows : 1));
+  if (!q || !row_list) { free(q); free(row_list); return ORC_ENOMEM; }
+  for (int r = 0; r < n_rows; ++r) row_list[r] = r;
+  for (int e = 0; e < E; ++e) {
+    int r0 = offsets[e], r1 = offsets[e + 1];
+    if (r1 < r0) { free(q); free(row_list); return ORC_EINVAL; }
+    if (r1 == r0) continue;
+    orc_deq32_ctx dq = {codes + (size_t)e * nout * (k / 2), scales + (size_t)e * nout * (k / 16), nout, k, q};
+    orc_parallel_for(nout, threads, orc_deq32_rows, &dq);
+    orc_lin32_ctx c = {a, q, global[e], k, nout, row_list + r0, out};
+    orc_parallel_for(r1 - r0, threads, orc_lin32_rows, &c);
+  }
+  free(q); free(row_list);
+  return ORC_OK;
+}
+
+/* WeightedRowSum in binary32: for each output element the j-sum is a chain of
+ * fmaf from a zero accumulator, j = 0..K-1, then one add onto dst.  A row
+ * index outside [0, n_src) is an error and nothing is written. */
+int orc_weighted_row_sum_f32(float *dst, const float *src, int n_src, const int32_t *rows,
+                             const float *w, int n, int K, int d) {
+  if (n < 0 || K < 1 || d < 0 || n_src < 0) return ORC_EINVAL;
+  for (long i = 0; i < (long)n * K; ++i)
+    if (rows[i] < 0 || rows[i] >= n_src) return ORC_ERANGE;
+  for (int i = 0; i < n; ++i) {
+    for (int c = 0; c < d; ++c) {
+      float acc = 0.0f;
+      for (int j = 0; j < K; ++j)
+        acc = fmaf(w[(size_t)i * K + j], src[(size_t)rows[(size_t)i * K + j] * d + c], acc);
+      dst[(size_t)i * d + c] = dst[(size_t)i * d + c] + acc;
     }
   }
   return ORC_OK;

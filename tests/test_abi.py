@@ -57,6 +57,13 @@ class W(ctypes.Structure):
 FAKE = ctypes.c_void_p(1 << 20)  # an aligned non-null address: never dereferenced on the host
 
 
+class Desc(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int), ("d_model", ctypes.c_int), ("n_experts", ctypes.c_int),
+                ("top_k", ctypes.c_int), ("x_dtype", ctypes.c_int), ("act", ctypes.c_int),
+                ("gemv_max_rows", ctypes.c_int), ("up", W), ("down", W), ("shared_up", W), ("shared_down", W),
+                ("flags", ctypes.c_int)]
+
+
 def _setup(lib):
     P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.moe_route_topk.argtypes = [P, I, I, I, P, P, P]
@@ -66,8 +73,14 @@ def _setup(lib):
     lib.nvfp4_expert_ffn_workspace_size.argtypes = [I, I, I, I]
     lib.nvfp4_expert_ffn_workspace_size.restype = SZ
     lib.nvfp4_expert_ffn.argtypes = [P, I, I, I, P, I, ctypes.POINTER(W), ctypes.POINTER(W), I, I, P, SZ, P, P]
-    lib.moe_weighted_row_sum.argtypes = [P, P, I, P, P, I, I, I, P]
-    lib.moe_weighted_row_sum_into.argtypes = [P, P, I, P, P, I, I, I, P]
+    lib.moe_weighted_row_sum.argtypes = [P, P, I, P, P, I, I, I, P, P]
+    lib.moe_weighted_row_sum_into.argtypes = [P, P, I, P, P, I, I, I, P, P]
+    lib.moe_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.moe_workspace_size.restype = SZ
+    lib.moe_error_word_clear.argtypes = [P, P]
+    lib.moe_error_word_read.argtypes = [P, P, P]
+    lib.moe_layer_workspace_size.argtypes = [ctypes.POINTER(Desc)]
+    lib.moe_layer_workspace_size.restype = SZ
     lib.nvfp4_unpack_bf16.argtypes = [P, P, I, I, P, P]
     lib.nvfp4_grouped_linear.argtypes = [P, I, I, I, P, I, ctypes.POINTER(W), I, P, SZ, P, P]
     lib.moe_status_string.argtypes = [I]
@@ -151,10 +164,13 @@ def test_ffn_argument_errors(lib):
 
 def test_wrs_and_unpack_and_linear_argument_errors(lib):
     _setup(lib)
-    assert lib.moe_weighted_row_sum(FAKE, FAKE, 4, FAKE, FAKE, 2, 2, 8, None) == 1      # dst aliases src
-    assert lib.moe_weighted_row_sum(FAKE, ctypes.c_void_p(2 << 20), 4, FAKE, FAKE, 2, 0, 8, None) == 1
-    assert lib.moe_weighted_row_sum_into(None, FAKE, 4, FAKE, FAKE, 2, 2, 8, None) == 1
-    assert lib.moe_weighted_row_sum(None, None, 0, None, None, 0, 2, 8, None) == 0    # empty
+    assert lib.moe_weighted_row_sum(FAKE, FAKE, 4, FAKE, FAKE, 2, 2, 8, None, None) == 1      # dst aliases src
+    assert lib.moe_weighted_row_sum(FAKE, ctypes.c_void_p(2 << 20), 4, FAKE, FAKE, 2, 0, 8, None, None) == 1
+    assert lib.moe_weighted_row_sum_into(None, FAKE, 4, FAKE, FAKE, 2, 2, 8, None, None) == 1
+    assert lib.moe_weighted_row_sum(None, None, 0, None, None, 0, 2, 8, None, None) == 0    # empty
+    # a misaligned error word
+    assert lib.moe_weighted_row_sum(FAKE, ctypes.c_void_p(2 << 20), 4, FAKE, FAKE, 2, 2, 8,
+                                    ctypes.c_void_p((3 << 20) + 2), None) == 1
     assert lib.nvfp4_unpack_bf16(FAKE, FAKE, 4, 48, FAKE, None) == 2                    # cols % 32
     assert lib.nvfp4_unpack_bf16(FAKE, FAKE, -1, 64, FAKE, None) == 1
     assert lib.nvfp4_unpack_bf16(ctypes.c_void_p((1 << 20) + 1), FAKE, 4, 64, FAKE, None) == 1
@@ -195,3 +211,79 @@ def test_packed_codes_size_and_pack_argument_errors(lib):
     assert lib.nvfp4_pack_codes(ctypes.byref(w), 2, FAKE, need - 1, None) == 1   # dst too small
     assert lib.nvfp4_pack_codes(ctypes.byref(_w(64, 40)), 2, FAKE, need, None) == 1  # cols % 32
     assert lib.nvfp4_pack_codes(ctypes.byref(w), 2, None, need, None) == 1       # null dst
+
+
+def test_workspace_size_serves_gather_and_both_expert_calls(lib):
+    """moe_workspace_size is the largest of the gather's and the two expert
+    calls' sizes (routed rows n*K, shared rows n; fp32 activations, the larger
+    dtype); 0 for invalid arguments.  Every workspace of these calls starts
+    with the 256 bytes of its error word."""
+    _setup(lib)
+    for n, K, E, d, f in ((4314, 6, 128, 2688, 3712), (1, 6, 128, 2688, 3712), (2, 8, 256, 2048, 1024),
+                          (0, 2, 8, 64, 128)):
+        got = lib.moe_workspace_size(n, K, E, d, f, 0)
+        parts = (lib.moe_gather_workspace_size(n, E), lib.nvfp4_expert_ffn_workspace_size(n * K, d, f, 0),
+                 lib.nvfp4_expert_ffn_workspace_size(n, d, f, 0), lib.nvfp4_expert_ffn_workspace_size(n * K, d, f, 1))
+        assert got == max(parts) and got % 256 == 0
+        assert lib.moe_workspace_size(n, K, E, d, f, 1) == got
+    assert lib.nvfp4_expert_ffn_workspace_size(0, 64, 128, 1) == 256
+    assert lib.moe_gather_workspace_size(0, 8) >= 256
+    assert lib.moe_workspace_size(4, 9, 8, 64, 128, 0) == 0      # top_k > E
+    assert lib.moe_workspace_size(4, 2, 8, 64, 128, 7) == 0      # unknown activation
+    assert lib.moe_workspace_size(-1, 2, 8, 64, 128, 0) == 0
+    assert lib.moe_workspace_size(4, 2, 2000, 64, 128, 0) == 0   # too many experts
+
+
+def test_error_word_helpers_reject_bad_pointers(lib):
+    _setup(lib)
+    v = ctypes.c_int32(0)
+    assert lib.moe_error_word_clear(None, None) == 1
+    assert lib.moe_error_word_clear(ctypes.c_void_p((1 << 20) + 2), None) == 1
+    assert lib.moe_error_word_read(None, ctypes.byref(v), None) == 1
+    assert lib.moe_error_word_read(FAKE, None, None) == 1
+
+
+def test_repacked_weights_are_both_or_neither_aligned_and_addressable(lib):
+    """A projection's repacked copies are checked on the host: both present or
+    both absent, 16-byte aligned, and one expert's repacked codes under 2 GiB
+    (the GEMM's 32-bit offsets)."""
+    _setup(lib)
+    dn = _w(64, 128)
+    ws = lib.nvfp4_expert_ffn_workspace_size(32, 64, 128, 1)
+
+    def call(up):
+        return lib.nvfp4_expert_ffn(FAKE, 1, 32, 16, FAKE, 8, ctypes.byref(up), ctypes.byref(dn), 0, 32,
+                                    FAKE, ws, FAKE, None)
+
+    ok = W(FAKE, FAKE, FAKE, 128, 64, ctypes.c_void_p(4 << 20), ctypes.c_void_p(5 << 20))
+    assert call(W(FAKE, FAKE, FAKE, 128, 64, ctypes.c_void_p(4 << 20), None)) == 1     # scales only
+    assert call(W(FAKE, FAKE, FAKE, 128, 64, None, ctypes.c_void_p(5 << 20))) == 1     # codes only
+    assert call(W(FAKE, FAKE, FAKE, 128, 64, ctypes.c_void_p((4 << 20) + 8), ctypes.c_void_p(5 << 20))) == 1
+    assert call(W(FAKE, FAKE, FAKE, 128, 64, ctypes.c_void_p(4 << 20), ctypes.c_void_p((5 << 20) + 4))) == 1
+    # 65536 rows x 32768 cols: 4096 blocks x 256 chunks x 1 KB = 1 GiB -> fine;
+    # 131072 rows: 2 GiB of repacked codes per expert -> refused
+    assert lib.nvfp4_packed_codes_bytes(1, 131072, 32768) == 1 << 31
+    big_up = W(FAKE, FAKE, FAKE, 131072, 32768, ctypes.c_void_p(4 << 20), ctypes.c_void_p(5 << 20))
+    big_dn = W(FAKE, FAKE, FAKE, 32768, 131072)
+    ws_big = lib.nvfp4_expert_ffn_workspace_size(1, 32768, 131072, 1)
+    assert lib.nvfp4_expert_ffn(FAKE, 1, 1, 1, FAKE, 1, ctypes.byref(big_up), ctypes.byref(big_dn), 0, 32,
+                                FAKE, ws_big, FAKE, None) == 1
+    # the well-formed pair passes the weight checks: with a too-small workspace
+    # the call gets as far as the workspace check (and launches nothing)
+    assert lib.nvfp4_expert_ffn(FAKE, 1, 32, 16, FAKE, 8, ctypes.byref(ok), ctypes.byref(dn), 0, 32,
+                                FAKE, ws - 1, FAKE, None) == 4
+
+
+def test_layer_description_flags_are_checked(lib):
+    """moe_layer_desc.flags takes only MOE_LAYER_SINGLE_LAUNCH; any other bit
+    makes the description invalid (size 0)."""
+    _setup(lib)
+    up, dn = W(FAKE, FAKE, FAKE, 128, 64), W(FAKE, FAKE, FAKE, 64, 128)
+    none = W(None, None, None, 0, 0)
+    d = Desc(16, 64, 8, 2, 0, 0, 32, up, dn, none, none, 0)
+    base = lib.moe_layer_workspace_size(ctypes.byref(d))
+    assert base > 0
+    d.flags = 1
+    assert lib.moe_layer_workspace_size(ctypes.byref(d)) == base
+    d.flags = 2
+    assert lib.moe_layer_workspace_size(ctypes.byref(d)) == 0

@@ -49,6 +49,27 @@ def bf16_bits_to_f64(b):
     return oracle.bf16_bits_to_f64(np.asarray(b).view(np.uint16))
 
 
+def ulps_f32(got, ref):
+    """|got - ref| in units of the binary32 spacing at ref (ref exact, float64)."""
+    ref = np.asarray(ref, dtype=np.float64)
+    spacing = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    return np.abs(np.asarray(got, dtype=np.float64) - ref) / spacing
+
+
+def route_weight_ulps_bound(K):
+    """Routing weights w_j = e_j / S on the GPU: each e_j = expf(l_j - l_0) is
+    within about 2 ulp of exp of the rounded difference (one rounding of the
+    difference, the device expf's error), S sums K of them in binary32 (K - 1
+    roundings) and the divide rounds once: a relative error below
+    (K + 4) * 2^-24, i.e. at most K + 4 units of the binary32 spacing."""
+    return K + 4
+
+
+def check_route_weights(got, ref, K):
+    u = ulps_f32(got, ref)
+    assert np.max(u) <= route_weight_ulps_bound(K), f"routing weights off by {np.max(u):.1f} ulp"
+
+
 # ----------------------------------------------------------------------------
 # unpack
 # ----------------------------------------------------------------------------
@@ -86,7 +107,7 @@ def _route_case(ops, logits, K):
     ids, w = ops.moe_route_topk(dev(logits), K)
     rids, rw = oracle.route_topk(logits, K)
     assert np.array_equal(host(ids), rids)
-    assert np.max(np.abs(host(w).astype(np.float64) - rw)) <= 4e-7
+    check_route_weights(host(w), rw, K)
 
 
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
@@ -121,10 +142,17 @@ def test_route_edge_cases(ops):
 # gather
 # ----------------------------------------------------------------------------
 
+def gather_ws(ops, n, E):
+    ws = torch.empty((ops.moe_gather_workspace_size(n, E),), dtype=torch.uint8, device=DEV)
+    ops.moe_error_word_clear(ws.view(torch.int32))
+    return ws
+
+
 def _gather_case(ops, x, ids, E):
     n, K = ids.shape
-    ws = torch.empty((ops.moe_gather_workspace_size(n, E),), dtype=torch.uint8, device=DEV)
+    ws = gather_ws(ops, n, E)
     xg, off, row_token, rows = ops.moe_gather_rows(dev(x), dev(ids), E, ws)
+    assert ops.moe_error_word_read(ws.view(torch.int32)) == 0
     r_off, r_rt, r_rows = oracle.gather_layout(ids, E)
     assert np.array_equal(host(off), r_off)
     assert np.array_equal(host(rows), r_rows)
@@ -152,17 +180,23 @@ def test_gather_edge_cases(ops):
     _gather_case(ops, x, ids, E)
 
 
-def test_gather_drops_invalid_ids(ops):
-    """Out-of-range ids are dropped: rows -1, not counted, tail rows untouched."""
+@pytest.mark.parametrize("n, K, E", [(10, 3, 5), (700, 4, 40)])
+def test_gather_drops_invalid_ids_and_sets_the_error_word(ops, n, K, E):
+    """Out-of-range ids are dropped (rows -1, not counted, tail rows untouched)
+    and set MOE_DEVERR_EXPERT_ID in the workspace's error word; the word is
+    sticky across a following valid call and cleared by moe_error_word_clear.
+    Both the one-workgroup path (10 tokens) and the multi-workgroup path (700)."""
     rng = np.random.default_rng(6)
-    n, K, E, d = 10, 3, 5, 16
+    d = 16
     ids = np.stack([rng.permutation(E)[:K] for _ in range(n)]).astype(np.int32)
-    ids[2, 1] = 5
+    ids[2, 1] = E
     ids[7, 0] = -3
     x = rng.standard_normal((n, d)).astype(np.float32)
-    ws = torch.empty((ops.moe_gather_workspace_size(n, E),), dtype=torch.uint8, device=DEV)
+    ws = gather_ws(ops, n, E)
+    word = ws.view(torch.int32)
     canary = torch.full((n * K, d), float("nan"), device=DEV)
     xg, off, row_token, rows = ops.moe_gather_rows(dev(x), dev(ids), E, ws, xg=canary)
+    assert ops.moe_error_word_read(word) == ops.MOE_DEVERR_EXPERT_ID
     valid = (ids >= 0) & (ids < E)
     got_rows = host(rows)
     assert np.all(got_rows[~valid] == -1)
@@ -178,6 +212,12 @@ def test_gather_drops_invalid_ids(ops):
                 assert rt[got_rows[t, j]] == t
                 assert np.array_equal(xgh[got_rows[t, j]], x[t])
     assert np.all(np.isnan(xgh[valid.sum():]))
+    good = np.stack([rng.permutation(E)[:K] for _ in range(n)]).astype(np.int32)
+    ops.moe_gather_rows(dev(x), dev(good), E, ws)
+    assert ops.moe_error_word_read(word) == ops.MOE_DEVERR_EXPERT_ID   # sticky
+    ops.moe_error_word_clear(word)
+    ops.moe_gather_rows(dev(x), dev(good), E, ws)
+    assert ops.moe_error_word_read(word) == 0
 
 
 # ----------------------------------------------------------------------------
@@ -198,26 +238,41 @@ def _wrs_bound(dst, src, rows, w):
 
 @pytest.mark.parametrize("d", [100, 33])
 def test_weighted_row_sum(ops, d):
+    """Bit for bit equal to the oracle's binary32 WeightedRowSum (a fixed-order
+    fmaf chain over j, then one add onto dst), with repeated source rows and a
+    pre-filled dst; within the rigorous bound of the exact sum; deterministic.
+    d = 100 takes the 16-byte kernel, d = 33 the element kernel.  Row 1 is the
+    case where an unfused multiply-add or the other j order gives other bits."""
     rng = np.random.default_rng(d)
     n, K, ns = 37, 6, 50
     src = rng.standard_normal((ns, d)).astype(np.float32)
     rows = rng.integers(0, ns, size=(n, K)).astype(np.int32)
     rows[0] = rows[0, 0]                       # repeated source rows
     w = rng.standard_normal((n, K)).astype(np.float32)
+    t = np.float32(1.0 + 2.0 ** -12)
+    src[0, 0], src[1, 0] = -1.0, t
+    rows[1, :2], w[1, :2], w[1, 2:] = [0, 1], [1.0, t], 0.0
     dst = rng.standard_normal((n, d)).astype(np.float32) * 10   # pre-filled dst
-    out = ops.moe_weighted_row_sum(dev(dst), dev(src), dev(rows), dev(w))
-    got = host(out).astype(np.float64)
+    dst[1, 0] = 0.0
+    word = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = ops.moe_weighted_row_sum(dev(dst), dev(src), dev(rows), dev(w), error_word=word)
+    got = host(out)
+    ref32 = oracle.weighted_row_sum_f32(dst, src, rows, w)
+    assert np.array_equal(got.view(np.uint32), ref32.view(np.uint32))
+    assert got[1, 0] == np.float32(2.0 ** -11 + 2.0 ** -24)
     ref = oracle.weighted_row_sum(dst, src, rows, w)
-    assert np.all(np.abs(got - ref) <= _wrs_bound(dst, src, rows, w))
+    assert np.all(np.abs(got.astype(np.float64) - ref) <= _wrs_bound(dst, src, rows, w))
+    assert int(host(word)[0]) == 0
     out2 = ops.moe_weighted_row_sum(dev(dst), dev(src), dev(rows), dev(w))
-    assert np.array_equal(host(out2), host(out))   # deterministic
+    assert np.array_equal(host(out2), got)   # deterministic
     into = ops.moe_weighted_row_sum_into(torch.full((n, d), 7.0, device=DEV), dev(src), dev(rows), dev(w))
     zero = np.zeros_like(dst)
-    assert np.all(np.abs(host(into) - oracle.weighted_row_sum(zero, src, rows, w)) <=
-                  _wrs_bound(zero, src, rows, w))
+    assert np.array_equal(host(into).view(np.uint32), oracle.weighted_row_sum_f32(zero, src, rows, w).view(np.uint32))
 
 
-def test_weighted_row_sum_skips_out_of_range_rows(ops):
+def test_weighted_row_sum_skips_out_of_range_rows_and_sets_the_error_word(ops):
+    """An out-of-range row contributes nothing (the oracle's binary32 sum with
+    that weight zeroed, bit for bit) and sets MOE_DEVERR_ROW in the error word."""
     rng = np.random.default_rng(8)
     n, K, ns, d = 6, 3, 4, 8
     src = rng.standard_normal((ns, d)).astype(np.float32)
@@ -225,12 +280,17 @@ def test_weighted_row_sum_skips_out_of_range_rows(ops):
     rows[1, 2], rows[4, 0] = 4, -1
     w = rng.standard_normal((n, K)).astype(np.float32)
     dst = rng.standard_normal((n, d)).astype(np.float32)
-    got = host(ops.moe_weighted_row_sum(dev(dst), dev(src), dev(rows), dev(w))).astype(np.float64)
+    word = torch.full((1,), 12345, dtype=torch.int32, device=DEV)
+    ops.moe_error_word_clear(word)
+    got = host(ops.moe_weighted_row_sum(dev(dst), dev(src), dev(rows), dev(w), error_word=word))
+    assert ops.moe_error_word_read(word) == ops.MOE_DEVERR_ROW
     w0 = w.copy()
     w0[1, 2] = w0[4, 0] = 0
     rows0 = np.clip(rows, 0, ns - 1)
-    ref = oracle.weighted_row_sum(dst, src, rows0, w0)
-    assert np.all(np.abs(got - ref) <= _wrs_bound(dst, src, rows, w) + 1e-30)
+    assert np.array_equal(got.view(np.uint32), oracle.weighted_row_sum_f32(dst, src, rows0, w0).view(np.uint32))
+    # without a word the call still skips the entry
+    got2 = host(ops.moe_weighted_row_sum(dev(dst), dev(src), dev(rows), dev(w)))
+    assert np.array_equal(got2, got)
 
 
 # ----------------------------------------------------------------------------
@@ -397,6 +457,10 @@ def test_layer_decode_workloads(ops, name):
     # routed expert outputs row by row (the packed yg buffer)
     R = inp.n * inp.K
     assert normwise(host(layer.yg)[:R], ref["yg"]) <= TOL_DECODE
+    # and against the oracle's binary32 fixed-order evaluation (another
+    # summation order than the kernels', so to the same tolerance, not bits)
+    ref32 = oracle.layer(inp, arith="f32")
+    assert normwise(got, ref32["out"]) <= TOL_DECODE
 
 
 # Every expert forced onto the prefill GEMM: a k that is not a whole number of
@@ -420,17 +484,61 @@ def test_layer_forced_onto_prefill_path(ops, case):
     assert normwise(got, oracle.layer(inp, bf16_act=True)["out"]) <= 2e-3
 
 
+def _whole_expert_checks(ops, inp, layer, off, row_token, experts):
+    """Every routed output row (yg) of the given experts against the oracle's
+    expert FFN over those rows: 2e-2 against the exact values, 2e-3 against
+    the bf16-activation mode (the path's own rounding of x and h)."""
+    yg = host(layer.yg)
+    x64 = oracle.activations_f64(inp.x, inp.x_dtype)
+    for e in experts:
+        r0, r1 = int(off[e]), int(off[e + 1])
+        rows_x = x64[row_token[r0:r1]]
+        one = np.array([0, r1 - r0], dtype=np.int32)
+        sub_up, sub_dn = oracle._one_expert(inp.up, e), oracle._one_expert(inp.down, e)
+        ref = oracle.expert_ffn(rows_x, one, sub_up, sub_dn, inp.f, inp.act)
+        ref_bf = oracle.expert_ffn(rows_x, one, sub_up, sub_dn, inp.f, inp.act, bf16_act=True)
+        got = yg[r0:r1].astype(np.float64)
+        print(f"  expert {e}: rows {r1 - r0}, err {normwise(got, ref):.2e} / bf16 mode {normwise(got, ref_bf):.2e}",
+              flush=True)
+        assert normwise(got, ref) <= TOL_PREFILL
+        assert normwise(got, ref_bf) <= 2e-3
+
+
+def _pick_experts(counts, k=8):
+    """The smallest and largest experts plus others spread over the row counts
+    (prefill4314: 160-250 rows, i.e. one full 128-row m-tile and a partial one)."""
+    order = np.argsort(counts, kind="stable")
+    idx = np.unique(np.linspace(0, len(order) - 1, k).round().astype(int))
+    return [int(order[i]) for i in idx]
+
+
+def _spread_tokens(n, m=64):
+    return sorted(set(np.linspace(0, n - 1, m).round().astype(int).tolist()))
+
+
 def test_layer_prefill_4314_tokens(ops):
+    """The largest workload (every expert on the bf16 MFMA GEMM): routing and
+    layout bit for bit; every yg row of 8 whole experts (smallest, largest and
+    six between); the layer output of 64 tokens spread over the batch (which
+    between them pick most experts) against the sampled oracle."""
     inp = cached_layer("prefill4314")
+    print("prefill4314 layer", flush=True)
     layer, got = _run_layer(ops, inp)
     ids, w = oracle.route_topk(inp.logits, inp.K)
     assert np.array_equal(host(layer.ids), ids)
+    check_route_weights(host(layer.w), w, inp.K)
     off, row_token, rows = oracle.gather_layout(ids, inp.E)
     assert np.array_equal(host(layer.offsets), off)
     assert np.array_equal(host(layer.rows), rows)
     assert np.array_equal(host(layer.row_token), row_token)
-    assert np.diff(off).min() > 32    # every expert on the prefill path
-    tokens = [0, 1, 777, 2048, 3001, 4313]
+    counts = np.diff(off)
+    assert counts.min() > 32    # every expert on the prefill path
+    experts = _pick_experts(counts)
+    assert len(experts) >= 8 and counts[experts].min() == counts.min() and counts[experts].max() == counts.max()
+    _whole_expert_checks(ops, inp, layer, off, row_token, experts)
+    tokens = _spread_tokens(inp.n)
+    assert len(tokens) >= 64
+    assert len(np.unique(ids[tokens])) >= 100
     ref = oracle.layer_sampled(inp, tokens, ids, w)
     assert normwise(got[tokens], ref) <= TOL_PREFILL
     ref_bf = oracle.layer_sampled(inp, tokens, ids, w, bf16_act_of_expert=lambda e: True)
@@ -500,9 +608,11 @@ def test_expert_ffn_writes_only_its_rows(ops):
 @pytest.mark.parametrize("name", ["tiny16", "decode1", "decode32_zipf", "gated2", "prefill4314"])
 def test_layer_forward_fused(ops, name):
     """moe_layer_forward matches the oracle at the path's tolerance, leaves the
-    same intermediates, and gives the same bits as the four calls in order."""
+    same intermediates, and gives the same bits as the four calls in order.
+    One- and two-token steps run as the single launch (the flag is set), and
+    without the flag as the per-step launches."""
     inp = cached_layer(name)
-    layer = ops.MoELayer(inp)
+    layer = ops.MoELayer(inp, single_launch=True)
     x, lg = dev(inp.x), dev(inp.logits)
     fused = layer.forward_fused(x, lg).clone()
     v = layer.views()
@@ -510,13 +620,13 @@ def test_layer_forward_fused(ops, name):
     ids, w = oracle.route_topk(inp.logits, inp.K)
     off, row_token, rows = oracle.gather_layout(ids, inp.E)
     assert np.array_equal(host(v["ids"]), ids)
-    assert np.max(np.abs(host(v["w"]).astype(np.float64) - w)) <= 4e-7
+    check_route_weights(host(v["w"]), w, inp.K)
     assert np.array_equal(host(v["offsets"]), off)
     assert np.array_equal(host(v["rows"]), rows)
     assert np.array_equal(host(v["row_token"]), row_token)
     got = host(fused).astype(np.float64)
     if name == "prefill4314":
-        tokens = [0, 5, 1234, 4313]
+        tokens = _spread_tokens(inp.n, 64)[::2]
         ref = oracle.layer_sampled(inp, tokens, ids, w)
         assert normwise(got[tokens], ref) <= TOL_PREFILL
     else:
@@ -532,6 +642,11 @@ def test_layer_forward_fused(ops, name):
         assert normwise(host(fused).astype(np.float64), host(unfused).astype(np.float64)) <= 2e-6
     else:
         assert torch.equal(fused, unfused)
+    layer.flags = 0   # without the flag: the per-step launches, bit for bit the four calls
+    plain = layer.forward_fused(x, lg).clone()
+    torch.cuda.synchronize()
+    assert int(host(v["decode_launch"])[0]) == (1 if single else 0)
+    assert torch.equal(plain, unfused)
 
 
 # Decode steps the single-launch layer takes (one or two tokens): tiny shapes
@@ -560,7 +675,7 @@ def test_layer_single_launch_decode(ops, case):
     name, ov, single = SINGLE_LAUNCH_CASES[case]
     inp = cached_layer(name, **ov)
     print(f"single-launch case {name} {ov}", flush=True)
-    layer = ops.MoELayer(inp)
+    layer = ops.MoELayer(inp, single_launch=True)
     x = dev(inp.x)
     logit_sets = [inp.logits, np.ascontiguousarray(np.roll(inp.logits, 1, axis=1))]
     lgs = [dev(l) for l in logit_sets]
@@ -575,7 +690,7 @@ def test_layer_single_launch_decode(ops, case):
     ids, w = oracle.route_topk(inp.logits, inp.K)
     off, row_token, rows = oracle.gather_layout(ids, inp.E)
     assert np.array_equal(host(v["ids"]), ids)
-    assert np.max(np.abs(host(v["w"]).astype(np.float64) - w)) <= 4e-7
+    check_route_weights(host(v["w"]), w, inp.K)
     assert np.array_equal(host(v["offsets"]), off)
     assert np.array_equal(host(v["rows"]), rows)
     assert np.array_equal(host(v["row_token"]), row_token)
@@ -595,7 +710,7 @@ def test_layer_single_launch_token_counts(ops):
     two tokens in any order (its flags and counters carry over between
     calls of different sizes)."""
     inp = cached_layer("decode1", n=2, K=3, E=32, fs=1856, seed=19)
-    layer = ops.MoELayer(inp)
+    layer = ops.MoELayer(inp, single_launch=True)
     x, lg = dev(inp.x), dev(inp.logits)
     order = [2, 1, 1, 2, 1, 2, 2]
     outs = [layer.forward_fused(x[:m], lg[:m]).clone()[:m] for m in order]
@@ -615,7 +730,7 @@ def test_layer_forward_fused_repeat_and_graph(ops, name):
     """Captured in a HIP graph and replayed, the fused layer gives the eager
     bits on every replay (the layer neither allocates nor synchronises)."""
     inp = cached_layer(name)
-    layer = ops.MoELayer(inp)
+    layer = ops.MoELayer(inp, single_launch=True)
     x, lg = dev(inp.x), dev(inp.logits)
     eager = layer.forward_fused(x, lg).clone()
     s = torch.cuda.Stream()
@@ -628,3 +743,70 @@ def test_layer_forward_fused_repeat_and_graph(ops, name):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(layer.out, eager)
+
+
+def test_layers_on_two_streams_concurrent_equal_alone_equal_serial(ops):
+    """Without the single-launch flag no kernel of a layer waits on another
+    workgroup, so layers may run concurrently: two layers (a 32-token and a
+    one-token decode step) launched on two streams at once, ten rounds, give
+    the bits each gives alone and the bits of running them one after the
+    other on one stream."""
+    a_inp, b_inp = cached_layer("decode32_zipf"), cached_layer("decode1")
+    la, lb = ops.MoELayer(a_inp), ops.MoELayer(b_inp)
+    xa, ga, xb, gb = dev(a_inp.x), dev(a_inp.logits), dev(b_inp.x), dev(b_inp.logits)
+    alone_a = la.forward_fused(xa, ga).clone()
+    torch.cuda.synchronize()
+    alone_b = lb.forward_fused(xb, gb).clone()
+    torch.cuda.synchronize()
+    serial_a = la.forward_fused(xa, ga).clone()
+    serial_b = lb.forward_fused(xb, gb).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(serial_a, alone_a) and torch.equal(serial_b, alone_b)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    torch.cuda.synchronize()
+    for _ in range(10):
+        with torch.cuda.stream(s1):
+            la.forward_fused(xa, ga, stream=s1)
+            oa = la.out.clone()
+        with torch.cuda.stream(s2):
+            lb.forward_fused(xb, gb, stream=s2)
+            ob = lb.out.clone()
+        outs.append((oa, ob))
+        s1.wait_stream(s2)   # the next round's writes of la.out / lb.out wait for the clones
+        s2.wait_stream(s1)
+    torch.cuda.synchronize()
+    for oa, ob in outs:
+        assert torch.equal(oa, alone_a) and torch.equal(ob, alone_b)
+    ref = oracle.layer(b_inp)["out"]
+    assert normwise(host(alone_b).astype(np.float64), ref) <= TOL_DECODE
+
+
+def test_single_launch_200_graph_replayed_steps(ops):
+    """The single-launch decode step, captured as 8 steps over two alternating
+    routings and replayed 25 times (200 steps): after every replay no bounded
+    wait has expired and every step's output equals the eager output of its
+    routing bit for bit.  Stops at the first mismatch or error word."""
+    inp = cached_layer("decode1")
+    layer = ops.MoELayer(inp, single_launch=True)
+    x = dev(inp.x)
+    lgs = [dev(inp.logits), dev(np.ascontiguousarray(np.roll(inp.logits, 5, axis=1)))]
+    eager = [layer.forward_fused(x, lg).clone() for lg in lgs]
+    torch.cuda.synchronize()
+    assert not torch.equal(eager[0], eager[1])
+    wait = layer.views()["wait_error"]
+    slots = torch.empty((8,) + tuple(layer.out.shape), dtype=torch.float32, device=DEV)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(8):
+            layer.forward_fused(x, lgs[i % 2], check=False)
+            slots[i].copy_(layer.out)
+    for rep in range(25):
+        slots.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(wait.cpu()[0]) == 0, f"a bounded wait expired in replay {rep}"
+        for i in range(8):
+            assert torch.equal(slots[i], eager[i % 2]), f"replay {rep}, step {i} differs"

@@ -414,3 +414,205 @@ def test_bf16_mode_rounds_activations(oracle_lib):
         h = np.array([[oracle.round_bf16(v) for v in row] for row in np.maximum(u, 0) ** 2])
         ref[r0:r1] = h @ _np_dequant(dn, e).T
     assert np.max(np.abs(got - ref)) <= 1e-13 * np.max(np.abs(ref))
+
+
+# ----------------------------------------------------------------------------
+# activation decode, and the sampled layer
+# ----------------------------------------------------------------------------
+
+def test_bf16_bits_decode_matches_torch_on_every_pattern(oracle_lib):
+    """PIN: the oracle's bf16 activation decode equals torch's bfloat16 -> float64
+    cast on all 65,536 bit patterns (NaNs where torch has NaNs, signed zeros and
+    subnormals included); the binary32 decode agrees with it."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.bf16_bits_to_f64(bits)
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 * 127   # exponent all ones, non-zero mantissa, both signs
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    g32 = oracle.activations_f32(bits, "bf16").astype(np.float64)
+    assert np.array_equal(np.isnan(g32), nan)
+    assert np.array_equal(g32[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("name, ov", [("tiny16", {}), ("gated2", {}),
+                                      ("decode1", dict(n=3, E=16, seed=71))])
+def test_layer_sampled_equals_layer(oracle_lib, name, ov):
+    """The sampled layer (the reference for the largest workload, where the whole
+    layer is too slow on a CPU) gives the full layer's rows bit for bit, in
+    both the exact and the bf16-activation mode, for any token subset and
+    order."""
+    inp = synth.make_layer(name, **ov)
+    full = oracle.layer(inp)
+    ids, w = full["ids"], full["weights"]
+    toks = list(range(inp.n))[::-1]
+    got = oracle.layer_sampled(inp, toks, ids, w)
+    assert np.array_equal(got, full["out"][toks])
+    sub = toks[: max(1, inp.n // 2)]
+    assert np.array_equal(oracle.layer_sampled(inp, sub, ids, w), full["out"][sub])
+    bf = oracle.layer(inp, bf16_act=True)["out"]
+    assert np.array_equal(oracle.layer_sampled(inp, toks, ids, w, bf16_act_of_expert=lambda e: True),
+                          bf[toks])
+
+
+# ----------------------------------------------------------------------------
+# the binary32 fixed-order arithmetic
+# ----------------------------------------------------------------------------
+
+from fractions import Fraction  # noqa: E402
+
+_F32_MAX = Fraction((2 ** 24 - 1) * 2 ** 104)
+
+
+def _round_f32(q: Fraction) -> float:
+    """Exact rational -> nearest binary32, ties to even (written from the
+    IEEE 754 definition: 24 significant bits, quantum 2^-149 at the bottom)."""
+    if q == 0:
+        return 0.0
+    neg = q < 0
+    a = -q if neg else q
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    qe = max(e - 23, -149)
+    scaled = a / Fraction(2) ** qe
+    m = scaled.numerator // scaled.denominator
+    rem = scaled - m
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and m % 2 == 1):
+        m += 1
+    v = Fraction(m) * Fraction(2) ** qe
+    out = float("inf") if v > _F32_MAX else float(v)
+    return -out if neg else out
+
+
+def _fmaf(a, b, c) -> float:
+    return _round_f32(Fraction(float(a)) * Fraction(float(b)) + Fraction(float(c)))
+
+
+def _mul32(a, b) -> float:
+    return _round_f32(Fraction(float(a)) * Fraction(float(b)))
+
+
+def _add32(a, b) -> float:
+    return _round_f32(Fraction(float(a)) + Fraction(float(b)))
+
+
+def test_round_f32_helper_matches_numpy():
+    """The test's own rational rounding agrees with numpy's float64 -> float32
+    cast wherever that cast is a single rounding (every double input)."""
+    rng = np.random.default_rng(81)
+    v = np.concatenate([rng.standard_normal(500) * 10.0 ** rng.integers(-40, 38, 500),
+                        [1 + 2.0 ** -24, 1 + 3 * 2.0 ** -24, 2.0 ** -149, 2.0 ** -150, 3 * 2.0 ** -150]])
+    for x in v:
+        assert _round_f32(Fraction(float(x))) == float(np.float32(x))
+
+
+def test_weighted_row_sum_f32_is_a_fixed_order_fma_chain(oracle_lib):
+    """PIN: the binary32 WeightedRowSum equals a chain of correctly rounded fmaf
+    over j from a zero accumulator followed by one rounded add onto dst,
+    evaluated here with exact rationals.  The first row is built so that an
+    unfused multiply-add, or the j-sum in the other order, gives another
+    value: fmaf(1, -1, 0) = -1, then fmaf(1+2^-12, 1+2^-12, -1) = 2^-11 + 2^-24
+    exactly, where rounding the product first loses the 2^-24."""
+    t = 1.0 + 2.0 ** -12
+    src = np.array([[-1.0, 3.0], [t, 0.5], [0.1, -7.25]], dtype=np.float32)
+    rows = np.array([[0, 1], [2, 2], [1, 0]], dtype=np.int32)
+    w = np.array([[1.0, t], [0.3, -0.7], [1e-3, 2.5]], dtype=np.float32)
+    dst = np.array([[0.0, 1.0], [5.0, -5.0], [1e8, 3.0]], dtype=np.float32)
+    got = oracle.weighted_row_sum_f32(dst, src, rows, w)
+    assert got[0, 0] == np.float32(2.0 ** -11 + 2.0 ** -24)
+    ref = np.zeros_like(dst)
+    for i in range(3):
+        for c in range(2):
+            acc = 0.0
+            for j in range(2):
+                acc = _fmaf(w[i, j], src[rows[i, j], c], acc)
+            ref[i, c] = _add32(dst[i, c], acc)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    # the hand fixture (every value exact in binary32) and a random case
+    g = _golden_wrs()
+    out = oracle.weighted_row_sum_f32(g["dst"], g["src"], g["rows"].astype(np.int32), g["weights"])
+    assert np.array_equal(out, g["expected"].astype(np.float32))
+    rng = np.random.default_rng(82)
+    src = rng.standard_normal((5, 3)).astype(np.float32)
+    rows = rng.integers(0, 5, size=(4, 6)).astype(np.int32)
+    w = rng.standard_normal((4, 6)).astype(np.float32)
+    dst = rng.standard_normal((4, 3)).astype(np.float32)
+    got = oracle.weighted_row_sum_f32(dst, src, rows, w)
+    for i in range(4):
+        for c in range(3):
+            acc = 0.0
+            for j in range(6):
+                acc = _fmaf(w[i, j], src[rows[i, j], c], acc)
+            assert got[i, c] == np.float32(_add32(dst[i, c], acc))
+    with pytest.raises(oracle.OracleError):
+        oracle.weighted_row_sum_f32(dst, src, np.full((4, 6), 5, dtype=np.int32), w)
+
+
+def _dot_chain(a, b):
+    acc = 0.0
+    for x, y in zip(a, b):
+        acc = _fmaf(x, y, acc)
+    return acc
+
+
+def test_linear_and_ffn_f32_are_fixed_order_fma_chains(oracle_lib):
+    """PIN: the binary32 projection is global * (fmaf chain over k ascending)
+    on weights decoded independently (torch's e4m3 cast, E2M1 bit fields), and
+    the binary32 FFN rounds relu^2 as max(u, 0) * max(u, 0): checked bit for bit
+    with exact rationals on a small case of two experts."""
+    d, f = 32, 16
+    up = synth.random_nvfp4(83, 2, f, d)
+    dn = synth.random_nvfp4(84, 2, d, f)
+    x = np.random.default_rng(85).standard_normal((3, d)).astype(np.float32)
+    off = np.array([0, 1, 3], dtype=np.int32)
+    lin = oracle.linear_f32(x, off, up)
+    ffn = oracle.expert_ffn_f32(x, off, up, dn, f, "relu2")
+    for e in range(2):
+        wu = _np_dequant(up, e) / float(up.globals_[e])
+        wd = _np_dequant(dn, e) / float(dn.globals_[e])
+        gu, gd = float(up.globals_[e]), float(dn.globals_[e])
+        for r in range(off[e], off[e + 1]):
+            u = [_mul32(gu, _dot_chain(x[r], wu[n])) for n in range(f)]
+            assert np.array_equal(lin[r], np.array(u, dtype=np.float32))
+            h = [_mul32(max(v, 0.0), max(v, 0.0)) for v in u]
+            y = [_mul32(gd, _dot_chain(h, wd[c])) for c in range(d)]
+            assert np.array_equal(ffn[r], np.array(y, dtype=np.float32))
+
+
+@pytest.mark.parametrize("act", ["relu2", "swiglu"])
+def test_ffn_f32_within_its_error_bound_of_the_exact_values(oracle_lib, act):
+    """The binary32 FFN stays within the forward error bound of a k-term fmaf
+    chain of the exact (double) FFN: per projection |err| <= (k+2) * 2^-24 *
+    (sum_k |a_k * b_k| * |g|), propagated through the activation; checked
+    here in the normwise form the layer tolerance uses (<= 1e-5)."""
+    E, d, f, n = 3, 256, 128, 17
+    up_rows = 2 * f if act == "swiglu" else f
+    up = synth.random_nvfp4(86, E, up_rows, d)
+    dn = synth.random_nvfp4(87, E, d, f)
+    x = np.random.default_rng(88).standard_normal((n, d)).astype(np.float32)
+    off = np.array([0, 5, 5, n], dtype=np.int32)
+    got = oracle.expert_ffn_f32(x, off, up, dn, f, act).astype(np.float64)
+    ref = oracle.expert_ffn(x.astype(np.float64), off, up, dn, f, act)
+    err = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
+    assert 0 < err <= 1e-5
+    lin = oracle.linear_f32(x, off, up).astype(np.float64)
+    lref = oracle.linear(x.astype(np.float64), off, up)
+    bound = (d + 2) * 2.0 ** -24 * (np.abs(x.astype(np.float64)) @ np.abs(
+        np.concatenate([_np_dequant(up, 0)]).T))
+    assert np.all(np.abs(lin[:5] - lref[:5]) <= bound[:5])
+
+
+def test_layer_f32_close_to_exact_layer(oracle_lib):
+    """The binary32 layer (fixed-order fmaf chains, binary32 routing weights)
+    agrees with the exact layer to the decode path's tolerance on the small
+    workload and on a gated shape."""
+    for name, ov in (("tiny16", {}), ("gated2", dict(n=3, E=16, seed=89))):
+        inp = synth.make_layer(name, **ov)
+        a = oracle.layer(inp, arith="f32")
+        b = oracle.layer(inp)
+        assert a["out"].dtype == np.float32
+        err = np.max(np.abs(a["out"].astype(np.float64) - b["out"])) / np.max(np.abs(b["out"]))
+        assert err <= 1e-5
