@@ -8,10 +8,18 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "launch.hpp"
 #include "moe_nvfp4.h"
 
 using namespace moe;
+
+// The layer workspace of moe_layer_forward_noalloc: one array per GPU, held
+// by the library until the process ends.  In host code `scratch` names a
+// host-side stand-in, not a device address; the device address comes from
+// hipGetSymbolAddress (noalloc_scratch below), once per device.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -432,6 +440,26 @@ bool plan_layer(const moe_layer_desc *dsc, LayerPlan *pl) {
   return true;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch`, its address looked up once per
+// device (with that device current) and kept.
+moe_status noalloc_scratch(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_HIP_ERROR;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_HIP_ERROR;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 size_t moe_layer_workspace_size(const moe_layer_desc *desc) {
@@ -467,6 +495,25 @@ moe_status moe_layer_workspace_init(const moe_layer_desc *desc, void *workspace,
 moe_status moe_layer_forward(const moe_layer_desc *dsc, const void *x, const float *logits, float *out,
                              void *workspace, size_t ws_bytes, hipStream_t stream) {
   return moe_layer_forward_profiled(dsc, x, logits, out, workspace, ws_bytes, nullptr, stream);
+}
+
+moe_status moe_layer_forward_noalloc(const moe_layer_desc *dsc, const void *x, const float *logits, float *out,
+                                     hipStream_t stream) {
+  LayerPlan p;
+  if (!plan_layer(dsc, &p)) return MOE_INVALID_ARG;
+  if (p.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_UNSUPPORTED;
+  if (p.n == 0) return MOE_OK;
+  if (!x || !logits || !out) return MOE_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(out, 16)) return MOE_INVALID_ARG;
+  void *ws = nullptr;
+  const moe_status st = noalloc_scratch(&ws);
+  if (st != MOE_OK) return st;
+  // the single-launch step's flags and counters start from zero on every
+  // call: the array keeps whatever the last call on this GPU left
+  if ((dsc->flags & MOE_LAYER_SINGLE_LAUNCH) &&
+      decode_layer_init((int32_t *)((char *)ws + p.off_sync), stream) != hipSuccess)
+    return MOE_HIP_ERROR;
+  return moe_layer_forward_profiled(dsc, x, logits, out, ws, MOE_NOALLOC_SCRATCH_BYTES, nullptr, stream);
 }
 
 moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, const float *logits, float *out,

@@ -116,6 +116,9 @@ _lib.moe_layer_forward.argtypes = [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _S
 _lib.moe_layer_forward.restype = _I
 _lib.moe_layer_forward_profiled.argtypes = [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _SZ, _P, _P]
 _lib.moe_layer_forward_profiled.restype = _I
+_lib.moe_layer_forward_noalloc.argtypes = [ctypes.POINTER(LayerDesc), _P, _P, _P, _P]
+_lib.moe_layer_forward_noalloc.restype = _I
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTED = ("moe_route_topk", "moe_gather_workspace_size", "moe_gather_rows",
             "nvfp4_expert_ffn_workspace_size", "nvfp4_grouped_linear_workspace_size",
@@ -125,7 +128,7 @@ EXPORTED = ("moe_route_topk", "moe_gather_workspace_size", "moe_gather_rows",
             "nvfp4_packed_codes_bytes", "nvfp4_pack_codes", "moe_status_string",
             "moe_layer_workspace_size",
             "moe_layer_workspace_init", "moe_layer_get_views",
-            "moe_layer_forward", "moe_layer_forward_profiled")
+            "moe_layer_forward", "moe_layer_forward_profiled", "moe_layer_forward_noalloc")
 
 
 def _check(fn: str, st: int):
@@ -353,6 +356,13 @@ def moe_layer_forward(desc: LayerDesc, x: torch.Tensor, logits: torch.Tensor, ou
     _check("moe_layer_forward", _lib.moe_layer_forward(
         ctypes.byref(desc), _ptr(x), _ptr(logits), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def moe_layer_forward_noalloc(desc: LayerDesc, x: torch.Tensor, logits: torch.Tensor, out: torch.Tensor,
+                              stream=None) -> torch.Tensor:
+    _check("moe_layer_forward_noalloc", _lib.moe_layer_forward_noalloc(
+        ctypes.byref(desc), _ptr(x), _ptr(logits), _ptr(out), _stream(stream)))
     return out
 
 

@@ -408,6 +408,26 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *desc, const void *x,
                                       float *out, void *workspace, size_t ws_bytes, hipEvent_t *events,
                                       hipStream_t stream);
 
+/* moe_layer_forward_noalloc -- moe_layer_forward for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The layer workspace is the library's own
+ * device array of MOE_NOALLOC_SCRATCH_BYTES, one per GPU, held until the
+ * process ends (its address is looked up at the first call on each GPU); the
+ * caller passes only x, logits and out, as for moe_layer_forward.  Nothing is
+ * allocated, freed or synchronised.
+ *   Limits: a description whose moe_layer_workspace_size exceeds
+ *   MOE_NOALLOC_SCRATCH_BYTES (e.g. thousands of tokens at d_model 2688) is
+ *   refused with MOE_UNSUPPORTED before anything runs.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (several streams or threads) race and give undefined results.  The
+ *   single-launch decode step (MOE_LAYER_SINGLE_LAUNCH) clears its flags and
+ *   counters with a small kernel on `stream` before each call.  The
+ *   intermediates are not exposed (no views).
+ * Errors as moe_layer_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_layer_forward_noalloc(const moe_layer_desc *desc, const void *x, const float *logits, float *out,
+                                     hipStream_t stream);
+
 /* A short English description of a status code (a static string). */
 const char *moe_status_string(moe_status status);
 

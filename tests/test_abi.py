@@ -287,3 +287,20 @@ def test_layer_description_flags_are_checked(lib):
     assert lib.moe_layer_workspace_size(ctypes.byref(d)) == base
     d.flags = 2
     assert lib.moe_layer_workspace_size(ctypes.byref(d)) == 0
+
+
+def test_noalloc_refuses_descriptions_beyond_its_scratch(lib):
+    """moe_layer_forward_noalloc checks the description's workspace size against
+    its static array before touching the device: the 4314-token layer (about
+    0.6 GB of intermediates) is refused with MOE_UNSUPPORTED, an invalid
+    description with MOE_INVALID_ARG."""
+    _setup(lib)
+    lib.moe_layer_forward_noalloc.argtypes = [ctypes.POINTER(Desc), ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_void_p]
+    up, dn = W(FAKE, FAKE, FAKE, 1856, 2688), W(FAKE, FAKE, FAKE, 2688, 1856)
+    sup, sdn = W(FAKE, FAKE, FAKE, 3712, 2688), W(FAKE, FAKE, FAKE, 2688, 3712)
+    d = Desc(4314, 2688, 128, 6, 1, 0, 32, up, dn, sup, sdn, 0)
+    assert lib.moe_layer_workspace_size(ctypes.byref(d)) > 64 << 20
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, None) == 2
+    d.flags = 4
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, None) == 1
