@@ -27,6 +27,9 @@ so tensors can be drawn in parallel and each is reproducible on its own):
                       (round to nearest even) for the bf16 workloads
     streams 2+2e, 3+2e  expert e's up and down weights, float32 N(0, 0.02)
     streams 2+2E, 3+2E  shared expert's up and down weights
+    stream 4+2E       router weights W_r [E, d], float32 N(0, 0.02) rounded to
+                      bfloat16 (for the router GEMM x . W_r^T; with d in the
+                      thousands its logits are about N(0, 1), like stream 0's)
 
 NVFP4 encoding of a weight W [rows, cols] (cols along the input axis):
 
@@ -200,7 +203,9 @@ def _cfg(name: str, overrides) -> dict:
 
 
 def _streams(cfg):
-    return np.random.SeedSequence(cfg["seed"]).spawn(4 + 2 * cfg["E"])
+    # child i depends only on (seed, i), so adding the router's stream at the
+    # end left every other stream unchanged
+    return np.random.SeedSequence(cfg["seed"]).spawn(5 + 2 * cfg["E"])
 
 
 def draw_logits(name: str, **overrides) -> np.ndarray:
@@ -224,6 +229,15 @@ def draw_activations(name: str, **overrides) -> np.ndarray:
     if cfg["x_dtype"] == "bf16":
         x = f32_to_bf16_bits(x)
     return x
+
+
+def draw_router(name: str, **overrides) -> np.ndarray:
+    """Router weights W_r [E, d] of workload ``name`` (stream 4 + 2E) as
+    bfloat16 bit patterns (uint16)."""
+    cfg = _cfg(name, overrides)
+    rng = np.random.default_rng(_streams(cfg)[4 + 2 * cfg["E"]])
+    w = rng.standard_normal((cfg["E"], cfg["d"]), dtype=np.float32) * np.float32(WEIGHT_STD)
+    return f32_to_bf16_bits(w)
 
 
 def make_layer(name: str, **overrides) -> LayerInputs:

@@ -69,6 +69,7 @@ def lib():
         L.orc_linear_f32.argtypes = [P, I, I, P, I, P, P, P, I, I, P]; L.orc_linear_f32.restype = I
         L.orc_weighted_row_sum_f32.argtypes = [P, P, I, P, P, I, I, I]
         L.orc_weighted_row_sum_f32.restype = I
+        L.orc_router_logits.argtypes = [P, I, I, P, I, P]; L.orc_router_logits.restype = I
         _lib = L
     return _lib
 
@@ -110,7 +111,8 @@ def round_bf16(v: float) -> float:
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """bfloat16 bit patterns -> float64 (a bf16 value is the top half of a binary32)."""
     b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
-    return b.view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
 
 
 def activations_f64(x: np.ndarray, x_dtype: str) -> np.ndarray:
@@ -142,6 +144,27 @@ def route_topk(logits: np.ndarray, K: int):
     w = np.empty((n, K), dtype=np.float64)
     _check(lib().orc_route_topk(_p(logits), n, E, K, _p(ids), _p(w)), "route_topk")
     return ids, w
+
+
+def router_logits(x64: np.ndarray, wr_bits: np.ndarray) -> np.ndarray:
+    """Router logits x . W_r^T in double, for activations x (double [n, d]) and
+    bf16 router weights W_r (bit patterns [E, d]).  Returns [n, E] float64."""
+    x64 = np.ascontiguousarray(x64, dtype=np.float64)
+    wr = bf16_bits_to_f64(wr_bits)
+    n, d = x64.shape
+    E = wr.shape[0]
+    out = np.empty((n, E), dtype=np.float64)
+    _check(lib().orc_router_logits(_p(x64), n, d, _p(np.ascontiguousarray(wr)), E, _p(out)), "router_logits")
+    return out
+
+
+def router_topk(x: np.ndarray, x_dtype: str, wr_bits: np.ndarray, K: int):
+    """The router step: logits = x . W_r^T (double, rounded once to binary32, the
+    logits' dtype), then route_topk on them.  Returns (ids, weights, logits
+    float64 before rounding)."""
+    lg = router_logits(activations_f64(x, x_dtype), wr_bits)
+    ids, w = route_topk(lg.astype(np.float32), K)
+    return ids, w, lg
 
 
 def gather_layout(ids: np.ndarray, E: int):

@@ -178,6 +178,21 @@ int orc_route_topk(const float *logits, int n, int E, int K, int32_t *ids, doubl
   return ORC_OK;
 }
 
+/* The router logits that routing ranks: logits[t][e] = sum_k x[t][k] * W_r[e][k]
+ * (the router's linear layer, x . W_r^T), k ascending, in double.  The
+ * linked PR "perf: cut host overhead from long prefills (routing, matmul
+ * scratch)" of [gllm#91] is about this step before routing. */
+int orc_router_logits(const double *x, int n, int d, const double *wr, int E, double *logits) {
+  if (n < 0 || d < 1 || E < 1) return ORC_EINVAL;
+  for (int t = 0; t < n; ++t)
+    for (int e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int k = 0; k < d; ++k) acc += x[(size_t)t * d + k] * wr[(size_t)e * d + k];
+      logits[(size_t)t * E + e] = acc;
+    }
+  return ORC_OK;
+}
+
 /* ------------------------------------------------------------------------- */
 /* Gather                                                                     */
 /* ------------------------------------------------------------------------- */

@@ -616,3 +616,66 @@ def test_layer_f32_close_to_exact_layer(oracle_lib):
         assert a["out"].dtype == np.float32
         err = np.max(np.abs(a["out"].astype(np.float64) - b["out"])) / np.max(np.abs(b["out"]))
         assert err <= 1e-5
+
+
+# ----------------------------------------------------------------------------
+# the router GEMM before routing
+# ----------------------------------------------------------------------------
+
+def test_router_logits_match_numpy_on_torch_decoded_weights(oracle_lib):
+    """PIN: the oracle's router logits equal numpy float64 x @ W_r^T with W_r
+    decoded by torch's bfloat16 cast (normwise 1e-13; another summation
+    order), for bf16 and fp32 activations."""
+    for name, ov in (("tiny16", {}), ("gated2", dict(n=5, E=32, seed=91))):
+        cfg = dict(synth.WORKLOADS[name], **ov)
+        wr = synth.draw_router(name, **ov)
+        assert wr.shape == (cfg["E"], cfg["d"]) and wr.dtype == np.uint16
+        x = synth.draw_activations(name, **ov)
+        x64 = oracle.activations_f64(x, cfg["x_dtype"])
+        wt = torch.from_numpy(wr.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+        ref = x64 @ wt.T
+        got = oracle.router_logits(x64, wr)
+        assert np.max(np.abs(got - ref)) <= 1e-13 * np.max(np.abs(ref))
+
+
+def test_router_logits_special_cases(oracle_lib):
+    """PIN: one-hot router rows pick columns of x exactly; a zero router gives
+    zero logits, i.e. all-tied routing to experts 0..K-1 with weights 1/K."""
+    rng = np.random.default_rng(92)
+    n, d, E = 6, 64, 8
+    x = rng.standard_normal((n, d))
+    onehot = np.zeros((E, d), dtype=np.float32)
+    cols = rng.permutation(d)[:E]
+    onehot[np.arange(E), cols] = 1.0
+    got = oracle.router_logits(x, synth.f32_to_bf16_bits(onehot))
+    assert np.array_equal(got, x[:, cols])
+    ids, w, lg = oracle.router_topk(x.astype(np.float32), "f32", np.zeros((E, d), dtype=np.uint16), 3)
+    assert np.all(lg == 0)
+    assert np.array_equal(ids, np.tile(np.arange(3, dtype=np.int32), (n, 1)))
+    assert np.allclose(w, 1.0 / 3.0, rtol=0, atol=1e-15)
+
+
+def test_router_topk_matches_torch_on_the_workload_router(oracle_lib):
+    """PIN: routing the router's logits equals torch.topk + softmax on numpy's
+    float64 logits rounded to binary32 (tie-free at these sizes); the logits
+    of a d = 2688 layer are about N(0, 1), like the workloads' drawn logits."""
+    name, ov = "decode1", dict(n=24, seed=93)
+    wr = synth.draw_router(name, **ov)
+    x = synth.draw_activations(name, **ov)
+    ids, w, lg = oracle.router_topk(x, "bf16", wr, 6)
+    assert 0.8 < float(np.std(lg)) < 1.3
+    wt = torch.from_numpy(wr.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    ref = (oracle.bf16_bits_to_f64(x) @ wt.T).astype(np.float32)
+    vals, idx = torch.topk(torch.from_numpy(ref), 6, dim=1)
+    assert np.array_equal(ids, idx.numpy().astype(np.int32))
+    assert np.max(np.abs(w - torch.softmax(vals.to(torch.float64), 1).numpy())) < 1e-15
+
+
+def test_router_stream_leaves_the_other_streams_unchanged():
+    """Adding the router's seed stream at the end keeps every earlier stream:
+    a SeedSequence child depends on its index only, not on how many are spawned."""
+    a = np.random.SeedSequence(2).spawn(4 + 2 * 128)
+    b = np.random.SeedSequence(2).spawn(5 + 2 * 128)
+    for i in (0, 1, 2, 257, 259):
+        assert np.array_equal(np.random.default_rng(a[i]).integers(0, 2 ** 31, 4),
+                              np.random.default_rng(b[i]).integers(0, 2 ** 31, 4))
