@@ -163,6 +163,36 @@ moe_status moe_route_topk(const float *logits, int n_tokens, int n_experts, int 
   return hip_status(launch_route_topk(logits, n_tokens, n_experts, top_k, topk_ids, topk_weights, stream));
 }
 
+size_t moe_router_workspace_size(int n_tokens, int n_experts) {
+  if (n_tokens < 0 || n_experts < 1 || n_experts > MOE_MAX_EXPERTS) return 0;
+  return align_up(router_counter_bytes(n_tokens)) + align_up((size_t)n_tokens * n_experts * sizeof(float)) + kAlign;
+}
+
+moe_status moe_router_workspace_init(void *workspace, size_t ws_bytes, int n_tokens, hipStream_t stream) {
+  if (!workspace || !aligned(workspace, kAlign) || n_tokens < 0) return MOE_INVALID_ARG;
+  if (ws_bytes < moe_router_workspace_size(n_tokens, 1)) return MOE_WORKSPACE_TOO_SMALL;
+  return hip_status(launch_router_init((int32_t *)workspace, n_tokens, stream));
+}
+
+moe_status moe_router_topk(const void *x, moe_dtype x_dtype, int n_tokens, int d_model, const uint16_t *router_w,
+                           int n_experts, int top_k, int32_t *topk_ids, float *topk_weights, float *logits,
+                           void *workspace, size_t ws_bytes, hipStream_t stream) {
+  if (n_tokens < 0 || d_model < 1 || n_experts < 1 || top_k < 1 || top_k > n_experts) return MOE_INVALID_ARG;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_INVALID_ARG;
+  if (n_experts > MOE_MAX_EXPERTS || top_k > MOE_MAX_TOPK) return MOE_UNSUPPORTED;
+  if (d_model % 32 != 0) return MOE_UNSUPPORTED;
+  if ((long)n_tokens * (n_experts > d_model ? n_experts : d_model) >= (1L << 40)) return MOE_UNSUPPORTED;
+  if (n_tokens == 0) return MOE_OK;
+  if (!x || !router_w || !topk_ids || !topk_weights || !workspace) return MOE_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(workspace, kAlign)) return MOE_INVALID_ARG;
+  if (logits && !aligned(logits, 4)) return MOE_INVALID_ARG;
+  if (ws_bytes < moe_router_workspace_size(n_tokens, n_experts)) return MOE_WORKSPACE_TOO_SMALL;
+  int32_t *counters = (int32_t *)workspace;
+  float *lg = logits ? logits : (float *)((char *)workspace + align_up(router_counter_bytes(n_tokens)));
+  return hip_status(launch_router_topk(x, x_dtype == MOE_F32, n_tokens, d_model, router_w, n_experts, top_k, lg,
+                                       counters, topk_ids, topk_weights, stream));
+}
+
 size_t moe_gather_workspace_size(int n_tokens, int n_experts) {
   if (n_tokens < 0 || n_experts < 1 || n_experts > MOE_MAX_EXPERTS) return 0;
   return kErrBytes + align_up(gather_workspace_bytes(n_tokens, n_experts));

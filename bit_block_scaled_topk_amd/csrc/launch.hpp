@@ -14,6 +14,16 @@ namespace moe {
 hipError_t launch_route_topk(const float *logits, int n_tokens, int n_experts, int top_k,
                              int32_t *ids, float *weights, hipStream_t stream);
 
+// Router GEMM (x . W_r^T, bf16 weights) fused with top-K and the softmax over
+// the picks.  counters: router_counter_bytes(n_tokens) bytes, zero before the
+// first call (launch_router_init) and left zero by every call; logits: [n][E]
+// fp32, written.
+size_t router_counter_bytes(int n_tokens);
+hipError_t launch_router_init(int32_t *counters, int n_tokens, hipStream_t stream);
+hipError_t launch_router_topk(const void *x, bool x_f32, int n_tokens, int d_model, const uint16_t *router_w,
+                              int n_experts, int top_k, float *logits, int32_t *counters, int32_t *ids,
+                              float *weights, hipStream_t stream);
+
 // Gather: bitmap layout + row copy (one workgroup for small problems).
 size_t gather_workspace_bytes(int n_tokens, int n_experts);
 bool gather_is_single_launch(int n_tokens, int top_k, int n_experts, int elem_bytes, int d_model);

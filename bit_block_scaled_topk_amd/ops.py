@@ -51,6 +51,12 @@ _lib.moe_status_string.argtypes = [_I]
 _lib.moe_status_string.restype = ctypes.c_char_p
 _lib.moe_route_topk.argtypes = [_P, _I, _I, _I, _P, _P, _P]
 _lib.moe_route_topk.restype = _I
+_lib.moe_router_workspace_size.argtypes = [_I, _I]
+_lib.moe_router_workspace_size.restype = _SZ
+_lib.moe_router_workspace_init.argtypes = [_P, _SZ, _I, _P]
+_lib.moe_router_workspace_init.restype = _I
+_lib.moe_router_topk.argtypes = [_P, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]
+_lib.moe_router_topk.restype = _I
 _lib.moe_gather_workspace_size.argtypes = [_I, _I]
 _lib.moe_gather_workspace_size.restype = _SZ
 _lib.moe_gather_rows.argtypes = [_P, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]
@@ -120,7 +126,8 @@ _lib.moe_layer_forward_noalloc.argtypes = [ctypes.POINTER(LayerDesc), _P, _P, _P
 _lib.moe_layer_forward_noalloc.restype = _I
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
-EXPORTED = ("moe_route_topk", "moe_gather_workspace_size", "moe_gather_rows",
+EXPORTED = ("moe_route_topk", "moe_router_workspace_size", "moe_router_workspace_init", "moe_router_topk",
+            "moe_gather_workspace_size", "moe_gather_rows",
             "nvfp4_expert_ffn_workspace_size", "nvfp4_grouped_linear_workspace_size",
             "nvfp4_expert_ffn", "moe_weighted_row_sum", "moe_weighted_row_sum_into", "moe_workspace_size",
             "moe_error_word_clear", "moe_error_word_read", "nvfp4_unpack_bf16",
@@ -201,6 +208,32 @@ def moe_route_topk(logits: torch.Tensor, top_k: int, ids: Optional[torch.Tensor]
     _check("moe_route_topk", _lib.moe_route_topk(_ptr(logits), n, E, top_k, _ptr(ids), _ptr(weights),
                                                  _stream(stream)))
     return ids, weights
+
+
+def moe_router_workspace_size(n_tokens: int, n_experts: int) -> int:
+    return int(_lib.moe_router_workspace_size(n_tokens, n_experts))
+
+
+def moe_router_workspace_init(workspace: torch.Tensor, n_tokens: int, stream=None) -> None:
+    _check("moe_router_workspace_init", _lib.moe_router_workspace_init(
+        _ptr(workspace), workspace.numel() * workspace.element_size(), n_tokens, _stream(stream)))
+
+
+def moe_router_topk(x: torch.Tensor, router_w: torch.Tensor, top_k: int, workspace: torch.Tensor,
+                    ids: Optional[torch.Tensor] = None, weights: Optional[torch.Tensor] = None,
+                    logits: Optional[torch.Tensor] = None, stream=None):
+    """x [n, d] (float32, or bf16 bits as int16), router_w [E, d] bf16 bits
+    (int16).  Returns (ids, weights, logits or None)."""
+    n, d = x.shape
+    E = router_w.shape[0]
+    if ids is None:
+        ids = torch.empty((n, top_k), dtype=torch.int32, device=x.device)
+    if weights is None:
+        weights = torch.empty((n, top_k), dtype=torch.float32, device=x.device)
+    _check("moe_router_topk", _lib.moe_router_topk(
+        _ptr(x), _dtype_code(x), n, d, _ptr(router_w), E, top_k, _ptr(ids), _ptr(weights), _ptr(logits),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return ids, weights, logits
 
 
 def moe_gather_workspace_size(n_tokens: int, n_experts: int) -> int:

@@ -156,6 +156,46 @@ moe_status nvfp4_pack_codes(const moe_nvfp4_weights *w, int n_experts, uint8_t *
 moe_status moe_route_topk(const float *logits, int n_tokens, int n_experts, int top_k,
                           int32_t *topk_ids, float *topk_weights, hipStream_t stream);
 
+/* Workspace bytes moe_router_topk needs for n_tokens tokens and n_experts
+ * experts: one counter per 16 tokens and a logits buffer [n_tokens][n_experts]
+ * (used when the caller does not ask for the logits); 0 for invalid
+ * arguments. */
+size_t moe_router_workspace_size(int n_tokens, int n_experts);
+
+/* moe_router_workspace_init -- prepare a router workspace once, after it is
+ * allocated and before its first moe_router_topk: zeroes the counters of up
+ * to n_tokens tokens (a kernel on `stream`; nothing is allocated).  Every
+ * moe_router_topk call leaves them at zero again.  MOE_INVALID_ARG for a null
+ * or unaligned (256-byte) workspace, MOE_WORKSPACE_TOO_SMALL if ws_bytes <
+ * moe_router_workspace_size(n_tokens, 1). */
+moe_status moe_router_workspace_init(void *workspace, size_t ws_bytes, int n_tokens, hipStream_t stream);
+
+/* moe_router_topk -- the router step before routing, fused with it: the
+ * logits x . W_r^T of every token on the matrix cores (bf16 operands, exact
+ * products, fp32 accumulation in a fixed order), then per token the top_k
+ * experts and their weights exactly as moe_route_topk computes them from
+ * those logits.  (The gllm #91 page links a pull request, "perf: cut host
+ * overhead from long prefills (routing, matmul scratch)", about this step.)
+ *   x         device [n_tokens][d_model] of x_dtype (BF16, or F32 taken as
+ *             three bf16 terms hi + mid + lo: 24 significant bits), 16-byte
+ *             aligned
+ *   router_w  device bf16 bits [n_experts][d_model], 16-byte aligned
+ *   topk_ids, topk_weights  device [n_tokens][top_k], as moe_route_topk's
+ *   logits    device float [n_tokens][n_experts] (out), or NULL: then they
+ *             live in the workspace only
+ *   workspace device, >= moe_router_workspace_size(n_tokens, n_experts),
+ *             256-byte aligned, prepared by moe_router_workspace_init; calls
+ *             that overlap on one workspace race
+ * The logits of a token differ from the exact x . W_r^T by at most about
+ * (d_model + 8) * 2^-24 * sum_k |x_k W_r[e][k]|, so two experts whose exact
+ * logits are closer than twice that may be ranked either way; the ids and
+ * weights are always those of the logits written.
+ * Limits: d_model a positive multiple of 32, 1 <= n_experts <= 1024,
+ * 1 <= top_k <= min(n_experts, 32); n_tokens == 0 launches nothing. */
+moe_status moe_router_topk(const void *x, moe_dtype x_dtype, int n_tokens, int d_model, const uint16_t *router_w,
+                           int n_experts, int top_k, int32_t *topk_ids, float *topk_weights, float *logits,
+                           void *workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Workspace bytes moe_gather_rows needs for n_tokens tokens and n_experts
  * experts, the 256 reserved bytes of the error word included (0 for invalid
  * arguments). */

@@ -304,3 +304,33 @@ def test_noalloc_refuses_descriptions_beyond_its_scratch(lib):
     assert lib.moe_layer_forward_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, None) == 2
     d.flags = 4
     assert lib.moe_layer_forward_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, None) == 1
+
+
+def test_router_argument_errors(lib):
+    """moe_router_topk and its workspace calls check their arguments on the host."""
+    _setup(lib)
+    P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.moe_router_workspace_size.argtypes = [I, I]
+    lib.moe_router_workspace_size.restype = SZ
+    lib.moe_router_workspace_init.argtypes = [P, SZ, I, P]
+    lib.moe_router_topk.argtypes = [P, I, I, I, P, I, I, P, P, P, P, SZ, P]
+    ws = lib.moe_router_workspace_size(4314, 128)
+    assert ws >= 4314 * 128 * 4 + 270 * 64 and ws % 256 == 0
+    assert lib.moe_router_workspace_size(16, 0) == 0
+    assert lib.moe_router_workspace_size(16, 2048) == 0
+    assert lib.moe_router_workspace_init(None, ws, 16, None) == 1
+    assert lib.moe_router_workspace_init(ctypes.c_void_p((1 << 20) + 16), ws, 16, None) == 1
+    assert lib.moe_router_workspace_init(FAKE, 0, 16, None) == 4
+    call = lambda **k: lib.moe_router_topk(*[dict(dict(x=FAKE, dt=1, n=16, d=64, w=FAKE, E=8, K=2, ids=FAKE,
+                                                       wt=FAKE, lg=None, ws=FAKE, wsb=ws), **k)[a]
+                                             for a in ("x", "dt", "n", "d", "w", "E", "K", "ids", "wt", "lg",
+                                                       "ws", "wsb")], None)
+    assert call(d=48) == 2                       # d_model % 32
+    assert call(K=9) == 1                        # top_k > E
+    assert call(E=2048) == 2
+    assert call(K=33, E=64) == 2
+    assert call(dt=3) == 1
+    assert call(w=None) == 1
+    assert call(x=ctypes.c_void_p((1 << 20) + 8)) == 1     # misaligned x
+    assert call(wsb=lib.moe_router_workspace_size(16, 8) - 1) == 4
+    assert call(n=0, x=None, w=None, ids=None, wt=None, ws=None) == 0

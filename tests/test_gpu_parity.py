@@ -810,3 +810,81 @@ def test_single_launch_200_graph_replayed_steps(ops):
         assert int(wait.cpu()[0]) == 0, f"a bounded wait expired in replay {rep}"
         for i in range(8):
             assert torch.equal(slots[i], eager[i % 2]), f"replay {rep}, step {i} differs"
+
+
+# ----------------------------------------------------------------------------
+# the router GEMM fused with routing
+# ----------------------------------------------------------------------------
+
+def router_ws(ops, n, E):
+    ws = torch.empty((ops.moe_router_workspace_size(n, E),), dtype=torch.uint8, device=DEV)
+    ops.moe_router_workspace_init(ws, n)
+    return ws
+
+
+def _router_case(ops, x, x_dtype, wr, K, min_separated=0.5):
+    """moe_router_topk against the oracle in three stages: its logits within the
+    fp32 accumulation bound of the exact x . W_r^T; its ids and weights those
+    of the routing rule applied to its own logits (ids bit for bit, weights
+    within the routing bound, and the same bits as moe_route_topk on them);
+    and the oracle's ids wherever the exact top K + 1 logits are separated by
+    more than twice the bound."""
+    n, d = x.shape
+    E = wr.shape[0]
+    ws = router_ws(ops, n, E)
+    logits = torch.full((n, E), float("nan"), device=DEV)
+    ids, w, _ = ops.moe_router_topk(dev(x), dev(wr), K, ws, logits=logits)
+    lg = host(logits).astype(np.float64)
+    x64 = oracle.activations_f64(x, x_dtype)
+    exact = oracle.router_logits(x64, wr)
+    bound = (d + 8) * 2.0 ** -24 * (np.abs(x64) @ np.abs(oracle.bf16_bits_to_f64(wr)).T)
+    assert np.all(np.abs(lg - exact) <= bound), f"router logits off by {np.max(np.abs(lg - exact) / bound):.2f} x bound"
+    rid, rw = oracle.route_topk(lg.astype(np.float32), K)
+    assert np.array_equal(host(ids), rid)
+    check_route_weights(host(w), rw, K)
+    ids2, w2 = ops.moe_route_topk(logits, K)
+    assert np.array_equal(host(ids2), host(ids)) and np.array_equal(host(w2), host(w))
+    oid, ow, _ = oracle.router_topk(x, x_dtype, wr, K)
+    srt = -np.sort(-exact, axis=1)[:, :min(K + 1, E)]
+    gaps = -np.diff(srt, axis=1).min(axis=1) if srt.shape[1] > 1 else np.full(n, np.inf)
+    sep = gaps > 2 * bound.max(axis=1)
+    assert sep.mean() >= min_separated, f"only {sep.mean():.2f} of the tokens are separated"
+    assert np.array_equal(host(ids)[sep], oid[sep])
+    # the counters were left at zero: a second call, without a logits output,
+    # gives the same bits
+    ids3, w3, _ = ops.moe_router_topk(dev(x), dev(wr), K, ws)
+    assert np.array_equal(host(ids3), host(ids)) and np.array_equal(host(w3), host(w))
+    return host(ids), sep
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_router_topk_workloads(ops, name):
+    """Each workload's activations through its seeded bf16 router (d_model 64
+    with fp32 activations for the small workload; 1 to 4314 tokens)."""
+    cfg = synth.WORKLOADS[name]
+    print(f"router case {name}", flush=True)
+    _router_case(ops, synth.draw_activations(name), cfg["x_dtype"], synth.draw_router(name), cfg["K"])
+
+
+def test_router_topk_edge_cases(ops):
+    """Ragged token tiles and expert groups (37 tokens, 77 experts), the largest
+    E and K (1024, 32), one expert, ties (a zero router: experts 0..K-1 with
+    weight 1/K), a long fp32 row, and no tokens."""
+    rng = np.random.default_rng(95)
+
+    def bf(a):
+        return synth.f32_to_bf16_bits(np.asarray(a, dtype=np.float32))
+
+    x = bf(rng.standard_normal((37, 96)))
+    _router_case(ops, x, "bf16", bf(rng.standard_normal((77, 96)) * 0.1), 5)
+    x = bf(rng.standard_normal((9, 64)))
+    _router_case(ops, x, "bf16", bf(rng.standard_normal((1024, 64)) * 0.1), 32, min_separated=0.0)
+    _router_case(ops, x, "bf16", bf(rng.standard_normal((1, 64))), 1)
+    ids, _ = _router_case(ops, x, "bf16", np.zeros((12, 64), dtype=np.uint16), 4, min_separated=0.0)
+    assert np.array_equal(ids, np.tile(np.arange(4, dtype=np.int32), (9, 1)))
+    xf = rng.standard_normal((20, 4096)).astype(np.float32)
+    _router_case(ops, xf, "f32", bf(rng.standard_normal((64, 4096)) * 0.02), 6)
+    ws = router_ws(ops, 0, 8)
+    ids, w, _ = ops.moe_router_topk(torch.empty((0, 64), dtype=torch.int16, device=DEV),
+                                    dev(np.zeros((8, 64), dtype=np.uint16)), 2, ws)
+    assert ids.shape == (0, 2)
