@@ -405,7 +405,8 @@ struct LayerPlan {
   int n, d, E, K, f, fs, R;
   bool has_shared, f32;
   size_t off_ids, off_w, off_offsets, off_row_token, off_rows, off_yg, off_gather, off_h, off_hs, off_split,
-      off_sync, total;
+      off_sync, off_cmb, total;
+  int n_ct;  // 256-column tiles of the output (the fused combine's counters per token)
   int sync_words;
 };
 
@@ -421,7 +422,7 @@ bool plan_layer(const moe_layer_desc *dsc, LayerPlan *pl) {
   if (dsc->x_dtype != MOE_F32 && dsc->x_dtype != MOE_BF16) return false;
   if (dsc->act != MOE_RELU2 && dsc->act != MOE_SWIGLU) return false;
   if (dsc->gemv_max_rows < 0 || dsc->gemv_max_rows > MOE_MAX_GEMV_ROWS) return false;
-  if (dsc->flags & ~MOE_LAYER_SINGLE_LAUNCH) return false;
+  if (dsc->flags & ~(MOE_LAYER_SINGLE_LAUNCH | MOE_LAYER_FUSED_COMBINE)) return false;
   if (!weights_ok(&dsc->up) || !weights_ok(&dsc->down)) return false;
   p.f = dsc->down.cols;
   if (dsc->up.cols != p.d || dsc->down.rows != p.d) return false;
@@ -464,6 +465,8 @@ bool plan_layer(const moe_layer_desc *dsc, LayerPlan *pl) {
   p.off_h = take(h_bytes(p.R, p.f));
   p.off_hs = take(p.has_shared ? h_bytes(p.n, p.fs) : 0);
   p.off_split = take(p.f32 ? split_bytes(p.n, p.d) : 0);
+  p.n_ct = (p.d + kGemmF32TileCols - 1) / kGemmF32TileCols;
+  p.off_cmb = take((size_t)p.n * p.n_ct * 64);
   (void)xb;
   p.total = o;
   *pl = p;
@@ -663,6 +666,29 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, 
     sd = make_problem(hs, hs_plane, p.fs, nullptr, 1, p.n, p.n, &dsc->shared_down, p.d, out, nullptr, p.d, 0);
   }
 
+  // With MOE_LAYER_FUSED_COMBINE the combine joins the down GEMM when both
+  // experts take it (a prefill step with a shared expert) and its coherent
+  // accesses fit 32-bit offsets; the up GEMM launch zeroes its counters.
+  const bool fuse_combine = (dsc->flags & MOE_LAYER_FUSED_COMBINE) && routed_gemm && shared_gemm && p.d % 4 == 0 &&
+                            (long)p.R * p.d * 4 < (1L << 31) && (long)p.n * p.d * 4 < (1L << 31);
+  CombineArgs cmb{};
+  if (fuse_combine) {
+    cmb.on = 1;
+    cmb.counters = (int32_t *)(ws + p.off_cmb);
+    cmb.ids = ids;
+    cmb.rows = rows;
+    cmb.row_token = row_token;
+    cmb.offsets = offsets;
+    cmb.w = w;
+    cmb.yg = yg;
+    cmb.out = out;
+    cmb.n = p.n;
+    cmb.K = p.K;
+    cmb.d = p.d;
+    cmb.gmax = gmax;
+    cmb.n_ct = p.n_ct;
+  }
+
   if (mark(2) != hipSuccess) return MOE_HIP_ERROR;
   // 3. up projections (+ activation); the shared expert joins the routed launch
   //    when both use the same epilogue
@@ -689,7 +715,9 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, 
     const bool gjoin = shared_gemm && epi == EPI_RELU2;
     if (gjoin) gem[g++] = as_prefill(su, gmax);
     if (routed_gemm) gem[g++] = as_prefill(ru, gmax);
-    if (g > 0 && launch_dq_gemm(gem, g, epi, stream) != hipSuccess) return MOE_HIP_ERROR;
+    if (g > 0 && launch_dq_gemm(gem, g, epi, stream, nullptr, fuse_combine ? cmb.counters : nullptr,
+                                fuse_combine ? (long)p.n * p.n_ct : 0) != hipSuccess)
+      return MOE_HIP_ERROR;
     if (shared_gemm && !gjoin) {
       ProjProblem s1 = as_prefill(su, gmax);
       if (launch_dq_gemm(&s1, 1, EPI_RELU2, stream) != hipSuccess) return MOE_HIP_ERROR;
@@ -714,12 +742,15 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, 
     int g = 0;
     if (shared_gemm) gem[g++] = as_prefill(sd, gmax);
     if (routed_gemm) gem[g++] = as_prefill(rd, gmax);
-    if (g > 0 && launch_dq_gemm(gem, g, EPI_F32, stream) != hipSuccess) return MOE_HIP_ERROR;
+    if (g > 0 && launch_dq_gemm(gem, g, EPI_F32, stream, fuse_combine ? &cmb : nullptr) != hipSuccess)
+      return MOE_HIP_ERROR;
   }
 
   if (mark(6) != hipSuccess) return MOE_HIP_ERROR;
-  // 5. combine: out += sum_j w * yg[rows]  (onto zero without a shared expert)
-  if (launch_weighted_row_sum(out, yg, p.R, rows, w, p.n, p.K, p.d, p.has_shared, nullptr, stream) != hipSuccess)
+  // 5. combine: out += sum_j w * yg[rows]  (onto zero without a shared
+  //    expert), unless the down launch did it
+  if (!fuse_combine &&
+      launch_weighted_row_sum(out, yg, p.R, rows, w, p.n, p.K, p.d, p.has_shared, nullptr, stream) != hipSuccess)
     return MOE_HIP_ERROR;
   if (mark(7) != hipSuccess) return MOE_HIP_ERROR;
   return MOE_OK;

@@ -22,9 +22,15 @@ constexpr uint32_t OOB = 0x80000000u; // a buffer offset past every extent: the 
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+constexpr int kSc1 = 16;  // cache-policy bit of a buffer access: device-coherent (past the per-XCD L2)
+static_assert(BN == kGemmF32TileCols, "the combine's column tiles are the f32 GEMM's");
+
 struct GemmBatch {
   ProjProblem p[2];
   int count;
+  CombineArgs cmb;
+  int32_t *zero;  // words zero[16 i], i < n_zero, set to 0 before the tiles
+  long n_zero;
 };
 
 // Half of dq8_bf16: code bytes 2h and 2h + 1 of `w` (elements 4h .. 4h + 3)
@@ -134,6 +140,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr bool SP = SM == 1;
   __shared__ int s_info[3];
   __shared__ __attribute__((aligned(1024))) uint8_t sA[2 * A_BYTES];
+  __shared__ int s_last[BM + 1];  // the combine: tokens this tile completes, and their count
+
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < batch.n_zero; i += (long)gridDim.x * blockDim.x)
+    batch.zero[16 * i] = 0;
 
   // Tiles in launch order, column tile fastest.  Workgroups are dealt
   // round-robin over the 8 XCDs, so with 8 column tiles (the routed up
@@ -363,6 +373,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   if constexpr (EPI == EPI_F32) {
     const bool aligned = (((uintptr_t)p.out_f32 | (uintptr_t)(p.ldo * 4)) & 15) == 0 && p.n_out % 4 == 0;
     const int c0 = nt * BN + wave * 64;  // first output column of this wavefront
+    const CombineArgs &cmb = batch.cmb;
+    // the combine stores the tile device-coherently (the host only fuses it
+    // with aligned outputs under 2 GiB)
+    const __amdgpu_buffer_rsrc_t o_rsrc =
+        make_rsrc(p.out_f32, cmb.on ? (uint32_t)((size_t)p.n_rows * p.ldo * 4) : 0u);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int m = 16 * i + nl;
@@ -378,13 +393,63 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
           v.y = value(i, j, 1);
           v.z = value(i, j, 2);
           v.w = value(i, j, 3);
-          *(f32x4_t *)(p.out_f32 + o) = v;
+          if (cmb.on)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), o_rsrc, (uint32_t)(o * 4), 0,
+                                                   kSc1);
+          else
+            *(f32x4_t *)(p.out_f32 + o) = v;
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             if (col + r < p.n_out) p.out_f32[o + r] = value(i, j, r);
         }
       }
+    }
+    if (!cmb.on) return;
+    // Count this tile's rows for their tokens once every store of the
+    // workgroup has completed; collect the tokens whose count is complete.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    if (tid == 0) s_last[BM] = 0;
+    __syncthreads();
+    if (tid < mrows) {
+      const int t = p.known_rows >= 0 ? r0 + tid : cmb.row_token[r0 + tid];
+      int target = 1;  // the shared expert's row
+      for (int j = 0; j < cmb.K; ++j) {
+        const int ej = cmb.ids[(size_t)t * cmb.K + j];
+        target += (cmb.offsets[ej + 1] - cmb.offsets[ej]) > cmb.gmax ? 1 : 0;
+      }
+      int32_t *ctr = cmb.counters + ((size_t)t * cmb.n_ct + nt) * 16;
+      const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old + 1 == target) s_last[atomicAdd(&s_last[BM], 1)] = t;
+    }
+    __syncthreads();
+    // out[t][c..c+3] = out + sum_j w_j * yg[rows[t][j]] for the tile's 256
+    // columns: four tokens at a time, 64 threads x 4 columns each
+    const int n_last = s_last[BM];
+    const __amdgpu_buffer_rsrc_t y_rsrc = make_rsrc(cmb.yg, (uint32_t)((size_t)cmb.n * cmb.K * cmb.d * 4));
+    const __amdgpu_buffer_rsrc_t s_rsrc = make_rsrc(cmb.out, (uint32_t)((size_t)cmb.n * cmb.d * 4));
+    const int c = nt * BN + 4 * lane;
+    for (int li = wave; li < n_last; li += 4) {
+      const int t = s_last[li];
+      if (c >= cmb.d) continue;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < cmb.K; ++j) {
+        const int r = cmb.rows[(size_t)t * cmb.K + j];
+        const float wt = cmb.w[(size_t)t * cmb.K + j];
+        const f32x4_t y = __builtin_bit_cast(
+            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(y_rsrc, (uint32_t)(((size_t)r * cmb.d + c) * 4), 0, kSc1));
+        acc.x = fmaf(wt, y.x, acc.x);
+        acc.y = fmaf(wt, y.y, acc.y);
+        acc.z = fmaf(wt, y.z, acc.z);
+        acc.w = fmaf(wt, y.w, acc.w);
+      }
+      f32x4_t o = __builtin_bit_cast(
+          f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(s_rsrc, (uint32_t)(((size_t)t * cmb.d + c) * 4), 0, kSc1));
+      o.x += acc.x;
+      o.y += acc.y;
+      o.z += acc.z;
+      o.w += acc.w;
+      *(f32x4_t *)(cmb.out + (size_t)t * cmb.d + c) = o;
     }
   } else {
     const bool vec = ((obase | (uintptr_t)(p.ldo * EB)) & 15) == 0 && p.n_out % PER == 0;
@@ -432,9 +497,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 
 }  // namespace
 
-hipError_t launch_dq_gemm(ProjProblem *probs, int count, int epi, hipStream_t stream) {
+hipError_t launch_dq_gemm(ProjProblem *probs, int count, int epi, hipStream_t stream, const CombineArgs *combine,
+                          int32_t *zero_counters, long n_zero) {
   GemmBatch b;
   b.count = 0;
+  b.cmb = CombineArgs{};
+  if (combine && combine->on) {
+    if (epi != EPI_F32) return hipErrorInvalidValue;
+    b.cmb = *combine;
+  }
+  b.zero = zero_counters;
+  b.n_zero = zero_counters ? n_zero : 0;
   long total = 0;
   for (int i = 0; i < count; ++i) {
     ProjProblem p = probs[i];

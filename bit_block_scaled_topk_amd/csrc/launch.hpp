@@ -106,7 +106,33 @@ hipError_t launch_pack_scales(const uint8_t *scales, int n_experts, int rows, in
 long packed_codes_bytes(long n_experts, int rows, int cols);
 hipError_t launch_pack_codes(const uint8_t *codes, int n_experts, int rows, int cols, uint8_t *dst,
                              hipStream_t stream);
-hipError_t launch_dq_gemm(ProjProblem *probs, int count, int epi, hipStream_t stream);
+// WeightedRowSum fused into the prefill down projection (a launch carrying the
+// shared expert's problem and the routed one, EPI_F32): every tile stores its
+// rows with device-coherent stores, counts each row's (token, 256-column tile)
+// once the stores have completed, and the workgroup that brings a token's
+// count to its number of producers -- the shared expert plus the token's picks
+// whose experts take this launch (more than gmax rows) -- computes
+//   out[t][c] = out[t][c] + sum_j w[t][j] * yg[rows[t][j]][c]
+// for the tile's columns, j in order from a zero accumulator by fmaf: the
+// bits of moe_weighted_row_sum.  counters[(t * n_ct + tile) * 16] must be zero
+// when the launch starts (the up launch zeroes them: zero_counters below).
+struct CombineArgs {
+  int on;
+  int32_t *counters;
+  const int32_t *ids, *rows, *row_token, *offsets;
+  const float *w;
+  const float *yg;  // [n*K][d], written by this launch and earlier ones
+  float *out;       // [n][d]: the shared expert's output, then the layer's
+  int n, K, d, gmax, n_ct;
+};
+// Columns of one tile of the f32-output GEMM (the combine's column tiles).
+constexpr int kGemmF32TileCols = 256;
+// zero_counters: words counters[16 i], i < n_zero, are zeroed by the launch
+// (grid-stride, before its tiles): the up launch prepares the down launch's
+// combine counters.
+hipError_t launch_dq_gemm(ProjProblem *probs, int count, int epi, hipStream_t stream,
+                          const CombineArgs *combine = nullptr, int32_t *zero_counters = nullptr,
+                          long n_zero = 0);
 
 // A whole decode step (n_tokens <= 2) in one persistent launch: routing, the
 // gather layout, the shared expert (up[0]/down[0], ignored unless has_shared)

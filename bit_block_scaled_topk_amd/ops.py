@@ -101,6 +101,7 @@ class LayerDesc(ctypes.Structure):
 
 
 MOE_LAYER_SINGLE_LAUNCH = 1
+MOE_LAYER_FUSED_COMBINE = 2
 PROFILE_EVENTS = 8  # events moe_layer_forward_profiled records per call
 
 
@@ -458,16 +459,19 @@ class MoELayer:
     at construction for n_tokens tokens, so a forward pass allocates nothing.
     ``single_launch`` sets MOE_LAYER_SINGLE_LAUNCH in the layer description:
     only for callers that run nothing else on the device during a step.
+    ``fused_combine`` sets MOE_LAYER_FUSED_COMBINE (WeightedRowSum inside the
+    prefill down projection).
     """
 
     def __init__(self, inp, device="cuda", gemv_max_rows: int = MAX_GEMV_ROWS, n_tokens: Optional[int] = None,
-                 single_launch: bool = False):
+                 single_launch: bool = False, fused_combine: bool = False):
         self.n = int(n_tokens if n_tokens is not None else inp.n)
         self.d, self.E, self.K, self.f, self.fs = inp.d, inp.E, inp.K, inp.f, inp.fs
         self.act = MOE_SWIGLU if inp.act == "swiglu" else MOE_RELU2
         self.x_dtype = MOE_F32 if inp.x_dtype == "f32" else MOE_BF16
         self.gemv_max_rows = gemv_max_rows
-        self.flags = MOE_LAYER_SINGLE_LAUNCH if single_launch else 0
+        self.flags = (MOE_LAYER_SINGLE_LAUNCH if single_launch else 0) | \
+            (MOE_LAYER_FUSED_COMBINE if fused_combine else 0)
         self.up = DeviceNVFP4.from_host(inp.up, device)
         self.down = DeviceNVFP4.from_host(inp.down, device)
         self.shared_up = DeviceNVFP4.from_host(inp.shared_up, device) if inp.fs > 0 else None
@@ -524,7 +528,7 @@ class MoELayer:
         if self.layer_ws is None or self.layer_ws.numel() < need:
             raise MoeError("moe_layer_forward", MOE_WORKSPACE_TOO_SMALL)
         out = moe_layer_forward(d, x, logits, self.out, self.layer_ws, stream=stream)
-        if check and self.flags and not torch.cuda.is_current_stream_capturing():
+        if check and (self.flags & MOE_LAYER_SINGLE_LAUNCH) and not torch.cuda.is_current_stream_capturing():
             self.check_wait_error(stream)
         return out
 

@@ -362,7 +362,7 @@ typedef struct {
   int gemv_max_rows;          /* 0..32, as in nvfp4_expert_ffn */
   moe_nvfp4_weights up, down; /* routed: [E][f or 2f][d], [E][d][f] */
   moe_nvfp4_weights shared_up, shared_down; /* [1][fs][d], [1][d][fs] */
-  int flags;                  /* 0, or MOE_LAYER_SINGLE_LAUNCH */
+  int flags;                  /* 0, or MOE_LAYER_SINGLE_LAUNCH | MOE_LAYER_FUSED_COMBINE */
 } moe_layer_desc;
 
 /* Allows the single-launch decode step (see moe_layer_forward).  Its
@@ -373,6 +373,17 @@ typedef struct {
  * kernels that never wait on each other, which is safe under any
  * concurrency. */
 #define MOE_LAYER_SINGLE_LAUNCH 1
+
+/* Runs WeightedRowSum inside the prefill down projection instead of as its own
+ * launch (gllm #91 "What changes": the combine onto the shared expert's
+ * output), for prefill steps with a shared expert: every down tile stores its
+ * rows device-coherently and counts them per (token, 256-column tile); the
+ * tile that completes a token's count sums that token's rows in slot order,
+ * with the same bits as moe_weighted_row_sum.  No workgroup waits on another,
+ * so it is safe under any concurrency.  It is measured slower than the
+ * separate launch on MI355X (each tile's epilogue then carries a chain of
+ * device-coherent atomics and loads), so it is opt-in. */
+#define MOE_LAYER_FUSED_COMBINE 2
 /* A description is invalid (MOE_INVALID_ARG; workspace size 0) when, with
  * n_tokens > gemv_max_rows, an activation matrix of the prefill GEMM (x as
  * n x d; h as n*K x f; the shared h as n x fs, all bf16) or one expert's codes

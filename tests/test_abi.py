@@ -275,8 +275,8 @@ def test_repacked_weights_are_both_or_neither_aligned_and_addressable(lib):
 
 
 def test_layer_description_flags_are_checked(lib):
-    """moe_layer_desc.flags takes only MOE_LAYER_SINGLE_LAUNCH; any other bit
-    makes the description invalid (size 0)."""
+    """moe_layer_desc.flags takes only MOE_LAYER_SINGLE_LAUNCH and
+    MOE_LAYER_FUSED_COMBINE; any other bit makes the description invalid."""
     _setup(lib)
     up, dn = W(FAKE, FAKE, FAKE, 128, 64), W(FAKE, FAKE, FAKE, 64, 128)
     none = W(None, None, None, 0, 0)
@@ -285,7 +285,9 @@ def test_layer_description_flags_are_checked(lib):
     assert base > 0
     d.flags = 1
     assert lib.moe_layer_workspace_size(ctypes.byref(d)) == base
-    d.flags = 2
+    d.flags = 3
+    assert lib.moe_layer_workspace_size(ctypes.byref(d)) == base
+    d.flags = 4
     assert lib.moe_layer_workspace_size(ctypes.byref(d)) == 0
 
 
@@ -302,7 +304,7 @@ def test_noalloc_refuses_descriptions_beyond_its_scratch(lib):
     d = Desc(4314, 2688, 128, 6, 1, 0, 32, up, dn, sup, sdn, 0)
     assert lib.moe_layer_workspace_size(ctypes.byref(d)) > 64 << 20
     assert lib.moe_layer_forward_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, None) == 2
-    d.flags = 4
+    d.flags = 8
     assert lib.moe_layer_forward_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, None) == 1
 
 

@@ -638,6 +638,10 @@ def test_layer_forward_fused(ops, name):
     assert int(host(v["decode_launch"])[0]) == (1 if single else 0)
     unfused = layer.forward(x, lg).clone()
     torch.cuda.synchronize()
+    if name == "prefill4314":  # and with the combine fused into the down GEMM
+        layer.flags |= ops.MOE_LAYER_FUSED_COMBINE
+        assert torch.equal(layer.forward_fused(x, lg), unfused)
+        layer.flags &= ~ops.MOE_LAYER_FUSED_COMBINE
     if single:  # fp32 dot products on the vector ALUs: equal to fp32 rounding
         assert normwise(host(fused).astype(np.float64), host(unfused).astype(np.float64)) <= 2e-6
     else:
@@ -888,3 +892,47 @@ def test_router_topk_edge_cases(ops):
     ids, w, _ = ops.moe_router_topk(torch.empty((0, 64), dtype=torch.int16, device=DEV),
                                     dev(np.zeros((8, 64), dtype=np.uint16)), 2, ws)
     assert ids.shape == (0, 2)
+
+
+# ----------------------------------------------------------------------------
+# WeightedRowSum fused into the prefill down projection
+# ----------------------------------------------------------------------------
+
+FUSED_COMBINE_CASES = [
+    # a skewed router: experts on both paths (some at most 32 rows, on the
+    # decode GEMV, whose rows the GEMM's combine reads but does not count)
+    ("tiny16", dict(n=100, logits="zipf", seed=31)),
+    # every expert on the GEMM; one and several 128-row m-tiles per expert
+    ("tiny16", dict(n=512, seed=32)),
+    # the workload's widths: 11 column tiles of 256 (the last one of 128)
+    ("decode1", dict(n=200, E=16, seed=33)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(FUSED_COMBINE_CASES)))
+def test_fused_combine_equals_the_separate_weighted_row_sum(ops, case):
+    """With MOE_LAYER_FUSED_COMBINE and a shared expert, a prefill step's
+    WeightedRowSum runs in the down
+    GEMM's epilogue (the last producer of a token's column tile sums its rows
+    in slot order): the output equals the four calls' (separate
+    moe_weighted_row_sum launch) bit for bit, twice in a row (the counters are
+    prepared by the up launch each call), and matches the oracle."""
+    name, ov = FUSED_COMBINE_CASES[case]
+    inp = cached_layer(name, **ov)
+    print(f"fused combine case {name} {ov}", flush=True)
+    layer = ops.MoELayer(inp, fused_combine=True)
+    x, lg = dev(inp.x), dev(inp.logits)
+    unfused = layer.forward(x, lg).clone()
+    yg_unfused = layer.yg.clone()
+    a = layer.forward_fused(x, lg).clone()
+    b = layer.forward_fused(x, lg).clone()
+    v = layer.views()
+    torch.cuda.synchronize()
+    counts = np.diff(host(v["offsets"]))
+    assert counts.max() > 32
+    assert torch.equal(a, unfused) and torch.equal(b, unfused)
+    R = inp.n * inp.K
+    assert torch.equal(v["yg"][:R], yg_unfused[:R])
+    ref = oracle.layer(inp)
+    assert normwise(host(a).astype(np.float64), ref["out"]) <= TOL_PREFILL
+    assert normwise(host(a).astype(np.float64), oracle.layer(inp, bf16_act=True)["out"]) <= 2e-3
