@@ -24,6 +24,10 @@ Fields beyond the contract:
                 counters read for a plain copy), taken from profiles/ only
                 while the kernel's sources are the ones that were counted.
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
+  router        the router step fused with routing (moe_router_topk: logits
+                x . W_r^T on the matrix cores, top-K, softmax) at 4314 and at 1
+                token, median of 50 event-timed calls, next to moe_route_topk
+                on given logits
   decode        the three decode workloads (1 token; 32 tokens with a skewed
                 router; 2 tokens with SwiGLU experts), each timed as the median
                 of --decode-replays replays of a HIP graph of 16 steps that
@@ -59,6 +63,7 @@ def parse():
     p.add_argument("--decode", default="decode1,decode32_zipf,gated2",
                    help="decode workloads benchmarked beside the main line ('' for none)")
     p.add_argument("--decode-replays", type=int, default=50)
+    p.add_argument("--no-router", action="store_true")
     p.add_argument("--copies", type=int, default=N_COPIES)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
@@ -369,6 +374,46 @@ def bench_decode(name, args, ops, synth):
     return out
 
 
+def bench_router(ops, synth, reps=50):
+    """Median event time of moe_router_topk (and of moe_route_topk on the same
+    logits) for the prefill and the batch-1 decode workloads."""
+    import numpy as np
+    import torch
+
+    out = {}
+    for name in ("prefill4314", "decode1"):
+        cfg = synth.WORKLOADS[name]
+        x = synth.draw_activations(name)
+        x = torch.from_numpy(np.ascontiguousarray(x.view(np.int16) if x.dtype == np.uint16 else x)).to("cuda:0")
+        wr = torch.from_numpy(synth.draw_router(name).view(np.int16)).to("cuda:0")
+        n, E, K, d = cfg["n"], cfg["E"], cfg["K"], cfg["d"]
+        ws = torch.empty((ops.moe_router_workspace_size(n, E),), dtype=torch.uint8, device="cuda:0")
+        ops.moe_router_workspace_init(ws, n)
+        logits = torch.empty((n, E), dtype=torch.float32, device="cuda:0")
+        ids = torch.empty((n, K), dtype=torch.int32, device="cuda:0")
+        w = torch.empty((n, K), dtype=torch.float32, device="cuda:0")
+        times = {"router_topk": [], "route_topk": []}
+        for _ in range(5):
+            ops.moe_router_topk(x, wr, K, ws, ids, w, logits)
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            for key, fn in (("router_topk", lambda: ops.moe_router_topk(x, wr, K, ws, ids, w, logits)),
+                            ("route_topk", lambda: ops.moe_route_topk(logits, K, ids, w))):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                times[key].append((a, b))
+        torch.cuda.synchronize()
+        med = {k: round(median([a.elapsed_time(b) * 1e3 for a, b in v]), 2) for k, v in times.items()}
+        flops = 2 * n * E * d
+        out[name] = {"tokens": n, "experts": E, "top_k": K, "d_model": d, "router_weights": "bf16",
+                     "us_router_topk_median": med["router_topk"], "us_route_topk_only_median": med["route_topk"],
+                     "router_gemm_tflops": round(flops / (med["router_topk"] * 1e-6) / 1e12, 2),
+                     "router_weight_gbs": round(E * d * 2 / (med["router_topk"] * 1e-6) / 1e9, 1)}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -389,6 +434,10 @@ def main():
     for name in [w for w in args.decode.split(",") if w]:
         log(f"decode workload {name}")
         decode[name] = bench_decode(name, args, ops, synth)
+    router = None
+    if not args.no_router:
+        log("router")
+        router = bench_router(ops, synth)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline")
@@ -418,6 +467,7 @@ def main():
         "step_breakdown_us_median": phases,
         "input_gen_s": round(gen_s, 1),
         "decode": decode,
+        "router": router,
     }
     print(json.dumps(line))
 

@@ -9,7 +9,8 @@
 // 32-element k-group g = g0 + 4*i + q of that column's weight row: one 16-byte
 // code load plus two scale bytes.  A chunk's weight loads are all issued before
 // any is used, so each lane keeps kNI k-groups in flight.  The 32 codes become
-// 4 bf16x8 B operands (exact: e2m1 * e4m3 has <= 6 significant bits) and feed 4
+// 4 bf16x8 B operands (exact: a code's value times its block scale fits a bf16
+// significand) and feed 4
 // MFMA 16x16x32 steps; the A operand holds the same 32 k-values of up to 16
 // activation rows, so the MFMA sums the dot product over the group.  The A
 // operands of a k-group are loaded once and used for all CT tiles: with one

@@ -1,7 +1,7 @@
-// gather.hip -- the MoE gather: each (token, picked expert) pair gets one row of
-// packed n*topK-row buffers grouped by expert, and the activations are copied
-// into those rows (gllm PR #91, "What changes": one Embedding gathers the
-// inputs).  Rows inside an expert's group are in ascending token order.
+// gather.hip -- the MoE gather (gllm PR #91, "What changes"): a dense buffer of
+// n*topK rows holds one row per (token, picked expert) pair, the rows of each
+// expert contiguous, and the activations are copied into them with a single
+// row lookup.  Rows inside an expert's group are in ascending token order.
 //
 // Layout without order-dependent atomics: a bitmap bit[e][t] marks that token t
 // picked expert e (atomicOr: the result does not depend on the order), prefix

@@ -4,8 +4,9 @@
 // NVFP4 (as used by the gllm PR "perf: gather tokens per MoE expert, run large
 // NVFP4 GEMMs on bf16 tensor cores #91", section "bf16 NVFP4 GEMM (CUDA)"):
 // 4-bit e2m1 codes, one e4m3 scale per 16 consecutive elements of a row, one
-// fp32 global per tensor.  code * scale has at most 6 significant bits, so it
-// is exact in bf16; the global is applied once, after the dot product.
+// fp32 global per tensor.  A code (2 significant bits) times a scale (4) is
+// representable in bf16 (8), so the unpack is exact; the global is applied
+// once, after the dot product.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -45,8 +46,8 @@ __device__ __forceinline__ void e4m3x2_to_f32(uint32_t two, float &s0, float &s1
 // Decode 8 codes (one 32-bit word, element 0 in the low nibble of byte 0) into
 // 8 bf16 values scale * e2m1, packed as 4 x (even element in the low half).
 // The FP4 converter (unit scale) gives exact e2m1 values; every product with
-// the e4m3 scale is exact in f32 and in bf16 (<= 6 significant bits, inside the
-// normal range), so the upper 16 bits of the f32 are the exact bf16.
+// the e4m3 scale is exact in f32 and in bf16 (2 + 4 significant bits, inside
+// the normal range), so the upper 16 bits of the f32 are the exact bf16.
 __device__ __forceinline__ u32x4_t dq8_bf16(uint32_t w, float scale) {
   u32x4_t r;
 #pragma unroll

@@ -1,6 +1,7 @@
 // unpack.hip -- exact NVFP4 -> bf16 unpack that drops the per-tensor global
-// (gllm PR #91, "bf16 NVFP4 GEMM (CUDA)": e2m1 code times e4m3 block scale has
-// at most 6 significant bits, so it is exact in bf16).  One thread per 32-element
+// (gllm PR #91, "bf16 NVFP4 GEMM (CUDA)"): the e2m1 magnitudes carry 2
+// significant bits and an e4m3 scale 4, so their product needs 6 and bf16's 8
+// hold it without rounding.  One thread per 32-element
 // group: a 16-byte code load, two scale bytes, 64 bytes of bf16 out.
 #include "launch.hpp"
 #include "nvfp4_device.hpp"

@@ -201,9 +201,9 @@ moe_status moe_router_topk(const void *x, moe_dtype x_dtype, int n_tokens, int d
  * arguments). */
 size_t moe_gather_workspace_size(int n_tokens, int n_experts);
 
-/* moe_gather_rows -- the MoE gather (gllm #91 "What changes": each (token,
- * picked expert) pair gets a row in packed buffers of n x topK rows, grouped by
- * expert; one Embedding gathers the inputs).
+/* moe_gather_rows -- the MoE gather (gllm #91 "What changes"): n x topK rows,
+ * one per (token, picked expert) pair, each expert's rows contiguous, filled by
+ * a single row lookup of the inputs.
  *   x               device [n_tokens][d_model] of x_dtype (F32 or BF16)
  *   topk_ids        device int32 [n_tokens][top_k], expert ids (each token
  *                   should pick an expert at most once)
@@ -240,8 +240,8 @@ size_t nvfp4_expert_ffn_workspace_size(int n_rows, int d_model, int d_ff, moe_dt
 /* Workspace bytes nvfp4_grouped_linear needs (fp32 activations only; 0 for bf16). */
 size_t nvfp4_grouped_linear_workspace_size(int n_rows, int k, moe_dtype a_dtype);
 
-/* nvfp4_expert_ffn -- each expert's FFN over its own rows (gllm #91 "What
- * changes": up -> relu^2 -> down over only its own rows; Glq v0.2.13 "v3b":
+/* nvfp4_expert_ffn -- each expert's FFN over the rows routed to it (gllm #91
+ * "What changes": up -> relu^2 -> down per expert; Glq v0.2.13 "v3b":
  * relu^2 for non-gated NemotronH; the gated experts' fused gate-up projection
  * of TensorFold issue #2265 "What ncu shows").
  *   xg              device [n_rows][up->cols] activations of act_dtype
@@ -321,8 +321,8 @@ moe_status moe_error_word_clear(int32_t *word, hipStream_t stream);
 moe_status moe_error_word_read(const int32_t *word, int32_t *value, hipStream_t stream);
 
 /* nvfp4_unpack_bf16 -- exact unpack of NVFP4 codes and scales to bf16 without
- * the per-tensor global (gllm #91 "bf16 NVFP4 GEMM (CUDA)": an e2m1 code times
- * an e4m3 block scale has at most 6 significant bits, so it is exact in bf16).
+ * the per-tensor global (gllm #91 "bf16 NVFP4 GEMM (CUDA)"): a code's value
+ * (2 significant bits) times its e4m3 scale (4) always fits bf16's 8.
  *   codes   device uint8 [rows][cols/2]; scales device uint8 [rows][cols/16]
  *   out     device uint16 (bf16 bits) [rows][cols] = e4m3(scale) * e2m1(code)
  * A NaN scale byte gives bf16 NaN for its 16 elements. */

@@ -197,8 +197,8 @@ int orc_router_logits(const double *x, int n, int d, const double *wr, int E, do
 /* Gather                                                                     */
 /* ------------------------------------------------------------------------- */
 
-/* [gllm#91] "What changes": each (token, picked expert) pair gets one row in
- * packed buffers of n*topK rows grouped by expert.  count_e -> exclusive offsets;
+/* [gllm#91] "What changes": n*topK rows, one per (token, picked expert) pair,
+ * the rows of each expert contiguous.  count_e -> exclusive offsets;
  * then walking tokens in ascending order (and slots j ascending), the pick
  * (t, j) of expert e gets row off_e + (number of earlier picks of e).
  * rows[t*K + j] = that row, row_token[row] = t.  An expert id outside [0, E)
@@ -225,8 +225,8 @@ int orc_gather_layout(const int32_t *ids, int n, int K, int E, int32_t *offsets,
   return ORC_OK;
 }
 
-/* [gllm#91] "What changes": one Embedding gathers the inputs, i.e. a row
- * lookup xg[r] = x[row_token[r]], copied bit for bit. */
+/* [gllm#91] "What changes": the inputs are gathered by a single row lookup,
+ * xg[r] = x[row_token[r]], copied bit for bit. */
 int orc_gather_copy(const void *x, int elem_bytes, int n, int d, const int32_t *row_token,
                     int R, void *xg) {
   size_t row_bytes = (size_t)elem_bytes * (size_t)d;
@@ -315,7 +315,8 @@ static void orc_deq_rows(void *p, long i0, long i1) {
 }
 
 /* Expert FFN over packed rows grouped by expert ([gllm#91] "What changes":
- * each picked expert runs up -> relu^2 -> down over only its own rows).
+ * an expert's up -> relu^2 -> down touches the rows routed to it and no
+ * others).
  *   x       [n_rows, d] in double; rows [offsets[e], offsets[e+1]) belong to e
  *   up      codes [E][up_rows][d/2], scales [E][up_rows][d/16], globals [E]
  *           up_rows = f (relu^2) or 2f (swiglu)
@@ -428,7 +429,7 @@ int orc_weighted_row_sum(double *dst, const double *src, int n_src, const int32_
 
 /* The workload describes its CPU reference as fp32 accumulation in a fixed
  * order.  These functions are that evaluation, written out step by step:
- *   q = e4m3(scale) * e2m1(code)      exact in binary32 (at most 6 significant
+ *   q = e4m3(scale) * e2m1(code)      exact in binary32 (2 + 4 significant
  *                                     bits, [gllm#91] "bf16 NVFP4 GEMM (CUDA)")
  *   F(a, b): acc = 0; for k ascending: acc = fmaf(a_k, b_k, acc)
  *   projection  out = global * F(a_row, q_row)   (the global applied once,

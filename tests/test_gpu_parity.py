@@ -583,7 +583,8 @@ def test_layer_is_deterministic_and_stream_independent(ops):
 
 def test_expert_ffn_writes_only_its_rows(ops):
     """A canary-filled output: the FFN writes rows [0, offsets[E]) and nothing
-    else (gllm #91 "Testing": a MatMul into a slice lands in exactly those rows)."""
+    else (gllm #91 "Testing": a product written into a row range of a larger
+    buffer must change those rows and no others)."""
     inp = cached_layer("tiny16")
     counts = np.array([3, 0, 9, 1, 0, 4, 2, 1], dtype=np.int64)
     off = _offsets(counts)

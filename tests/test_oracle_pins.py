@@ -54,8 +54,8 @@ def test_e2m1_table_matches_bit_fields(oracle_lib):
 
 
 def test_every_e2m1_times_e4m3_is_exact_in_bf16(oracle_lib):
-    """PIN (gllm #91, "bf16 NVFP4 GEMM (CUDA)"): an e2m1 code times an e4m3 block
-    scale has at most 6 significant bits, so it is exact in bf16.  Checked over
+    """PIN (gllm #91, "bf16 NVFP4 GEMM (CUDA)"): the product of an e2m1 value and
+    an e4m3 scale is representable in bf16, so the unpack loses nothing.  Checked over
     all 16 x 254 finite products with torch's own float64 -> bfloat16 cast."""
     prods = []
     for c in range(16):
@@ -71,7 +71,7 @@ def test_every_e2m1_times_e4m3_is_exact_in_bf16(oracle_lib):
     nz = p[p != 0]
     mant, _ = np.frexp(np.abs(nz))
     sig = mant * 2.0 ** 6
-    assert np.all(sig == np.round(sig))  # at most 6 significant bits
+    assert np.all(sig == np.round(sig))  # no more than 6 significant bits
 
 
 def test_round_bf16_matches_torch(oracle_lib):
