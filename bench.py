@@ -26,8 +26,8 @@ Fields beyond the contract:
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
   router        the router step fused with routing (moe_router_topk: logits
                 x . W_r^T on the matrix cores, top-K, softmax) at 4314 and at 1
-                token, median of 50 event-timed calls, next to moe_route_topk
-                on given logits
+                token (graph replays of 20 calls, so host launch latency is
+                not counted), next to moe_route_topk on given logits
   decode        the three decode workloads (1 token; 32 tokens with a skewed
                 router; 2 tokens with SwiGLU experts), each timed as the median
                 of --decode-replays replays of a HIP graph of 16 steps that
@@ -374,9 +374,11 @@ def bench_decode(name, args, ops, synth):
     return out
 
 
-def bench_router(ops, synth, reps=50):
-    """Median event time of moe_router_topk (and of moe_route_topk on the same
-    logits) for the prefill and the batch-1 decode workloads."""
+def bench_router(ops, synth, reps=10, per_graph=20):
+    """GPU time of moe_router_topk (and of moe_route_topk on the same logits)
+    for the prefill and the batch-1 decode workloads: each call captured
+    per_graph times into a HIP graph, the median replay time over `reps`
+    replays divided by per_graph (so host launch latency is not counted)."""
     import numpy as np
     import torch
 
@@ -392,25 +394,34 @@ def bench_router(ops, synth, reps=50):
         logits = torch.empty((n, E), dtype=torch.float32, device="cuda:0")
         ids = torch.empty((n, K), dtype=torch.int32, device="cuda:0")
         w = torch.empty((n, K), dtype=torch.float32, device="cuda:0")
-        times = {"router_topk": [], "route_topk": []}
-        for _ in range(5):
-            ops.moe_router_topk(x, wr, K, ws, ids, w, logits)
-        torch.cuda.synchronize()
-        for _ in range(reps):
-            for key, fn in (("router_topk", lambda: ops.moe_router_topk(x, wr, K, ws, ids, w, logits)),
-                            ("route_topk", lambda: ops.moe_route_topk(logits, K, ids, w))):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                fn()
-                b.record()
-                times[key].append((a, b))
-        torch.cuda.synchronize()
-        med = {k: round(median([a.elapsed_time(b) * 1e3 for a, b in v]), 2) for k, v in times.items()}
+        stream = torch.cuda.Stream()
+        med = {}
+        for key, fn in (("router_topk", lambda: ops.moe_router_topk(x, wr, K, ws, ids, w, logits, stream=stream)),
+                        ("route_topk", lambda: ops.moe_route_topk(logits, K, ids, w, stream=stream))):
+            with torch.cuda.stream(stream):
+                for _ in range(3):
+                    fn()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for _ in range(per_graph):
+                    fn()
+            g.replay()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            with torch.cuda.stream(stream):
+                for a, b in ev:
+                    a.record(stream)
+                    g.replay()
+                    b.record(stream)
+            torch.cuda.synchronize()
+            med[key] = round(median([a.elapsed_time(b) * 1e3 for a, b in ev]) / per_graph, 2)
         flops = 2 * n * E * d
         out[name] = {"tokens": n, "experts": E, "top_k": K, "d_model": d, "router_weights": "bf16",
                      "us_router_topk_median": med["router_topk"], "us_route_topk_only_median": med["route_topk"],
                      "router_gemm_tflops": round(flops / (med["router_topk"] * 1e-6) / 1e12, 2),
-                     "router_weight_gbs": round(E * d * 2 / (med["router_topk"] * 1e-6) / 1e9, 1)}
+                     "router_weight_gbs": round(E * d * 2 / (med["router_topk"] * 1e-6) / 1e9, 1),
+                     "timing": f"median of {reps} replays of a graph of {per_graph} calls"}
     return out
 
 

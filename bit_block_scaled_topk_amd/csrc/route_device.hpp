@@ -64,20 +64,17 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
   return k;
 }
 
-// COH: the logits were written by other workgroups of the same launch with
-// device-coherent stores; read them with device-coherent loads (past the
-// per-XCD L2).
-template <int PER_LANE, bool COH = false>
-__device__ __forceinline__ void route_one_token(const float *__restrict__ row, int n_experts, int top_k, int lane,
-                                                int &my_id, float &my_w) {
+// Top-K and softmax from logits already in registers: lane keeps v[i], the
+// logit of expert lane + 64 i (entries for experts >= n_experts are ignored).
+// PER_LANE may exceed what n_experts needs (the extra entries are not used).
+template <int PER_LANE>
+__device__ __forceinline__ void route_one_token_keys(const float (&v)[PER_LANE], int n_experts, int top_k, int lane,
+                                                     int &my_id, float &my_w) {
   uint64_t key[PER_LANE];
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) {
-    const int e = lane + i * 64;  // coalesced: consecutive lanes read consecutive experts
-    float v = 0.0f;
-    if (e < n_experts)
-      v = COH ? __hip_atomic_load(row + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : row[e];
-    key[i] = (e < n_experts) ? route_key(v, e) : 0ull;
+    const int e = lane + i * 64;
+    key[i] = (e < n_experts) ? route_key(v[i], e) : 0ull;
   }
   float my_logit = 0.0f;
   my_id = 0;
@@ -101,16 +98,27 @@ __device__ __forceinline__ void route_one_token(const float *__restrict__ row, i
   my_w = ex / sum;
 }
 
+template <int PER_LANE>
+__device__ __forceinline__ void route_one_token(const float *__restrict__ row, int n_experts, int top_k, int lane,
+                                                int &my_id, float &my_w) {
+  float v[PER_LANE];
+#pragma unroll
+  for (int i = 0; i < PER_LANE; ++i) {
+    const int e = lane + i * 64;  // coalesced: consecutive lanes read consecutive experts
+    v[i] = (e < n_experts) ? row[e] : 0.0f;
+  }
+  route_one_token_keys<PER_LANE>(v, n_experts, top_k, lane, my_id, my_w);
+}
+
 // Dispatch on the number of logits per lane.
-template <bool COH = false>
 __device__ __forceinline__ void route_one_token_any(const float *__restrict__ row, int n_experts, int top_k,
                                                     int lane, int &my_id, float &my_w) {
   if (n_experts <= 128)
-    route_one_token<2, COH>(row, n_experts, top_k, lane, my_id, my_w);
+    route_one_token<2>(row, n_experts, top_k, lane, my_id, my_w);
   else if (n_experts <= 256)
-    route_one_token<4, COH>(row, n_experts, top_k, lane, my_id, my_w);
+    route_one_token<4>(row, n_experts, top_k, lane, my_id, my_w);
   else
-    route_one_token<MOE_MAX_EXPERTS / 64, COH>(row, n_experts, top_k, lane, my_id, my_w);
+    route_one_token<MOE_MAX_EXPERTS / 64>(row, n_experts, top_k, lane, my_id, my_w);
 }
 
 }  // namespace moe

@@ -889,6 +889,12 @@ def test_router_topk_edge_cases(ops):
     assert np.array_equal(ids, np.tile(np.arange(4, dtype=np.int32), (9, 1)))
     xf = rng.standard_normal((20, 4096)).astype(np.float32)
     _router_case(ops, xf, "f32", bf(rng.standard_normal((64, 4096)) * 0.02), 6)
+    # many token tiles: 128-expert groups per workgroup, routed in place (up to
+    # 128 experts, bf16 and fp32 x) or through the counters (256 experts)
+    _router_case(ops, bf(rng.standard_normal((600, 256))), "bf16", bf(rng.standard_normal((128, 256)) * 0.06), 6)
+    _router_case(ops, bf(rng.standard_normal((700, 128))), "bf16", bf(rng.standard_normal((256, 128)) * 0.09), 8)
+    xf = rng.standard_normal((2100, 96)).astype(np.float32)
+    _router_case(ops, xf, "f32", bf(rng.standard_normal((64, 96)) * 0.1), 4)
     ws = router_ws(ops, 0, 8)
     ids, w, _ = ops.moe_router_topk(torch.empty((0, 64), dtype=torch.int16, device=DEV),
                                     dev(np.zeros((8, 64), dtype=np.uint16)), 2, ws)
