@@ -48,10 +48,20 @@ bool packed_ok(const moe_nvfp4_weights *w) {
   return packed_codes_bytes(1, w->rows, w->cols) < (1L << 31);
 }
 
+// A projection is given by its canonical codes and scales, its repacked
+// copies, or both.  Without the canonical layout every kernel that reads the
+// weights must take the repacked one: whole 16-row blocks (the prefill GEMM's
+// condition; SwiGLU also needs the up half block-aligned, see swiglu_ok).
 bool weights_ok(const moe_nvfp4_weights *w) {
-  return w && w->codes && w->scales && w->global && w->rows > 0 && w->cols > 0 && aligned(w->codes, 16) &&
-         aligned(w->scales, 2) && aligned(w->global, 4) && packed_ok(w);
+  if (!w || !w->global || w->rows <= 0 || w->cols <= 0 || !aligned(w->global, 4) || !packed_ok(w)) return false;
+  if (!w->codes != !w->scales) return false;  // both canonical arrays or neither
+  if (w->codes) return aligned(w->codes, 16) && aligned(w->scales, 2);
+  return w->codes_packed != nullptr && w->rows % 16 == 0;
 }
+
+// SwiGLU's up projection holds 2f rows: without the canonical layout its gate
+// and up halves must each be whole 16-row blocks.
+bool swiglu_ok(const moe_nvfp4_weights *up) { return up->codes != nullptr || up->rows % 32 == 0; }
 
 // Every workspace of nvfp4_expert_ffn and moe_gather_rows starts with 256
 // bytes reserved for its error word (the int32 at offset 0).
@@ -301,6 +311,7 @@ moe_status nvfp4_expert_ffn(const void *xg, moe_dtype act_dtype, int n_rows, int
   if (n_experts > MOE_MAX_EXPERTS) return MOE_UNSUPPORTED;
   if (gemv_max_rows < 0 || gemv_max_rows > MOE_MAX_GEMV_ROWS) return MOE_UNSUPPORTED;
   if (!weights_ok(up) || !weights_ok(down)) return MOE_INVALID_ARG;
+  if (act == MOE_SWIGLU && !swiglu_ok(up)) return MOE_INVALID_ARG;
   const int d = up->cols, f = down->cols, d_out = down->rows;
   if (up->rows != (act == MOE_SWIGLU ? 2 * f : f)) return MOE_INVALID_ARG;
   if (d % 32 != 0 || f % 32 != 0) return MOE_UNSUPPORTED;
@@ -424,11 +435,12 @@ bool plan_layer(const moe_layer_desc *dsc, LayerPlan *pl) {
   if (dsc->gemv_max_rows < 0 || dsc->gemv_max_rows > MOE_MAX_GEMV_ROWS) return false;
   if (dsc->flags & ~(MOE_LAYER_SINGLE_LAUNCH | MOE_LAYER_FUSED_COMBINE)) return false;
   if (!weights_ok(&dsc->up) || !weights_ok(&dsc->down)) return false;
+  if (dsc->act == MOE_SWIGLU && !swiglu_ok(&dsc->up)) return false;
   p.f = dsc->down.cols;
   if (dsc->up.cols != p.d || dsc->down.rows != p.d) return false;
   if (dsc->up.rows != (dsc->act == MOE_SWIGLU ? 2 * p.f : p.f)) return false;
   if (p.d % 32 || p.f % 32) return false;
-  p.has_shared = dsc->shared_up.codes != nullptr;
+  p.has_shared = dsc->shared_up.codes != nullptr || dsc->shared_up.codes_packed != nullptr;
   p.fs = 0;
   if (p.has_shared) {
     if (!weights_ok(&dsc->shared_up) || !weights_ok(&dsc->shared_down)) return false;

@@ -548,6 +548,8 @@ hipError_t launch_dq_gemm(ProjProblem *probs, int count, int epi, hipStream_t st
   bool pc = pk;
   for (int i = 0; i < b.count; ++i) pc = pc && b.p[i].codes_packed != nullptr;
   const int sm = pc ? 3 : pk ? 2 : sp ? 1 : 0;
+  for (int i = 0; i < b.count; ++i)  // modes 0-2 read the canonical codes (and 0-1 the canonical scales)
+    if (sm != 3 && (!b.p[i].codes || (sm < 2 && !b.p[i].scales))) return hipErrorInvalidValue;
   dim3 grid((unsigned)total), block(256);
   switch (epi * 4 + sm) {
 #define MOE_GEMM_CASE(E, M) \

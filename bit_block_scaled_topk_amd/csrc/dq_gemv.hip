@@ -326,6 +326,8 @@ hipError_t dispatch_epi(const GemvBatch &b, int epi, dim3 grid, hipStream_t s) {
   dim3 block(64 * WAVES);
   bool pk = true;  // every problem carries both repacked copies
   for (int i = 0; i < b.count; ++i) pk = pk && b.p[i].codes_packed && b.p[i].scales_packed;
+  for (int i = 0; i < b.count; ++i)  // the canonical layout is read otherwise
+    if (!pk && (!b.p[i].codes || !b.p[i].scales)) return hipErrorInvalidValue;
   switch (epi * 2 + (pk ? 1 : 0)) {
     case EPI_F32 * 2: hipLaunchKernelGGL((k_dq_gemv<WAVES, MT, NT, EPI_F32, kCT, false>), grid, block, 0, s, b); break;
     case EPI_F32 * 2 + 1: hipLaunchKernelGGL((k_dq_gemv<WAVES, MT, NT, EPI_F32, kCT, true>), grid, block, 0, s, b); break;

@@ -938,6 +938,12 @@ hipError_t launch_decode_layer(const DecodeLayerProblem &lp, hipStream_t stream)
   const bool swiglu = lp.act == EPI_SWIGLU;
   // the shared expert is relu^2: with a gated routed FFN it keeps its own launches
   if (!decode_layer_takes(n, lp.top_k, d) || (swiglu && lp.has_shared) || d % 32 != 0) return hipErrorNotSupported;
+  // it reads the canonical layout: weights given only as repacked copies take
+  // the per-step launches
+  for (int i = 0; i < 2; ++i) {
+    if (i == 0 && !lp.has_shared) continue;
+    if (!lp.up[i].codes || !lp.up[i].scales || !lp.down[i].codes || !lp.down[i].scales) return hipErrorNotSupported;
+  }
   if (lp.n_experts < lp.top_k || lp.n_experts > MOE_MAX_EXPERTS || lp.n_rows != n * lp.top_k)
     return hipErrorNotSupported;
   if (lp.max_slots != (lp.n_experts < lp.n_rows ? lp.n_experts : lp.n_rows)) return hipErrorNotSupported;

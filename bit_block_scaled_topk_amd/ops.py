@@ -163,9 +163,10 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 @dataclass
 class DeviceNVFP4:
-    """One NVFP4 projection for E experts resident on the device."""
-    codes: torch.Tensor    # uint8 [E, rows, cols/2]
-    scales: torch.Tensor   # uint8 [E, rows, cols/16]
+    """One NVFP4 projection for E experts resident on the device: the canonical
+    codes and scales, the repacked copies, or both (see drop_canonical)."""
+    codes: Optional[torch.Tensor]    # uint8 [E, rows, cols/2]
+    scales: Optional[torch.Tensor]   # uint8 [E, rows, cols/16]
     globals_: torch.Tensor  # float32 [E]
     rows: int
     cols: int
@@ -178,7 +179,8 @@ class DeviceNVFP4:
                    torch.from_numpy(t.globals_).to(device), int(t.rows), int(t.cols))
 
     def struct(self) -> NVFP4Weights:
-        return NVFP4Weights(self.codes.data_ptr(), self.scales.data_ptr(), self.globals_.data_ptr(),
+        return NVFP4Weights(None if self.codes is None else self.codes.data_ptr(),
+                            None if self.scales is None else self.scales.data_ptr(), self.globals_.data_ptr(),
                             self.rows, self.cols,
                             None if self.scales_packed is None else self.scales_packed.data_ptr(),
                             None if self.codes_packed is None else self.codes_packed.data_ptr())
@@ -190,9 +192,18 @@ class DeviceNVFP4:
         self.codes_packed = nvfp4_pack_codes(self, stream=stream)
         return self
 
+    def drop_canonical(self) -> "DeviceNVFP4":
+        """Free the canonical codes and scales once the repacked copies exist:
+        one copy of the weights stays on the device.  Returns self."""
+        if self.codes_packed is None or self.scales_packed is None:
+            raise ValueError("pack() first: the repacked copies are the only copy left")
+        self.codes = None
+        self.scales = None
+        return self
+
     @property
     def n_experts(self) -> int:
-        return int(self.codes.shape[0])
+        return int(self.globals_.shape[0])
 
 
 # ----------------------------------------------------------------------------
@@ -460,11 +471,14 @@ class MoELayer:
     ``single_launch`` sets MOE_LAYER_SINGLE_LAUNCH in the layer description:
     only for callers that run nothing else on the device during a step.
     ``fused_combine`` sets MOE_LAYER_FUSED_COMBINE (WeightedRowSum inside the
-    prefill down projection).
+    prefill down projection).  The weights are repacked once when the layer is
+    built; the canonical copy is kept only when ``keep_canonical`` (by default:
+    with ``single_launch``, whose kernel reads it), so otherwise one copy of
+    the weights stays on the device.
     """
 
     def __init__(self, inp, device="cuda", gemv_max_rows: int = MAX_GEMV_ROWS, n_tokens: Optional[int] = None,
-                 single_launch: bool = False, fused_combine: bool = False):
+                 single_launch: bool = False, fused_combine: bool = False, keep_canonical: Optional[bool] = None):
         self.n = int(n_tokens if n_tokens is not None else inp.n)
         self.d, self.E, self.K, self.f, self.fs = inp.d, inp.E, inp.K, inp.f, inp.fs
         self.act = MOE_SWIGLU if inp.act == "swiglu" else MOE_RELU2
@@ -476,9 +490,12 @@ class MoELayer:
         self.down = DeviceNVFP4.from_host(inp.down, device)
         self.shared_up = DeviceNVFP4.from_host(inp.shared_up, device) if inp.fs > 0 else None
         self.shared_down = DeviceNVFP4.from_host(inp.shared_down, device) if inp.fs > 0 else None
+        keep = single_launch if keep_canonical is None else keep_canonical
         for w in self.weights():
             if w is not None:
                 w.pack()  # the one-time repack the prefill GEMM and the decode GEMV read
+                if not keep:
+                    w.drop_canonical()
         self.device = device
         self.layer_ws = None
         self._alloc(self.n)

@@ -81,8 +81,12 @@ typedef int moe_act;
 #define MOE_MAX_TOPK 32
 #define MOE_MAX_GEMV_ROWS 32
 
-/* One NVFP4 projection for n_experts experts; all three pointers are device
- * pointers laid out as described in the file header. */
+/* One NVFP4 projection for n_experts experts; all pointers are device
+ * pointers laid out as described in the file header.  codes and scales (the
+ * canonical layout) may both be NULL when the repacked copies below are given
+ * and rows is a multiple of 16 (32 for a SwiGLU up projection): every kernel
+ * then reads the repacked copies, and the single-launch decode step falls back
+ * to the per-step launches.  So a caller keeps one copy of the weights. */
 typedef struct {
   const uint8_t *codes;
   const uint8_t *scales;
@@ -94,8 +98,9 @@ typedef struct {
    * the same weights as `codes` / `scales`.  When both are present the decode
    * GEMV reads them, and so does the prefill GEMM when rows is a multiple of
    * 16 (SwiGLU: f too); the single-launch decode step and the standalone
-   * unpack read the canonical layout.  With them, one expert's repacked codes
-   * (ceil(rows/16) * ceil(cols/128) KB) must stay under 2 GiB. */
+   * unpack read the canonical layout (when it is given).  With them, one
+   * expert's repacked codes (ceil(rows/16) * ceil(cols/128) KB) must stay
+   * under 2 GiB. */
   const uint8_t *scales_packed;
   const uint8_t *codes_packed;
 } moe_nvfp4_weights;
@@ -350,8 +355,9 @@ moe_status nvfp4_grouped_linear(const void *a, moe_dtype a_dtype, int n_rows,
 /* ------------------------------------------------------------------------- */
 
 /* Shapes and weights of one MoE layer.  The shared expert is optional
- * (shared_up.codes == NULL: none, so the output is the routed sum alone); it
- * always uses relu^2, the routed experts use `act`. */
+ * (shared_up.codes and shared_up.codes_packed both NULL: none, so the output
+ * is the routed sum alone); it always uses relu^2, the routed experts use
+ * `act`. */
 typedef struct {
   int n_tokens;               /* n */
   int d_model;                /* d: columns of x, up.cols, down.rows */

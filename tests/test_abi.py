@@ -336,3 +336,25 @@ def test_router_argument_errors(lib):
     assert call(x=ctypes.c_void_p((1 << 20) + 8)) == 1     # misaligned x
     assert call(wsb=lib.moe_router_workspace_size(16, 8) - 1) == 4
     assert call(n=0, x=None, w=None, ids=None, wt=None, ws=None) == 0
+
+
+def test_weights_given_only_as_repacked_copies(lib):
+    """Without the canonical codes and scales a projection needs both repacked
+    copies and whole 16-row blocks (32 for a SwiGLU up projection); one
+    canonical array without the other is refused."""
+    _setup(lib)
+    pk = dict(scales_packed=ctypes.c_void_p(4 << 20), codes_packed=ctypes.c_void_p(5 << 20))
+
+    def call(up, dn, act=0):
+        return lib.nvfp4_expert_ffn(FAKE, 1, 32, 16, FAKE, 8, ctypes.byref(up), ctypes.byref(dn), act, 32,
+                                    FAKE, 255, FAKE, None)   # too small a workspace: nothing launches
+
+    up, dn = W(None, None, FAKE, 128, 64, **pk), W(None, None, FAKE, 64, 128, **pk)
+    assert call(up, dn) == 4                                       # accepted up to the workspace check
+    assert call(W(None, None, FAKE, 120, 64, **pk), W(None, None, FAKE, 64, 120, **pk)) in (1, 2)  # rows % 16
+    assert call(W(None, None, FAKE, 128, 64), dn) == 1             # no copy at all
+    assert call(W(FAKE, None, FAKE, 128, 64, **pk), dn) == 1       # codes without scales
+    sw_up = W(None, None, FAKE, 2 * 48, 64, **pk)                  # 2f rows, f = 48: halves not whole blocks
+    sw_dn = W(None, None, FAKE, 64, 48, **pk)
+    assert call(sw_up, sw_dn, act=1) in (1, 2)
+    assert call(W(None, None, FAKE, 2 * 64, 64, **pk), W(None, None, FAKE, 64, 64, **pk), act=1) == 4

@@ -943,3 +943,32 @@ def test_fused_combine_equals_the_separate_weighted_row_sum(ops, case):
     ref = oracle.layer(inp)
     assert normwise(host(a).astype(np.float64), ref["out"]) <= TOL_PREFILL
     assert normwise(host(a).astype(np.float64), oracle.layer(inp, bf16_act=True)["out"]) <= 2e-3
+
+
+# ----------------------------------------------------------------------------
+# one copy of the weights
+# ----------------------------------------------------------------------------
+
+ONE_COPY_CASES = [("decode32_zipf", {}, 32), ("decode1", {}, 32), ("tiny16", dict(n=512, seed=32), 32),
+                  ("gated2", dict(n=40, seed=22), 0)]
+
+
+@pytest.mark.parametrize("case", range(len(ONE_COPY_CASES)))
+def test_one_weight_copy_gives_the_same_bits(ops, case):
+    """A layer that keeps only the repacked copies of its weights (the canonical
+    codes and scales freed) gives the bits of one that keeps both, on the
+    decode GEMV, the relu^2 GEMM and the SwiGLU GEMM; the single-launch step
+    falls back to the per-step launches when the canonical layout is gone."""
+    name, ov, gmax = ONE_COPY_CASES[case]
+    inp = cached_layer(name, **ov)
+    print(f"one-copy case {name} {ov}", flush=True)
+    both = ops.MoELayer(inp, gemv_max_rows=gmax, keep_canonical=True)
+    one = ops.MoELayer(inp, gemv_max_rows=gmax, single_launch=True, keep_canonical=False)
+    assert all(w is None or (w.codes is None and w.codes_packed is not None) for w in one.weights())
+    x, lg = dev(inp.x), dev(inp.logits)
+    a = both.forward(x, lg).clone()
+    b = one.forward(x, lg).clone()
+    c = one.forward_fused(x, lg).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(a, c)
+    assert int(host(one.views()["decode_launch"])[0]) == 0   # no single launch without the canonical layout
