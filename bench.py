@@ -299,9 +299,7 @@ def bench_decode(name, args, ops, synth):
     layer = ops.MoELayer(inp, device=dev, single_launch=True)
     copies = [layer.weights()]
     for _ in range(args.copies - 1):
-        copies.append(tuple(None if w is None else ops.DeviceNVFP4(w.codes.clone(), w.scales.clone(),
-                                                                   w.globals_.clone(), w.rows, w.cols).pack()
-                            for w in layer.weights()))
+        copies.append(tuple(None if w is None else w.clone() for w in layer.weights()))
     x = torch.from_numpy(np.ascontiguousarray(inp.x.view(np.int16) if inp.x.dtype == np.uint16 else inp.x)).to(dev)
     logits = torch.from_numpy(inp.logits).to(dev)
     L = len(copies)

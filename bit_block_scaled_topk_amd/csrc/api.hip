@@ -416,9 +416,10 @@ struct LayerPlan {
   int n, d, E, K, f, fs, R;
   bool has_shared, f32;
   size_t off_ids, off_w, off_offsets, off_row_token, off_rows, off_yg, off_gather, off_h, off_hs, off_split,
-      off_sync, off_cmb, total;
+      off_sync, off_cmb, off_part, total;
   int n_ct;  // 256-column tiles of the output (the fused combine's counters per token)
   int sync_words;
+  size_t part_bytes;
 };
 
 bool plan_layer(const moe_layer_desc *dsc, LayerPlan *pl) {
@@ -467,6 +468,11 @@ bool plan_layer(const moe_layer_desc *dsc, LayerPlan *pl) {
   // description, so a workspace initialised once serves calls of any size
   p.sync_words = (int)decode_layer_sync_words();
   p.off_sync = take((size_t)p.sync_words * 4);
+  // then its partial sums, tagged with launch counts: sized for a two-token
+  // step whatever n is, so every token count of a layer puts them in the
+  // same bytes, which nothing else writes
+  p.part_bytes = p.n > 0 ? decode_layer_part_bytes(2, p.E, p.K, p.d, p.f, p.fs) : 0;
+  p.off_part = take(p.part_bytes);
   p.off_ids = take((size_t)p.R * 4);
   p.off_w = take((size_t)p.R * 4);
   p.off_offsets = take((size_t)(p.E + 1) * 4);
@@ -533,7 +539,9 @@ moe_status moe_layer_workspace_init(const moe_layer_desc *desc, void *workspace,
   LayerPlan p;
   if (!plan_layer(desc, &p) || !workspace || !aligned(workspace, kAlign)) return MOE_INVALID_ARG;
   if (ws_bytes < p.total) return MOE_WORKSPACE_TOO_SMALL;
-  if (decode_layer_init((int32_t *)((char *)workspace + p.off_sync), stream) != hipSuccess) return MOE_HIP_ERROR;
+  if (decode_layer_init((int32_t *)((char *)workspace + p.off_sync), (char *)workspace + p.off_part, p.part_bytes,
+                        stream) != hipSuccess)
+    return MOE_HIP_ERROR;
   return MOE_OK;
 }
 
@@ -553,10 +561,11 @@ moe_status moe_layer_forward_noalloc(const moe_layer_desc *dsc, const void *x, c
   void *ws = nullptr;
   const moe_status st = noalloc_scratch(&ws);
   if (st != MOE_OK) return st;
-  // the single-launch step's flags and counters start from zero on every
-  // call: the array keeps whatever the last call on this GPU left
+  // the single-launch step's launch counts and partial sums start from zero
+  // on every call: the array keeps whatever the last call on this GPU left
   if ((dsc->flags & MOE_LAYER_SINGLE_LAUNCH) &&
-      decode_layer_init((int32_t *)((char *)ws + p.off_sync), stream) != hipSuccess)
+      decode_layer_init((int32_t *)((char *)ws + p.off_sync), (char *)ws + p.off_part, p.part_bytes, stream) !=
+          hipSuccess)
     return MOE_HIP_ERROR;
   return moe_layer_forward_profiled(dsc, x, logits, out, ws, MOE_NOALLOC_SCRATCH_BYTES, nullptr, stream);
 }
@@ -605,8 +614,7 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *dsc, const void *x, 
     lp.x = x;
     lp.x_f32 = p.f32;
     lp.logits = logits;
-    lp.h[0] = (float *)hs;
-    lp.h[1] = (float *)h;
+    lp.part = ws + p.off_part;
     lp.out = out;
     lp.yg = yg;
     lp.ids = ids;

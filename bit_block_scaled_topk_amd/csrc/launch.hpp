@@ -137,14 +137,16 @@ hipError_t launch_dq_gemm(ProjProblem *probs, int count, int epi, hipStream_t st
 // A whole decode step (n_tokens <= 2) in one persistent launch: routing, the
 // gather layout, the shared expert (up[0]/down[0], ignored unless has_shared)
 // and the routed experts (up[1]/down[1]; only their weights and shapes are
-// read), and the combine.  h[0] ([n][fs]) and h[1] ([n*K][f]) are fp32
-// scratch; out gets (shared ? shared : 0) + sum_j w[t][j] * yg[rows[t][j]].
-// The routing and layout views (ids, topk_w, offsets, row_token, rows) are
-// written as by the separate routing and gather launches.  sync points to
-// decode_layer_sync_words() int32 words that decode_layer_init zeroed once;
-// every launch leaves them ready for the next (sync[0]: set once a bounded
-// wait expires; sync[1]: launches so far).  Returns hipErrorNotSupported for
-// shapes it does not take (the caller then uses the per-step launches).
+// read; the repacked copies are required), and the combine.  part is
+// decode_layer_part_bytes() of scratch (each work unit's share of the down
+// projection, tagged with the launch's epoch), zeroed with the sync words by
+// decode_layer_init; out gets (shared ? shared : 0) + sum_j w[t][j] *
+// yg[rows[t][j]], and yg the routed experts' outputs.  The routing and layout
+// views (ids, topk_w, offsets, row_token, rows) are written as by the separate
+// routing and gather launches.  sync points to decode_layer_sync_words()
+// int32 words; every launch leaves them and part ready for the next (sync[0]:
+// set once a bounded wait expires; sync[1]: launches so far).  Returns hipErrorNotSupported for shapes it does not take
+// (the caller then uses the per-step launches).
 struct DecodeLayerProblem {
   ProjProblem up[2], down[2];
   bool has_shared;
@@ -153,7 +155,7 @@ struct DecodeLayerProblem {
   const void *x;       // [n][d] activations
   bool x_f32;          // else bf16
   const float *logits; // [n][n_experts]
-  float *h[2];
+  void *part;
   float *out, *yg;
   int32_t *ids, *rows, *offsets, *row_token;
   float *topk_w;
@@ -162,7 +164,10 @@ struct DecodeLayerProblem {
 };
 size_t decode_layer_sync_words();
 bool decode_layer_takes(int n_tokens, int top_k, int d_model);
-hipError_t decode_layer_init(int32_t *sync, hipStream_t stream);
+// Bytes of DecodeLayerProblem::part (0 when the step is never taken).
+size_t decode_layer_part_bytes(int n_tokens, int n_experts, int top_k, int d_model, int d_ff, int shared_d_ff);
+// Zeroes the sync words and the partial sums (part may be NULL).
+hipError_t decode_layer_init(int32_t *sync, void *part, size_t part_bytes, hipStream_t stream);
 hipError_t launch_decode_layer(const DecodeLayerProblem &lp, hipStream_t stream);
 
 }  // namespace moe

@@ -201,6 +201,12 @@ class DeviceNVFP4:
         self.scales = None
         return self
 
+    def clone(self) -> "DeviceNVFP4":
+        """A second device copy of whatever this projection holds."""
+        c = lambda t: None if t is None else t.clone()
+        return DeviceNVFP4(c(self.codes), c(self.scales), self.globals_.clone(), self.rows, self.cols,
+                           c(self.scales_packed), c(self.codes_packed))
+
     @property
     def n_experts(self) -> int:
         return int(self.globals_.shape[0])
@@ -472,13 +478,13 @@ class MoELayer:
     only for callers that run nothing else on the device during a step.
     ``fused_combine`` sets MOE_LAYER_FUSED_COMBINE (WeightedRowSum inside the
     prefill down projection).  The weights are repacked once when the layer is
-    built; the canonical copy is kept only when ``keep_canonical`` (by default:
-    with ``single_launch``, whose kernel reads it), so otherwise one copy of
-    the weights stays on the device.
+    built; every kernel of the layer reads the repacked copies, so the
+    canonical copy is freed unless ``keep_canonical``: one copy of the weights
+    stays on the device.
     """
 
     def __init__(self, inp, device="cuda", gemv_max_rows: int = MAX_GEMV_ROWS, n_tokens: Optional[int] = None,
-                 single_launch: bool = False, fused_combine: bool = False, keep_canonical: Optional[bool] = None):
+                 single_launch: bool = False, fused_combine: bool = False, keep_canonical: bool = False):
         self.n = int(n_tokens if n_tokens is not None else inp.n)
         self.d, self.E, self.K, self.f, self.fs = inp.d, inp.E, inp.K, inp.f, inp.fs
         self.act = MOE_SWIGLU if inp.act == "swiglu" else MOE_RELU2
@@ -490,11 +496,10 @@ class MoELayer:
         self.down = DeviceNVFP4.from_host(inp.down, device)
         self.shared_up = DeviceNVFP4.from_host(inp.shared_up, device) if inp.fs > 0 else None
         self.shared_down = DeviceNVFP4.from_host(inp.shared_down, device) if inp.fs > 0 else None
-        keep = single_launch if keep_canonical is None else keep_canonical
         for w in self.weights():
             if w is not None:
-                w.pack()  # the one-time repack the prefill GEMM and the decode GEMV read
-                if not keep:
+                w.pack()  # the one-time repack every kernel of the layer reads
+                if not keep_canonical:
                     w.drop_canonical()
         self.device = device
         self.layer_ws = None

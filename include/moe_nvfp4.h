@@ -85,8 +85,8 @@ typedef int moe_act;
  * pointers laid out as described in the file header.  codes and scales (the
  * canonical layout) may both be NULL when the repacked copies below are given
  * and rows is a multiple of 16 (32 for a SwiGLU up projection): every kernel
- * then reads the repacked copies, and the single-launch decode step falls back
- * to the per-step launches.  So a caller keeps one copy of the weights. */
+ * then reads the repacked copies.  So a caller keeps one copy of the
+ * weights. */
 typedef struct {
   const uint8_t *codes;
   const uint8_t *scales;
@@ -97,10 +97,10 @@ typedef struct {
    * nvfp4_pack_codes -- both present or both NULL, 16-byte aligned, holding
    * the same weights as `codes` / `scales`.  When both are present the decode
    * GEMV reads them, and so does the prefill GEMM when rows is a multiple of
-   * 16 (SwiGLU: f too); the single-launch decode step and the standalone
-   * unpack read the canonical layout (when it is given).  With them, one
-   * expert's repacked codes (ceil(rows/16) * ceil(cols/128) KB) must stay
-   * under 2 GiB. */
+   * 16 (SwiGLU: f too); the single-launch decode step reads only them (it
+   * falls back to the per-step launches without them), and the standalone
+   * unpack reads the canonical layout.  With them, one expert's repacked
+   * codes (ceil(rows/16) * ceil(cols/128) KB) must stay under 2 GiB. */
   const uint8_t *scales_packed;
   const uint8_t *codes_packed;
 } moe_nvfp4_weights;
@@ -417,12 +417,15 @@ typedef struct {
 /* Workspace bytes moe_layer_forward needs (0 for an invalid description). */
 size_t moe_layer_workspace_size(const moe_layer_desc *desc);
 
-/* Prepare a layer workspace for moe_layer_forward: clears the flags and
- * counters at its start (with a kernel on `stream`; nothing is allocated).
- * Required once after the workspace is allocated, before its first
- * moe_layer_forward; every later call leaves them ready for the next, for any
- * description whose workspace size fits ws_bytes.  A workspace belongs to one
- * device.  MOE_INVALID_ARG for a bad description or an unaligned (256-byte)
+/* Prepare a layer workspace for moe_layer_forward: clears the launch counts
+ * and the single-launch step's partial sums at its start (with a kernel on
+ * `stream`; nothing is allocated).  Required once after the workspace is
+ * allocated, before its first moe_layer_forward; every later call leaves them
+ * ready for the next, for any token count of the same layer shape (experts,
+ * top_k, d_model, d_ff, shared d_ff) whose workspace size fits ws_bytes.
+ * Those partial sums are trusted by their launch-count tags, so a workspace
+ * moved to a layer of another shape must be prepared again.  A workspace
+ * belongs to one device.  MOE_INVALID_ARG for a bad description or an unaligned (256-byte)
  * workspace, MOE_WORKSPACE_TOO_SMALL if ws_bytes < moe_layer_workspace_size. */
 moe_status moe_layer_workspace_init(const moe_layer_desc *desc, void *workspace, size_t ws_bytes,
                                     hipStream_t stream);
@@ -437,10 +440,12 @@ moe_status moe_layer_get_views(const moe_layer_desc *desc, void *workspace, moe_
  * up and each down launch, and nothing synchronises or allocates (Glq v0.2.13
  * "Remaining gap to bf16-native": fewer launches per layer).  For a decode
  * step -- desc->flags has MOE_LAYER_SINGLE_LAUNCH, n_tokens <= min(2,
- * gemv_max_rows), d_model <= 16384 and the weights fit the LDS of the CUs --
- * the whole layer (routing, gather layout, up and down projections, combine)
- * is ONE persistent launch whose workgroups hand results to each other
- * through flags and counters in the workspace (waits are bounded; see
+ * gemv_max_rows), d_model <= 3072 (2048 with SwiGLU), the repacked weight
+ * copies given and no shared expert beside a SwiGLU FFN -- the whole layer
+ * (routing, gather layout, up and down projections, combine) is ONE
+ * persistent launch: each workgroup computes slices of the experts' hidden
+ * width and hands its share of the down projection to the others through
+ * the workspace, tagged with a launch count (waits are bounded; see
  * moe_layer_views.wait_error); its dot products run in fp32 on the vector
  * ALUs, so it agrees with the four calls to fp32 rounding rather than bit for
  * bit.  The workspace must have been prepared by
@@ -477,9 +482,9 @@ moe_status moe_layer_forward_profiled(const moe_layer_desc *desc, const void *x,
  *   refused with MOE_UNSUPPORTED before anything runs.
  *   Every call on one GPU shares that GPU's array: calls that overlap on one
  *   GPU (several streams or threads) race and give undefined results.  The
- *   single-launch decode step (MOE_LAYER_SINGLE_LAUNCH) clears its flags and
- *   counters with a small kernel on `stream` before each call.  The
- *   intermediates are not exposed (no views).
+ *   single-launch decode step (MOE_LAYER_SINGLE_LAUNCH) clears its launch
+ *   counts and partial sums with a small kernel on `stream` before each
+ *   call.  The intermediates are not exposed (no views).
  * Errors as moe_layer_forward. */
 #define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
 moe_status moe_layer_forward_noalloc(const moe_layer_desc *desc, const void *x, const float *logits, float *out,

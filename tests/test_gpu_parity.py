@@ -958,7 +958,8 @@ def test_one_weight_copy_gives_the_same_bits(ops, case):
     """A layer that keeps only the repacked copies of its weights (the canonical
     codes and scales freed) gives the bits of one that keeps both, on the
     decode GEMV, the relu^2 GEMM and the SwiGLU GEMM; the single-launch step
-    falls back to the per-step launches when the canonical layout is gone."""
+    (which reads only the repacked copies) runs for the one-token step and
+    agrees to fp32 rounding."""
     name, ov, gmax = ONE_COPY_CASES[case]
     inp = cached_layer(name, **ov)
     print(f"one-copy case {name} {ov}", flush=True)
@@ -970,5 +971,10 @@ def test_one_weight_copy_gives_the_same_bits(ops, case):
     b = one.forward(x, lg).clone()
     c = one.forward_fused(x, lg).clone()
     torch.cuda.synchronize()
-    assert torch.equal(a, b) and torch.equal(a, c)
-    assert int(host(one.views()["decode_launch"])[0]) == 0   # no single launch without the canonical layout
+    assert torch.equal(a, b)
+    single = inp.n <= min(2, gmax)
+    assert int(host(one.views()["decode_launch"])[0]) == (1 if single else 0)
+    if single:
+        assert normwise(host(c).astype(np.float64), host(a).astype(np.float64)) <= 2e-6
+    else:
+        assert torch.equal(a, c)
