@@ -362,18 +362,24 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
     uint64_t *s_cand = s_key + kMaxRows * kKeyRow;                         // [n][Cp]
     float *s_logit = (float *)(s_cand + kMaxRows * kKeyRow);               // [n][E]
     uint64_t *s_pick = (uint64_t *)(s_logit + kMaxRows * MOE_MAX_EXPERTS);  // [n][K]
-    for (int c = tid; c < n * Ep; c += kThreads) s_key[c] = 0ull;
-    if (a.rk_two)
-      for (int c = tid; c < n * Cp; c += kThreads) s_cand[c] = 0ull;
-    lds_barrier();
 #pragma unroll
     for (int i = 0; i < kLogitsPerThread; ++i) {
+      if (kThreads * i >= NE) break;  // uniform
       const int c = tid + kThreads * i;
       if (c < NE) {
         const int t = c >= E, e = c - t * E;
         s_logit[c] = lg[i];
         s_key[t * Ep + e] = route_key(lg[i], e);
       }
+    }
+    {  // the padding of each key row, and the candidate rows
+      const int pad = Ep - E;
+      for (int c = tid; c < n * pad; c += kThreads) {
+        const int t = c >= pad;
+        s_key[t * Ep + E + c - t * pad] = 0ull;
+      }
+      if (a.rk_two)
+        for (int c = tid; c < n * Cp; c += kThreads) s_cand[c] = 0ull;
     }
     lds_barrier();
     if (!a.rk_two) {
