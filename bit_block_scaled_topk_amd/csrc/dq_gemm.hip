@@ -126,7 +126,7 @@ __device__ __forceinline__ void find_tile(const int32_t *offsets, int E, int n_r
 // SM, how the weights are loaded: 0, one 2-byte scale load per chunk and
 // block from the canonical layout; 2, the same from the repacked scales (a
 // block's 16 rows of one chunk in one 128-byte line instead of 16 lines); 3,
-// as 2 with the codes repacked too (a block's chunk, 16 rows x 64 bytes, is
+// as 2 with the codes repacked too (a block's chunk, 2 halves x 16 rows x 32 bytes, is
 // 1 KB contiguous: one load reads 8 whole lines instead of 16 half lines); 1 (K a
 // multiple of 64, scales 4-byte aligned, no repacked copy): loaded
 // for a pair of chunks at a time -- lane (n, q) loads bytes 4q .. 4q + 3 of
@@ -197,7 +197,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const __amdgpu_buffer_rsrc_t c_rsrc =
       SM == 3 ? make_rsrc(p.codes_packed + (size_t)e * pkc_bytes, pkc_bytes)
               : make_rsrc(p.codes + e_rows * (size_t)(K >> 1), (uint32_t)p.n_w * (uint32_t)(K >> 1));
-  // repacked scales (SM 2): [16-row block][128-wide chunk][16 rows][8 bytes] per expert
+  // repacked scales (SM 2): [16-row block][128-wide chunk][64-wide half][16 rows][4 bytes] per expert
   const uint32_t nch = (uint32_t)(K + 127) >> 7, pk_bytes = (uint32_t)((p.n_w + 15) >> 4) * nch * 128u;
   const __amdgpu_buffer_rsrc_t s_rsrc =
       SM >= 2 ? make_rsrc(p.scales_packed + (size_t)e * pk_bytes, pk_bytes)
@@ -215,7 +215,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // a column past n_out reads past the expert's rows (zero), or -- for the
   // gate half of a partial SwiGLU tile -- rows whose results are not stored
   const uint32_t c_off0 = (uint32_t)wrow0 * (uint32_t)(K >> 1) + 16u * q;
-  const uint32_t s_off0 = SM >= 2 ? 8u * (uint32_t)nl + 2u * q : (uint32_t)wrow0 * (uint32_t)(K >> 4) + (SP ? 4u : 2u) * q;
+  const uint32_t s_off0 = SM >= 2 ? 64u * (uint32_t)(q >> 1) + 4u * (uint32_t)nl + 2u * (uint32_t)(q & 1) : (uint32_t)wrow0 * (uint32_t)(K >> 4) + (SP ? 4u : 2u) * q;
   // A wavefront whose output columns all lie past n_out (the last column tile
   // of a ragged width, e.g. 1856 = 7 x 256 + 64) skips its MFMAs and decode:
   // it still fills its share of the activation tile and meets every barrier,
@@ -249,9 +249,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t co;
-      if constexpr (SM == 3) {  // the block's chunk: 16 rows x 64 bytes
+      if constexpr (SM == 3) {  // the block's chunk: 2 halves x 16 rows x 32 bytes
         const uint32_t blk = (uint32_t)((wrow0 - nl + dj[j]) >> 4) * nch_c + (uint32_t)(k0 >> 7);
-        co = b_in ? (blk * 16u + (uint32_t)nl) * 64u + 16u * q : OOB;
+        co = b_in ? blk * 1024u + (uint32_t)(q >> 1) * 512u + (uint32_t)nl * 32u + 16u * (uint32_t)(q & 1) : OOB;
       } else
         co = b_in ? c_off0 + (uint32_t)(dj[j] * (K >> 1)) + (uint32_t)(k0 >> 1) : OOB;
       rc[j] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, co, 0, 0);
@@ -563,31 +563,30 @@ hipError_t launch_dq_gemm(ProjProblem *probs, int count, int epi, hipStream_t st
   return hipGetLastError();
 }
 
-// One 8-byte unit u = ((e nrb + b) nch + c) 16 + r of the repacked scales per
-// thread: row 16 b + r of expert e, bytes 8 c .. 8 c + 7 of its kb scale bytes
-// (zero past the row count or past kb).
+// One 4-byte unit u = (((e nrb + b) nch + c) 2 + h) 16 + r of the repacked
+// scales per thread: row 16 b + r of expert e, bytes 8 c + 4 h .. + 3 of its kb
+// scale bytes (the scales of k 128 c + 64 h .. + 63; zero past the row count or
+// past kb).
 __global__ void __launch_bounds__(256) k_pack_scales(const uint8_t *__restrict__ s, int rows, int kb, int nrb, int nch,
                                                      long units, uint8_t *__restrict__ dst) {
   const long u = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (u >= units) return;
   const int r = (int)(u & 15);
-  long t = u >> 4;
+  const int h = (int)((u >> 4) & 1);
+  long t = u >> 5;
   const int c = (int)(t % nch);
   t /= nch;
   const int blk = (int)(t % nrb);
   const long e = t / nrb;
-  const int row = 16 * blk + r;
-  uint32_t w[2] = {0u, 0u};
+  const int row = 16 * blk + r, col = 8 * c + 4 * h;
+  uint32_t w = 0u;
   if (row < rows) {
-    const uint8_t *src = s + (e * rows + row) * (long)kb + 8 * c;
+    const uint8_t *src = s + (e * rows + row) * (long)kb + col;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (8 * c + i < kb) w[i >> 2] |= (uint32_t)src[i] << (8 * (i & 3));
+    for (int i = 0; i < 4; ++i)
+      if (col + i < kb) w |= (uint32_t)src[i] << (8 * i);
   }
-  uint2 v;
-  v.x = w[0];
-  v.y = w[1];
-  ((uint2 *)dst)[u] = v;
+  ((uint32_t *)dst)[u] = w;
 }
 
 long packed_scales_bytes(long n_experts, int rows, int cols) {
@@ -597,28 +596,30 @@ long packed_scales_bytes(long n_experts, int rows, int cols) {
 hipError_t launch_pack_scales(const uint8_t *scales, int n_experts, int rows, int cols, uint8_t *dst,
                               hipStream_t stream) {
   const int nrb = (rows + 15) / 16, nch = (cols + 127) / 128;
-  const long units = (long)n_experts * nrb * nch * 16;
+  const long units = (long)n_experts * nrb * nch * 32;
   if (units <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_pack_scales, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream, scales, rows,
                      cols / 16, nrb, nch, units, dst);
   return hipGetLastError();
 }
 
-// One 16-byte piece u = (((e nrb + b) nch + c) 16 + r) 4 + i of the repacked
-// codes per thread: row 16 b + r of expert e, bytes 64 c + 16 i .. + 15 of its
-// kc code bytes (zero past the row count or past kc).
+// One 16-byte piece u = ((((e nrb + b) nch + c) 2 + h) 16 + r) 2 + i of the
+// repacked codes per thread: row 16 b + r of expert e, bytes 64 c + 32 h + 16 i
+// .. + 15 of its kc code bytes (the codes of k 128 c + 64 h + 32 i .. + 31;
+// zero past the row count or past kc).
 __global__ void __launch_bounds__(256) k_pack_codes(const uint8_t *__restrict__ s, int rows, int kc, int nrb, int nch,
                                                     long units, uint8_t *__restrict__ dst) {
   const long u = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (u >= units) return;
-  const int piece = (int)(u & 3);
-  const int r = (int)((u >> 2) & 15);
+  const int piece = (int)(u & 1);
+  const int r = (int)((u >> 1) & 15);
+  const int h = (int)((u >> 5) & 1);
   long t = u >> 6;
   const int c = (int)(t % nch);
   t /= nch;
   const int blk = (int)(t % nrb);
   const long e = t / nrb;
-  const int row = 16 * blk + r, col = 64 * c + 16 * piece;
+  const int row = 16 * blk + r, col = 64 * c + 32 * h + 16 * piece;
   u32x4_t v = {0u, 0u, 0u, 0u};
   if (row < rows && col < kc) {
     const uint8_t *src = s + (e * rows + row) * (long)kc + col;

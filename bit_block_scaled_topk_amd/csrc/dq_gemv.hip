@@ -106,7 +106,8 @@ __device__ __forceinline__ void find_expert(const int32_t *__restrict__ offsets,
 }
 
 // PK: the weights are read from their repacked copies (nvfp4_pack_codes and
-// nvfp4_pack_scales: [16-row block][128-wide k chunk][16 rows][64 or 8 bytes]),
+// nvfp4_pack_scales: [16-row block][128-wide k chunk][64-wide half][16 rows]
+// [32 or 4 bytes]),
 // where the 16 rows of a round's k-groups are contiguous (one 1 KB piece of
 // codes and one 128-byte line of scales per tile) instead of 16 row segments.
 template <int WAVES, int MT, int NT, int EPI, int CT, bool PK>
@@ -156,8 +157,9 @@ __global__ void __launch_bounds__(64 * WAVES) k_dq_gemv(GemvBatch batch) {
     const int col = min((tile0 + ct) * 16 + nl, p.n_out - 1);
     return base + ((size_t)e * p.n_w + (size_t)col + (size_t)b * p.n_out) * pitch;
   };
-  // repacked: byte offset of k-group g of weight row `row` (codes: 16 bytes
-  // per k-group, scales: 2), inside this expert's copy
+  // repacked: slot (block-chunk index x 16 + row in the block) of k-group g of
+  // a weight row; the k-group's 16 code bytes and 2 scale bytes sit in half
+  // (g >> 1) & 1 of the block-chunk, at byte 16 (g & 1) / 2 (g & 1) of the row
   const int nch = (p.k + 127) >> 7;
   const size_t pk_rows = (size_t)((p.n_w + 15) >> 4) * (size_t)nch * 16;  // 16-row slots of one expert
   auto pk_slot = [&](int ct, int b, int g) -> size_t {
@@ -193,8 +195,9 @@ __global__ void __launch_bounds__(64 * WAVES) k_dq_gemv(GemvBatch batch) {
         for (int b = 0; b < NB; ++b) {
           if constexpr (PK) {
             const size_t slot = pk_slot(ct, b, gc);
-            wq[ct][b][i] = *(const u32x4_t *)(p.codes_packed + slot * 64 + (gc & 3) * 16);
-            const uint32_t s2 = *(const uint16_t *)(p.scales_packed + slot * 8 + (gc & 3) * 2);
+            const size_t bc = slot >> 4, rr = slot & 15, hf = (gc >> 1) & 1, qt = gc & 1;
+            wq[ct][b][i] = *(const u32x4_t *)(p.codes_packed + bc * 1024 + hf * 512 + rr * 32 + qt * 16);
+            const uint32_t s2 = *(const uint16_t *)(p.scales_packed + bc * 128 + hf * 64 + rr * 4 + qt * 2);
             sc[ct][b][i] = (g < ge) ? s2 : 0u;  // a zero scale neutralises a clamped group
             continue;
           }

@@ -28,13 +28,15 @@
 // with fmaf in j order.
 //
 // Lane maps.  The repacked weights hold, per expert, 16-row block and
-// 128-wide k chunk, 16 rows x 64 bytes of codes (1 KB) and 16 rows x 8 scales
-// (128 B).  Up rows: one load of a wavefront reads a whole chunk of one block
-// -- lane (n, q) = (l % 16, l / 16) gets row n's codes for k = 128 c + 32 q ..
-// + 31; chunk c goes to wavefront c % 8.  Down: one load covers the unit's
-// k-slice of two blocks -- lane l takes block 2 p + l / 32, row (l % 32) / 2
-// and half l % 2 of the slice; block pair p goes to wavefront p % 8.  Each
-// piece's two scales come with it (a 2-byte load).  The dot products run on
+// 128-wide k chunk, two 64-wide halves of 16 rows x 32 bytes of codes (1 KB in
+// all) and of 16 rows x 4 scales (128 B in all).  Up rows: one load of a
+// wavefront reads a whole chunk of one block -- lane (n, q) = (l % 16, l / 16)
+// gets row n's codes for k = 128 c + 32 q .. + 31; chunk c goes to wavefront
+// c % 8.  Down: one load covers the unit's k-slice of two blocks, which is one
+// half of a chunk, 512 contiguous bytes per block -- lane l takes block
+// 2 p + l / 32, row (l % 32) / 2 and quarter l % 2 of the slice; block pair p
+// goes to wavefront p % 8.  Each piece's two scales come with it (a 2-byte
+// load).  The dot products run on
 // the vector ALUs
 // in fp32 (bf16 x through the bf16 dot instruction: exact products, fp32
 // sums), each 16-element block's sum scaled by its e4m3 scale.  (A
@@ -240,7 +242,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
   constexpr int SU = CU * 4 * NB, S = SU + DP;
   const int nq = lane >> 4, nn = lane & 15;                        // up: k-quarter, row
   const int dq = lane & 1, dr = (lane & 31) >> 1, dh = lane >> 5;  // down: slice half, row, block of the pair
-  const int up_lc = nn * 64 + nq * 16;
+  const int up_lc = (nq >> 1) * 512 + nn * 32 + (nq & 1) * 16;
   struct UnitSrc {
     __amdgpu_buffer_rsrc_t uc, us, dc, dsc;
     int nb_out, dnch, s;
@@ -267,7 +269,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
     u32x4_t w;
     uint32_t sc;
   };
-  const int up_ls = nn * 8 + nq * 2;
+  const int up_ls = (nq >> 1) * 64 + nn * 4 + (nq & 1) * 2;
   auto load_piece = [&](const UnitSrc &q, int i) -> Piece {
     Piece p;
     if (i < SU) {
@@ -282,12 +284,12 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
     const int pr = min(wave + kWaves * jj, (a.dblk - 1) >> 1);
     // block 2 pr + dh (the first block of a half-used last pair), row dr, half dq
     const bool whole = 2 * pr + 1 < a.dblk;
-    const int lc = (whole ? dh * q.dnch * 1024 : 0) + dr * 64 + dq * 16;
-    const int ls = (whole ? dh * q.dnch * 128 : 0) + dr * 8 + dq * 2;
+    const int lc = (whole ? dh * q.dnch * 1024 : 0) + dr * 32 + dq * 16;
+    const int ls = (whole ? dh * q.dnch * 128 : 0) + dr * 4 + dq * 2;
     const int piece = 2 * pr * q.dnch + (q.s >> 1);
     p.w = __builtin_bit_cast(u32x4_t,
-                             __builtin_amdgcn_raw_buffer_load_b128(q.dc, lc, piece * 1024 + (q.s & 1) * 32, 0));
-    p.sc = __builtin_amdgcn_raw_buffer_load_b16(q.dsc, ls, piece * 128 + (q.s & 1) * 4, 0);
+                             __builtin_amdgcn_raw_buffer_load_b128(q.dc, lc, piece * 1024 + (q.s & 1) * 512, 0));
+    p.sc = __builtin_amdgcn_raw_buffer_load_b16(q.dsc, ls, piece * 128 + (q.s & 1) * 64, 0);
     return p;
   };
 

@@ -111,14 +111,16 @@ typedef struct {
 size_t nvfp4_packed_scales_bytes(int n_experts, int rows, int cols);
 
 /* nvfp4_pack_scales -- the optional one-time repack of a projection's e4m3
- * block scales into the order the prefill GEMM reads them in (the boundary's
- * "prepack": same bytes, another order, no global):
- *   dst[e][b][c][r][i] = scales[e][16 b + r][8 c + i]
- * for 16-row block b, 128-column chunk c, row r < 16 and i < 8; entries past
- * rows or past cols/16 are zero.  In that order one 16-row block's scales of
- * one 128-wide k chunk are 128 contiguous bytes, one cache line, where the
- * canonical layout spreads them over 16 (the GEMM's scale loads were a third
- * of its requests to L2).
+ * block scales into the order the GEMM, GEMV and single-launch decode kernels
+ * read them in (the boundary's "prepack": same bytes, another order, no
+ * global):
+ *   dst[e][b][c][h][r][i] = scales[e][16 b + r][8 c + 4 h + i]
+ * for 16-row block b, 128-column chunk c, 64-column half h < 2, row r < 16 and
+ * i < 4; entries past rows or past cols/16 are zero.  In that order one 16-row
+ * block's scales of one 128-wide k chunk are 128 contiguous bytes, one cache
+ * line, where the canonical layout spreads them over 16 (the GEMM's scale
+ * loads were a third of its requests to L2), and those of one 64-wide half
+ * are 64 contiguous bytes.
  *   w       the projection (w->codes and w->global are not read)
  *   dst     device, dst_bytes >= nvfp4_packed_scales_bytes(n_experts, rows, cols)
  * Errors: MOE_INVALID_ARG for null pointers, n_experts < 1, rows < 1, cols not a
@@ -133,13 +135,14 @@ moe_status nvfp4_pack_scales(const moe_nvfp4_weights *w, int n_experts, uint8_t 
 size_t nvfp4_packed_codes_bytes(int n_experts, int rows, int cols);
 
 /* nvfp4_pack_codes -- the optional one-time repack of a projection's e2m1
- * codes into the order the prefill GEMM reads them in (same bytes, another
- * order):
- *   dst[e][b][c][r][i] = codes[e][16 b + r][64 c + i]
- * for 16-row block b, 128-column chunk c, row r < 16 and i < 64; entries past
- * rows or past cols/2 are zero.  One 16-row block's codes of one 128-wide k
- * chunk are then 1 KB contiguous, which one 16-byte-per-lane load reads as 8
- * whole cache lines (16 half lines in the canonical layout).
+ * codes into the order the GEMM, GEMV and single-launch decode kernels read
+ * them in (same bytes, another order):
+ *   dst[e][b][c][h][r][i] = codes[e][16 b + r][64 c + 32 h + i]
+ * for 16-row block b, 128-column chunk c, 64-column half h < 2, row r < 16 and
+ * i < 32; entries past rows or past cols/2 are zero.  One 16-row block's codes
+ * of one 128-wide k chunk are then 1 KB contiguous, which one 16-byte-per-lane
+ * load reads as 8 whole cache lines (16 half lines in the canonical layout),
+ * and those of one 64-wide half are 512 contiguous bytes.
  *   w       the projection (w->scales and w->global are not read)
  *   dst     device, dst_bytes >= nvfp4_packed_codes_bytes(n_experts, rows, cols)
  * Errors as nvfp4_pack_scales.  Stream-ordered on `stream`; allocates nothing. */

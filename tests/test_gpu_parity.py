@@ -337,42 +337,50 @@ def test_grouped_linear(ops, a_dtype, path):
 
 def test_pack_scales_layout(ops):
     """nvfp4_pack_scales against the layout written out on the host: 16-row
-    blocks, 128-wide k chunks, 8 scale bytes per row and chunk, zeros past the
-    rows (40 = 2.5 blocks) and past the row's 14 scale bytes (224 columns)."""
+    blocks, 128-wide k chunks, each in two 64-wide halves of 4 scale bytes per
+    row, zeros past the rows (40 = 2.5 blocks) and past the row's 14 scale
+    bytes (224 columns: the second chunk's second half is half empty)."""
     E, rows, cols = 3, 40, 224
     w = synth.random_bytes_nvfp4(41, E, rows, cols)
     got = host(ops.nvfp4_pack_scales(ops.DeviceNVFP4.from_host(w)))
     kb, nrb, nch = cols // 16, (rows + 15) // 16, (cols + 127) // 128
     sc = np.asarray(w.scales).reshape(E, rows, kb)
-    ref = np.zeros((E, nrb, nch, 16, 8), dtype=np.uint8)
+    ref = np.zeros((E, nrb, nch, 2, 16, 4), dtype=np.uint8)
     for b in range(nrb):
         for r in range(16):
             if 16 * b + r >= rows:
                 continue
             for c in range(nch):
-                n = min(8, kb - 8 * c)
-                ref[:, b, c, r, :n] = sc[:, 16 * b + r, 8 * c:8 * c + n]
+                for h in range(2):
+                    lo = 8 * c + 4 * h
+                    n = min(4, kb - lo)
+                    if n > 0:
+                        ref[:, b, c, h, r, :n] = sc[:, 16 * b + r, lo:lo + n]
     assert got.size == ops.nvfp4_packed_scales_bytes(E, rows, cols) == ref.size
     assert np.array_equal(got.reshape(ref.shape), ref)
 
 
 def test_pack_codes_layout(ops):
     """nvfp4_pack_codes against the layout written out on the host: 16-row
-    blocks, 128-wide k chunks, 64 code bytes per row and chunk, zeros past the
-    rows (40) and past the row's 112 code bytes (224 columns)."""
+    blocks, 128-wide k chunks, each in two 64-wide halves of 32 code bytes per
+    row, zeros past the rows (40) and past the row's 112 code bytes (224
+    columns: the second chunk's second half is half empty)."""
     E, rows, cols = 3, 40, 224
     w = synth.random_bytes_nvfp4(42, E, rows, cols)
     got = host(ops.nvfp4_pack_codes(ops.DeviceNVFP4.from_host(w)))
     kc, nrb, nch = cols // 2, (rows + 15) // 16, (cols + 127) // 128
     cd = np.asarray(w.codes).reshape(E, rows, kc)
-    ref = np.zeros((E, nrb, nch, 16, 64), dtype=np.uint8)
+    ref = np.zeros((E, nrb, nch, 2, 16, 32), dtype=np.uint8)
     for b in range(nrb):
         for r in range(16):
             if 16 * b + r >= rows:
                 continue
             for c in range(nch):
-                n = min(64, kc - 64 * c)
-                ref[:, b, c, r, :n] = cd[:, 16 * b + r, 64 * c:64 * c + n]
+                for h in range(2):
+                    lo = 64 * c + 32 * h
+                    n = min(32, kc - lo)
+                    if n > 0:
+                        ref[:, b, c, h, r, :n] = cd[:, 16 * b + r, lo:lo + n]
     assert got.size == ops.nvfp4_packed_codes_bytes(E, rows, cols) == ref.size
     assert np.array_equal(got.reshape(ref.shape), ref)
 
