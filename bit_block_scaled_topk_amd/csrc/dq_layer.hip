@@ -79,6 +79,7 @@ constexpr int kMaxD = 3072;            // d_model the register tiles cover
 constexpr int kLogitsPerThread = kMaxRows * MOE_MAX_EXPERTS / kThreads;
 constexpr int kXLoads = kMaxRows * kMaxD * 4 / 16 / kThreads;  // 16-byte pieces of x per thread (fp32 x)
 constexpr int kSumGroup = 8;           // slices one reducer thread adds
+constexpr int kRedCols = 16;           // output columns one reducer block combines
 constexpr int kWin = 8;                // weight loads in flight per wavefront
 constexpr int kKeyRow = 2 * MOE_MAX_EXPERTS;  // routing keys of one token, padded
 
@@ -206,9 +207,10 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
   extern __shared__ u32x4_t s_dyn[];  // x | phase scratch
   __shared__ int s_id[kMaxPicks], s_prow[kMaxPicks], s_pslot[kMaxPicks];  // per pick t*K + j
   __shared__ float s_pw[kMaxPicks];
+  __shared__ float s_gl[kMaxPicks + 1];  // the down projections' globals: per pick, then the shared expert's
   __shared__ int s_rt[kMaxPicks];       // token of each packed row
-  __shared__ int s_e[kMaxPicks], s_r0[kMaxPicks], s_rows[kMaxPicks], s_stok[kMaxPicks][kMaxRows];  // per slot
-  __shared__ int s_nact;
+  __shared__ int s_r0[kMaxPicks];       // first packed row of each slot
+  __shared__ uint32_t s_bits[kMaxRows][MOE_MAX_EXPERTS / 32];  // each token's picked experts
   const DecodeLayerProblem &lp = a.lp;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -232,14 +234,21 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
   }
   const int32_t epoch = __hip_atomic_load(&flags[blockIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // ---- a unit's weights.  Pieces in a fixed order -- the up pieces [chunk
-  //      iteration j][tile t], then the down block pairs -- and a window of
-  //      kWin loads in flight: piece i + kWin is requested as piece i is
-  //      used, so the compiler waits for each piece alone.  No branches: an
-  //      absent piece reloads a valid one, which is not used.  Buffer loads
+  // ---- a unit's weights.  Pieces in a fixed order -- the up pieces, then
+  //      the down block pairs -- and a window of kWin loads in flight: piece
+  //      i + kWin is requested as piece i is used, so the compiler waits for
+  //      each piece alone.  The unit's up pieces, (chunk, tile) with the tile
+  //      fastest, are dealt round-robin to the wavefronts, so each wavefront
+  //      keeps one tile (its index mod the tiles per chunk) and the counts
+  //      differ by at most one.  No branches: an absent piece (past the
+  //      chunks, tiles or block pairs) reloads a present one, which the
+  //      caches hold, and is not used (requesting it past the buffer's extent
+  //      instead, so that nothing is read, was measured slower).  Buffer loads
   //      over the expert's region: the per-lane part of an address is one
   //      register for all pieces, the rest a scalar offset.
-  constexpr int SU = CU * 4 * NB, S = SU + DP;
+  constexpr int TPC = 4 * NB;  // up tiles per chunk
+  constexpr int SU = CU * TPC, S = SU + DP;
+  const int my_t = wave % TPC;  // this wavefront's up tile
   const int nq = lane >> 4, nn = lane & 15;                        // up: k-quarter, row
   const int dq = lane & 1, dr = (lane & 31) >> 1, dh = lane >> 5;  // down: slice half, row, block of the pair
   const int up_lc = (nq >> 1) * 512 + nn * 32 + (nq & 1) * 16;
@@ -273,9 +282,8 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
   auto load_piece = [&](const UnitSrc &q, int i) -> Piece {
     Piece p;
     if (i < SU) {
-      const int j = i / (4 * NB), t = i % (4 * NB);
-      const int c = min(wave + kWaves * j, a.dch - 1);
-      const int piece = ((t >> 2) * q.nb_out + min(4 * q.s + (t & 3), q.nb_out - 1)) * a.dch + c;
+      const int c = min((wave + kWaves * i) / TPC, a.dch - 1), blk = min(4 * q.s + (my_t & 3), q.nb_out - 1);
+      const int piece = ((my_t >> 2) * q.nb_out + blk) * a.dch + c;
       p.w = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(q.uc, up_lc, piece * 1024, 0));
       p.sc = __builtin_amdgcn_raw_buffer_load_b16(q.us, up_ls, piece * 128, 0);
       return p;
@@ -293,6 +301,11 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
     return p;
   };
 
+  // the gather layout, in every wavefront's registers (lane = pick t K + j):
+  // the pick's expert and token, its slot, whether it owns the slot (the
+  // slot's lower token) and the slot's rows; and the number of slots
+  int r_e = 0, r_t = 0, r_slot = 0, r_rows = 0, r_nact = 0;
+  bool r_own = false;
   auto resolve = [&](int uidx, UnitRef &u) {
     u.shared = uidx < a.ns;
     if (u.shared) {
@@ -303,16 +316,17 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
       u.rows = n;
       u.tok[0] = 0;
       u.tok[1] = 1;
-    } else {
+    } else {  // from the layout registers: the lane of the pick that owns the slot
       const int v = uidx - a.ns;
       u.slot = v / a.nr;
       u.s = v - u.slot * a.nr;
-      u.ok = u.slot < s_nact;
-      const int sl = u.ok ? u.slot : 0;
-      u.e = min(max(s_e[sl], 0), E - 1);
-      u.rows = s_rows[sl];
-      u.tok[0] = s_stok[sl][0];
-      u.tok[1] = s_stok[sl][1];
+      u.ok = u.slot < r_nact;
+      const uint64_t m = __ballot(r_own && r_slot == u.slot);
+      const int ol = m ? (int)__builtin_ctzll(m) : 0;
+      u.e = min(max(__builtin_amdgcn_readlane(r_e, ol), 0), E - 1);
+      u.rows = __builtin_amdgcn_readlane(r_rows, ol);
+      u.tok[0] = __builtin_amdgcn_readlane(r_t, ol);
+      u.tok[1] = 1;
     }
   };
 
@@ -374,6 +388,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
         s_key[t * Ep + e] = route_key(lg[i], e);
       }
     }
+    for (int c = tid; c < n * (MOE_MAX_EXPERTS / 32); c += kThreads) (&s_bits[0][0])[c] = 0u;
     {  // the padding of each key row, and the candidate rows
       const int pad = Ep - E;
       for (int c = tid; c < n * pad; c += kThreads) {
@@ -384,9 +399,14 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
         for (int c = tid; c < n * Cp; c += kThreads) s_cand[c] = 0ull;
     }
     lds_barrier();
+    auto pick = [&](int t, int cnt, uint64_t key) {  // slot cnt of token t; its expert's bit
+      s_pick[t * K + cnt] = key;
+      const int e = min(max(route_key_index(key), 0), E - 1);
+      __hip_atomic_fetch_or(&s_bits[t][e >> 5], 1u << (e & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
     if (!a.rk_two) {
       rank_pass(s_key, E, Ep, 30, a.rk_p1, a.rk_s1, [&](int t, int, int cnt, uint64_t key) {
-        if (cnt < K) s_pick[t * K + cnt] = key;
+        if (cnt < K) pick(t, cnt, key);
       });
     } else {
       rank_pass(s_key, E, Ep, a.rk_gs, a.rk_p1, a.rk_s1, [&](int t, int i, int cnt, uint64_t key) {
@@ -394,53 +414,62 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
       });
       lds_barrier();
       rank_pass(s_cand, C, Cp, 30, a.rk_p2, a.rk_s2, [&](int t, int, int cnt, uint64_t key) {
-        if (key != 0ull && cnt < K) s_pick[t * K + cnt] = key;
+        if (key != 0ull && cnt < K) pick(t, cnt, key);
       });
     }
     lds_barrier();
-    // gather layout (one wavefront, lane = pick t * K + j; lane reads instead
-    // of LDS round trips): rows grouped by expert in ascending id, tokens
-    // ascending within an expert; a slot per distinct expert, in ascending id
-    if (wave == 0) {
+    // gather layout, from the picked-expert bitmaps, in every wavefront (no
+    // barrier after it): rows grouped by expert in ascending id, tokens
+    // ascending within an expert; a slot per distinct expert, in ascending id.
+    // A pick's row is the number of picks (of both tokens) with a lower id,
+    // plus one for the second token of an expert both picked; its slot the
+    // number of distinct experts with a lower id.
+    {
       const bool ok = lane < P;
       const int t = lane >= K;
-      const int e = ok ? min(max(route_key_index(s_pick[lane]), 0), E - 1) : 0x7FFFFFFF;
-      int other = 0, below = 0;  // the other token picked e too; picks with a lower id
-      for (int qq = 0; qq < P; ++qq) {
-        const int eq = __builtin_amdgcn_readlane(e, qq);
-        other |= (eq == e) & ((qq >= K) != t);
-        below += eq < e;
-      }
-      int dup_below = 0;  // experts below e picked by both tokens (counted twice in `below`)
-      if (n > 1)
-        for (int qq = 0; qq < K; ++qq)
-          dup_below += __builtin_amdgcn_readlane(other, qq) & (__builtin_amdgcn_readlane(e, qq) < e);
-      const int slot = below - dup_below;
-      if (ok) {
-        s_id[lane] = e;
-        const int r = below + (t == 1 && other);
-        s_prow[lane] = r;
-        s_pslot[lane] = slot;
-        s_rt[r] = t;
-        if (t == 0 || !other) {
-          s_e[slot] = e;
-          s_r0[slot] = below;
-          s_rows[slot] = 1 + (t == 0 && other);
-          s_stok[slot][0] = t;
-          s_stok[slot][1] = 1;
+      const int e = ok ? min(max(route_key_index(s_pick[lane]), 0), E - 1) : 0;
+      const int ew = e >> 5;
+      int below = 0, below_u = 0, nact = 0;
+      uint32_t w0e = 0u, w1e = 0u;
+      for (int w = 0; w < (E + 31) >> 5; ++w) {
+        const uint32_t b0 = s_bits[0][w], b1 = n > 1 ? s_bits[1][w] : 0u;
+        const uint32_t m = w < ew ? 0xFFFFFFFFu : (w == ew ? (1u << (e & 31)) - 1u : 0u);
+        below += __builtin_popcount(b0 & m) + __builtin_popcount(b1 & m);
+        below_u += __builtin_popcount((b0 | b1) & m);
+        nact += __builtin_popcount(b0 | b1);
+        if (w == ew) {
+          w0e = b0;
+          w1e = b1;
         }
       }
-      const int nboth = (int)__popcll(__ballot(ok && t == 0 && other));
-      if (lane == 0) s_nact = P - nboth;
+      const bool other = ((t ? w0e : w1e) >> (e & 31)) & 1u;  // the other token picked e too
+      r_e = e;
+      r_t = t;
+      r_slot = below_u;
+      r_own = ok && (t == 0 || !other);
+      r_rows = 1 + (t == 0 && other);
+      r_nact = nact;
+      if (wave == 0 && ok) {  // the tables the reducer and the routing views read
+        const int r = below + (t == 1 && other);
+        s_id[lane] = e;
+        s_prow[lane] = r;
+        s_pslot[lane] = below_u;
+        s_rt[r] = t;
+        if (r_own) s_r0[below_u] = below;
+      }
     }
-    lds_barrier();
   };
   // The routing weights (wavefront 0), off the critical path: read after
-  // later barriers.
+  // later barriers.  The down globals the reducer scales by are requested
+  // here too and kept in registers until it runs, so their latency hides
+  // under the units.
+  float gl_pick = 0.f, gl_sh = 0.f;
   auto route_weights = [&]() {
     const float *s_logit = (const float *)((const uint64_t *)s_scr + 2 * kMaxRows * kKeyRow);
     if (wave == 0) {
       const bool ok = lane < P;
+      gl_pick = ok ? lp.down[1].global[s_id[lane]] : 0.f;
+      gl_sh = lp.has_shared ? lp.down[0].global[0] : 0.f;
       const int t = lane >= K;
       const float l = ok ? s_logit[t * E + s_id[lane]] : 0.f;
       const float l0 = t ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), K))
@@ -480,17 +509,15 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
     const int nout = up.n_out;
     const float gl_up = up.global[u.e];
     const int R = u.rows;
-    float acc[4 * NB][NR];
+    float acc[NR];  // tile my_t, per row
 #pragma unroll
-    for (int t = 0; t < 4 * NB; ++t)
-#pragma unroll
-      for (int r = 0; r < NR; ++r) acc[t][r] = 0.f;
+    for (int r = 0; r < NR; ++r) acc[r] = 0.f;
     u32x4_t x4[NR][4];
     f32x4_t x8[NR][8];
     f32x4_t hq[NR][8];
     uint64_t *part = (uint64_t *)lp.part + (size_t)(u.shared ? u.s : a.ns + u.slot * a.nr + u.s) * kMaxRows * d;
-    float *s_up = (float *)s_scr;                         // [4 NB][kMaxRows][8 waves][64 lanes]
-    float *s_usum = s_up + 4 * NB * kMaxRows * kThreads;  // [4 NB][kMaxRows][16]
+    float *s_up = (float *)s_scr;                         // [kMaxRows][8 waves][64 lanes]
+    float *s_usum = s_up + kMaxRows * kThreads;           // [4 NB][kMaxRows][16]
     float *s_h = s_usum + 4 * NB * kMaxRows * 16;         // [kMaxRows][64]
 #pragma unroll
     for (int i = 0; i < S; ++i) {
@@ -500,23 +527,20 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
       const u32x4_t w = ring[i % kWin].w;
       const uint32_t psc = ring[i % kWin].sc;
       if (i + kWin < S) ring[i % kWin] = load_piece(q, i + kWin);
-      if (i < SU) {  // ---- up piece (chunk iteration j, tile t)
-        const int j = i / (4 * NB), t = i % (4 * NB);
-        const int c = wave + kWaves * j;
+      if (i < SU) {  // ---- up piece: chunk c, tile my_t
+        const int c = (wave + kWaves * i) / TPC;
         if (c < a.dch) {  // uniform
           const int k0 = 128 * c + 32 * nq;
-          if (t == 0) {  // this chunk's x, all rows
 #pragma unroll
-            for (int r = 0; r < NR; ++r) {
-              if constexpr (XF) {
-                const f32x4_t *xs = (const f32x4_t *)(s_xb + ((size_t)u.tok[r] * a.x_stride + k0) * 4);
+          for (int r = 0; r < NR; ++r) {  // this chunk's x, all rows
+            if constexpr (XF) {
+              const f32x4_t *xs = (const f32x4_t *)(s_xb + ((size_t)u.tok[r] * a.x_stride + k0) * 4);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x8[r][e] = xs[e];
-              } else {
-                const u32x4_t *xs = (const u32x4_t *)(s_xb + ((size_t)u.tok[r] * a.x_stride + k0) * 2);
+              for (int e = 0; e < 8; ++e) x8[r][e] = xs[e];
+            } else {
+              const u32x4_t *xs = (const u32x4_t *)(s_xb + ((size_t)u.tok[r] * a.x_stride + k0) * 2);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x4[r][e] = xs[e];
-              }
+              for (int e = 0; e < 4; ++e) x4[r][e] = xs[e];
             }
           }
           float s0, s1;
@@ -525,28 +549,27 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
           for (int r = 0; r < NR; ++r) {
             if (r >= R) break;  // uniform
             if constexpr (XF) {
-              acc[t][r] = fmaf(s0, dot16v(w.x, w.y, x8[r][0], x8[r][1], x8[r][2], x8[r][3]), acc[t][r]);
-              acc[t][r] = fmaf(s1, dot16v(w.z, w.w, x8[r][4], x8[r][5], x8[r][6], x8[r][7]), acc[t][r]);
+              acc[r] = fmaf(s0, dot16v(w.x, w.y, x8[r][0], x8[r][1], x8[r][2], x8[r][3]), acc[r]);
+              acc[r] = fmaf(s1, dot16v(w.z, w.w, x8[r][4], x8[r][5], x8[r][6], x8[r][7]), acc[r]);
             } else {
-              acc[t][r] = fmaf(s0, dot16_bf16(w.x, w.y, x4[r][0], x4[r][1]), acc[t][r]);
-              acc[t][r] = fmaf(s1, dot16_bf16(w.z, w.w, x4[r][2], x4[r][3]), acc[t][r]);
+              acc[r] = fmaf(s0, dot16_bf16(w.x, w.y, x4[r][0], x4[r][1]), acc[r]);
+              acc[r] = fmaf(s1, dot16_bf16(w.z, w.w, x4[r][2], x4[r][3]), acc[r]);
             }
           }
         }
       }
-      if (i == SU - 1) {  // ---- the up sums of every wavefront and k-quarter, in a fixed order -> h
+      if (i == SU - 1) {  // ---- the up sums of the wavefronts and k-quarters of a tile, in a fixed order -> h
 #pragma unroll
-        for (int t = 0; t < 4 * NB; ++t)
-#pragma unroll
-          for (int r = 0; r < kMaxRows; ++r)
-            s_up[((t * kMaxRows + r) * kWaves + wave) * 64 + lane] = r < NR ? acc[t][r < NR ? r : 0] : 0.f;
+        for (int r = 0; r < kMaxRows; ++r) s_up[(r * kWaves + wave) * 64 + lane] = r < NR ? acc[r < NR ? r : 0] : 0.f;
         lds_barrier();
-        if (tid < 4 * NB * kMaxRows * 16) {
-          const float *pp = s_up + (tid >> 4) * kThreads;
+        if (tid < TPC * kMaxRows * 16) {  // (tile t, row r, column n): tid = (t kMaxRows + r) 16 + n
+          const int tr = tid >> 4, t = tr / kMaxRows, r = tr - t * kMaxRows;
+          const float *pp = s_up + r * kThreads + (tid & 15);
           float sum = 0.f;
-          for (int wv = 0; wv < kWaves; ++wv)
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) sum += pp[wv * 64 + qq * 16 + (tid & 15)];
+          for (int wv = t; wv < kWaves; wv += TPC)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) sum += pp[wv * 64 + qq * 16];
           s_usum[tid] = sum;
         }
         lds_barrier();
@@ -609,7 +632,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
     run_unit(u, q, ring);
   }
   route();
-  const int n_units = a.ns + s_nact * a.nr;
+  const int n_units = a.ns + r_nact * a.nr;
   bool weighted = false;
   for (int ui = blockIdx.x + (pre ? a.grid : 0); ui < n_units; ui += a.grid) {
     UnitRef u;
@@ -625,20 +648,31 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
     }
     run_unit(u, q, ring);
   }
-  if (!weighted) route_weights();
+  if (!weighted) {
+    route_weights();
+    lds_barrier();  // wavefront 0's layout tables, for the reducer
+  }
 
   // ---- reduce and combine output columns [16 cb, 16 cb + 16): each thread
   //      loads kSumGroup slices of two columns of one term (the shared
-  //      expert, then the picks), until all carry this launch's epoch
+  //      expert, then the picks), until all carry this launch's epoch.
+  //      (Dealing the column blocks first to the workgroups that finish early,
+  //      with 32-column blocks so that fewer workgroups reduce, was measured
+  //      slower: a poll round over twice the loads takes longer.)
+  constexpr int G2 = kRedCols / 2;  // two-column groups of a block
   const int terms = 1 + K;
-  const int items = n * terms * 8 * a.sgroups;
-  f32x2_t *s_yp = (f32x2_t *)s_scr;                                      // [n][terms][8][sgroups]
-  float *s_y = (float *)(s_yp + kMaxRows * (1 + MOE_MAX_TOPK) * 8 * a.sgroups);  // [n][terms][16]
+  const int items = n * terms * G2 * a.sgroups;
+  f32x2_t *s_yp = (f32x2_t *)s_scr;                                       // [n][terms][G2][sgroups]
+  float *s_y = (float *)(s_yp + kMaxRows * (1 + MOE_MAX_TOPK) * G2 * a.sgroups);  // [n][terms][kRedCols]
   const __amdgpu_buffer_rsrc_t pr =
       coherent_rsrc(lp.part, (size_t)n_units_max * kMaxRows * d * sizeof(uint64_t));
-  for (int cb = blockIdx.x; cb < a.dblk; cb += a.grid) {
+  if (wave == 0) {  // read after the first barrier below
+    if (lane < P) s_gl[lane] = gl_pick;
+    if (lane == 0) s_gl[kMaxPicks] = gl_sh;
+  }
+  for (int cb = blockIdx.x; cb < d / kRedCols; cb += a.grid) {
     for (int it = tid; it < items; it += kThreads) {
-      const int sg = it % a.sgroups, g = (it / a.sgroups) & 7, tt = it / (a.sgroups * 8);
+      const int sg = it % a.sgroups, g = (it / a.sgroups) % G2, tt = it / (a.sgroups * G2);
       const int t = tt / terms, term = tt - t * terms;
       int base, count, row;
       if (term == 0) {
@@ -657,7 +691,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
 #pragma unroll
       for (int i = 0; i < kSumGroup; ++i) {
         const int sl2 = min(s_lo + i, max(count - 1, 0));
-        off[i] = (uint32_t)((((size_t)(base + sl2) * kMaxRows + row) * d + 16 * cb + 2 * g) * 8);
+        off[i] = (uint32_t)((((size_t)(base + sl2) * kMaxRows + row) * d + kRedCols * cb + 2 * g) * 8);
         v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(pr, off[i], 0, kSc1));
       }
       for (int spins = 0;; ++spins) {
@@ -685,22 +719,21 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
       s_yp[it] = acc2;
     }
     lds_barrier();
-    if (tid < n * terms * 16) {
-      const int col = tid & 15, tt = tid >> 4, t = tt / terms, term = tt - t * terms;
-      const float gl = term == 0 ? (lp.has_shared ? lp.down[0].global[0] : 0.f)
-                                 : lp.down[1].global[s_id[t * K + term - 1]];
-      const f32x2_t *pp = s_yp + (size_t)(tt * 8 + (col >> 1)) * a.sgroups;
+    for (int c = tid; c < n * terms * kRedCols; c += kThreads) {
+      const int col = c % kRedCols, tt = c / kRedCols, t = tt / terms, term = tt - t * terms;
+      const float gl = term == 0 ? s_gl[kMaxPicks] : s_gl[t * K + term - 1];
+      const f32x2_t *pp = s_yp + (size_t)(tt * G2 + (col >> 1)) * a.sgroups;
       float y = 0.f;
       for (int sg = 0; sg < a.sgroups; ++sg) y += pp[sg][col & 1];
-      s_y[tid] = gl * y;
+      s_y[c] = gl * y;
     }
     lds_barrier();
-    if (tid < n * 16) {
-      const int t = tid >> 4, col = 16 * cb + (tid & 15);
-      const float *yt = s_y + (size_t)t * terms * 16 + (tid & 15);
+    if (tid < n * kRedCols) {
+      const int t = tid / kRedCols, col = kRedCols * cb + tid % kRedCols;
+      const float *yt = s_y + (size_t)t * terms * kRedCols + tid % kRedCols;
       float accw = 0.f;
       for (int j = 0; j < K; ++j) {
-        const float y = yt[(1 + j) * 16];
+        const float y = yt[(1 + j) * kRedCols];
         accw = fmaf(s_pw[t * K + j], y, accw);
         lp.yg[(size_t)s_prow[t * K + j] * d + col] = y;
       }
@@ -740,7 +773,7 @@ __global__ void k_zero_words_long(int32_t *w, long n) {
 // unit's up sums and h slice.
 size_t scratch_bytes(int NB) {
   const size_t route = (size_t)kMaxRows * kKeyRow * 16 + (size_t)kMaxRows * MOE_MAX_EXPERTS * 4 + (size_t)kMaxPicks * 8;
-  const size_t up = (size_t)4 * NB * kMaxRows * (kThreads + 16) * 4 + (size_t)kMaxRows * kSlice * 4;
+  const size_t up = ((size_t)kMaxRows * kThreads + (size_t)4 * NB * kMaxRows * 16 + (size_t)kMaxRows * kSlice) * 4;
   return std::max(route, up);
 }
 
@@ -885,8 +918,8 @@ hipError_t launch_decode_layer(const DecodeLayerProblem &lp, hipStream_t stream)
   a.sgroups = (std::max(a.ns, a.nr) + kSumGroup - 1) / kSumGroup;
   a.x_stride = a.dch * 128;
   a.x_lds = (int)((size_t)n * a.x_stride * (lp.x_f32 ? 4 : 2));
-  const size_t reduce = (size_t)kMaxRows * (1 + MOE_MAX_TOPK) * 8 * a.sgroups * 8 +
-                        (size_t)kMaxRows * (1 + MOE_MAX_TOPK) * 16 * 4;
+  const size_t reduce = (size_t)kMaxRows * (1 + MOE_MAX_TOPK) * (kRedCols / 2) * a.sgroups * 8 +
+                        (size_t)kMaxRows * (1 + MOE_MAX_TOPK) * kRedCols * 4;
   const size_t lds = (size_t)a.x_lds + std::max(scratch_bytes(swiglu ? 2 : 1), reduce);
   int cus = 0, dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidValue;
