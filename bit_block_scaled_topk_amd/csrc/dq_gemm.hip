@@ -249,15 +249,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t co;
-      if constexpr (SM == 3) {  // the block's chunk: 2 halves x 16 rows x 32 bytes
+      if constexpr (SM == 3) {  // the block's chunk: 2 halves x 16 rows x 32 bytes, zero past K (no test)
         const uint32_t blk = (uint32_t)((wrow0 - nl + dj[j]) >> 4) * nch_c + (uint32_t)(k0 >> 7);
-        co = b_in ? blk * 1024u + (uint32_t)(q >> 1) * 512u + (uint32_t)nl * 32u + 16u * (uint32_t)(q & 1) : OOB;
+        co = blk * 1024u + (uint32_t)(q >> 1) * 512u + (uint32_t)nl * 32u + 16u * (uint32_t)(q & 1);
       } else
         co = b_in ? c_off0 + (uint32_t)(dj[j] * (K >> 1)) + (uint32_t)(k0 >> 1) : OOB;
       rc[j] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, co, 0, 0);
       uint32_t so;
-      if constexpr (SM >= 2)  // this lane's row's 16-row block, chunk k0 / 128
-        so = s_in ? s_off0 + ((uint32_t)((wrow0 - nl + dj[j]) >> 4) * nch + (uint32_t)(k0 >> 7)) * 128u : OOB;
+      if constexpr (SM >= 2)  // this lane's row's 16-row block, chunk k0 / 128 (zero past K: no test)
+        so = s_off0 + ((uint32_t)((wrow0 - nl + dj[j]) >> 4) * nch + (uint32_t)(k0 >> 7)) * 128u;
       else
         so = s_in ? s_off0 + (uint32_t)(dj[j] * (K >> 4)) + (uint32_t)(k0 >> 4) : OOB;
       if constexpr (SP) {

@@ -232,7 +232,10 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
     const int c = tid + kThreads * i;
     if (c < n * xpr) xv[i] = *((const u32x4_t *)lp.x + c);
   }
-  const int32_t epoch = __hip_atomic_load(&flags[blockIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // this launch's count, requested after the shared expert's first weights
+  // (below): used only when partial sums are stored and compared, so that no
+  // wait for it holds back the weight requests
+  int32_t epoch = 0;
 
   // ---- a unit's weights.  Pieces in a fixed order -- the up pieces, then
   //      the down block pairs -- and a window of kWin loads in flight: piece
@@ -503,7 +506,6 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
 
   // ---- one unit: up rows -> h slice (LDS) -> down partials (stored with
   //      the epoch).  ring holds the first kWin pieces on entry.
-  const uint32_t epoch1 = (uint32_t)epoch + 1u;
   auto run_unit = [&](const UnitRef &u, const UnitSrc &q, Piece (&ring)[kWin]) {
     const ProjProblem &up = u.shared ? lp.up[0] : lp.up[1];
     const int nout = up.n_out;
@@ -603,7 +605,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
             v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
             if (dq == 0 && blk < a.dblk)
               __hip_atomic_store(part + (size_t)r * d + 16 * blk + dr,
-                                 ((uint64_t)epoch1 << 32) | (uint64_t)__float_as_uint(v), __ATOMIC_RELAXED,
+                                 ((uint64_t)((uint32_t)epoch + 1u) << 32) | (uint64_t)__float_as_uint(v), __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
           }
         }
@@ -622,14 +624,17 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
     for (int i = 0; i < kWin; ++i) ring[i] = load_piece(q, i);
   };
   const bool pre = (int)blockIdx.x < a.ns;
-  if (pre) {
+  if (pre) {  // one block from the requests to the unit, so each wait counts the loads in flight
     UnitRef u;
     UnitSrc q;
     resolve(blockIdx.x, u);
     start_unit(u, q);
+    epoch = __hip_atomic_load(&flags[blockIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     stage_x();
     lds_barrier();
     run_unit(u, q, ring);
+  } else {
+    epoch = __hip_atomic_load(&flags[blockIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   route();
   const int n_units = a.ns + r_nact * a.nr;
@@ -698,7 +703,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
         bool ready = true;
 #pragma unroll
         for (int i = 0; i < kSumGroup; ++i)
-          if (s_lo + i < count) ready &= v[i].y == epoch1 && v[i].w == epoch1;
+          if (s_lo + i < count) ready &= v[i].y == (uint32_t)epoch + 1u && v[i].w == (uint32_t)epoch + 1u;
         if (ready) break;
         if (spins >= kSpinLimit) {
           __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
