@@ -342,8 +342,8 @@ def bench_decode(name, args, ops, synth):
         ach = b["total"] / (step_us * 1e-6) / 1e9
         out["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(ach / HBM_PEAK_GBS, 4),
-                           "traffic": measured_traffic("k_decode_layer", name, DECODE_KERNEL_SOURCES),
-                           "kernel": "k_decode_layer (the whole decode step in one persistent launch)",
+                           "traffic": measured_traffic("k_decode_step", name, DECODE_KERNEL_SOURCES),
+                           "kernel": "k_decode_step (the whole decode step in one persistent launch)",
                            "bytes_per_launch": b["total"], "us_per_launch": round(step_us, 3), "bytes": b}
     else:
         # the weight-streaming launches of k_dq_gemv (one up, one down), timed
