@@ -31,20 +31,20 @@
 // 128-wide k chunk, two 64-wide halves of 16 rows x 32 bytes of codes (1 KB in
 // all) and of 16 rows x 4 scales (128 B in all).  Up rows: one load of a
 // wavefront reads a whole chunk of one block -- lane (n, q) = (l % 16, l / 16)
-// gets row n's codes for k = 128 c + 32 q .. + 31; chunk c goes to wavefront
-// c % 8.  Down: one load covers the unit's k-slice of two blocks, which is one
-// half of a chunk, 512 contiguous bytes per block -- lane l takes block
-// 2 p + l / 32, row (l % 32) / 2 and quarter l % 2 of the slice; block pair p
-// goes to wavefront p % 8.  Each piece's two scales come with it (a 2-byte
-// load).  The dot products run on
-// the vector ALUs
-// in fp32 (bf16 x through the bf16 dot instruction: exact products, fp32
-// sums), each 16-element block's sum scaled by its e4m3 scale.  (A
-// matrix-core tile would be 1/16 used here, and gfx950's FP4 converters apply
-// only the exponent of a scale, so an exact bf16 decode would cost more ALU
-// work than these dot products.)  The up sums of the 8 wavefronts x 4
-// k-quarters meet in LDS and are added in a fixed order; the two halves of a
-// down row by one DPP move.
+// gets row n's codes for k = 128 c + 32 q .. + 31; the unit's (chunk, tile)
+// pieces, tile fastest, are dealt round-robin to the wavefronts, so each
+// wavefront keeps one tile.  Down: one load covers the unit's k-slice of two
+// blocks, which is one half of a chunk, 512 contiguous bytes per block --
+// lane l takes block 2 p + l / 32, row (l % 32) / 2 and quarter l % 2 of the
+// slice; block pair p goes to wavefront p % 8.  Each piece's two scales come
+// with it (a 2-byte load).  The dot products run on the vector ALUs in fp32
+// (bf16 x through the bf16 dot instruction: exact products, fp32 sums), each
+// 16-element block's sum scaled by its e4m3 scale.  (A matrix-core tile would
+// be 1/16 used here, and gfx950's FP4 converters apply only the exponent of a
+// scale, so an exact bf16 decode would cost more ALU work than these dot
+// products.)  The up sums of a tile's wavefronts and 4 k-quarters meet in LDS
+// and are added in a fixed order; the two halves of a down row by one DPP
+// move.
 //
 // sync[0] is the error word, sync[1] the launch count, sync[2 + w] workgroup
 // w's launch count, read at start (e) and stored as e + 1 at the end: e + 1
