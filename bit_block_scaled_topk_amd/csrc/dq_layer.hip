@@ -221,7 +221,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
   const int n = lp.n_tokens, d = lp.d, E = lp.n_experts, K = lp.top_k, P = n * K, NE = n * E;
   const int n_units_max = a.ns + lp.max_slots * a.nr;
 
-  // ---- the logits, x and this launch's count first: everything waits on them
+  // ---- the logits and x first: everything waits on them
   float lg[kLogitsPerThread];
 #pragma unroll
   for (int i = 0; i < kLogitsPerThread; ++i) lg[i] = lp.logits[min(tid + kThreads * i, NE - 1)];

@@ -665,8 +665,9 @@ def test_layer_forward_fused(ops, name):
 # Decode steps the single-launch layer takes (one or two tokens): tiny shapes
 # (fp32 x) with every expert holding both rows, one expert, k-slices that leave
 # wavefronts empty; realistic shapes with a skewed router, without a shared
-# expert and with the gated FFN (bf16 x).  The last case (seven tokens) falls
-# back to the per-step launches.
+# expert and with the gated FFN (bf16 x); the gated FFN with fp32 x, also with
+# a ragged last chunk (d 160) and a half-filled last unit (d_ff 96).  The last
+# case (seven tokens) falls back to the per-step launches.
 SINGLE_LAUNCH_CASES = [
     ("tiny16", dict(n=1, seed=11), True),
     ("tiny16", dict(n=2, E=4, K=4, seed=12), True),
@@ -675,6 +676,8 @@ SINGLE_LAUNCH_CASES = [
     ("decode1", dict(n=2, K=2, E=32, fs=1856, logits="zipf", seed=15), True),
     ("decode1", dict(n=1, E=32, fs=0, seed=16), True),
     ("gated2", dict(n=1, seed=17), True),
+    ("tiny16", dict(n=2, act="swiglu", fs=0, seed=19), True),
+    ("tiny16", dict(n=1, act="swiglu", fs=0, d=160, f=96, seed=20), True),
     ("decode1", dict(n=7, E=32, fs=0, seed=18), False),
 ]
 
