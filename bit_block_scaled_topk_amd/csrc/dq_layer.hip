@@ -82,6 +82,20 @@ constexpr int kSumGroup = 8;           // slices one reducer thread adds
 constexpr int kRedCols = 16;           // output columns one reducer block combines
 constexpr int kWin = 8;                // weight loads in flight per wavefront
 constexpr int kKeyRow = 2 * MOE_MAX_EXPERTS;  // routing keys of one token, padded
+// LDS of a wavefront's scale copies, in whole 1 KB buffer-to-LDS loads (every
+// lane writes its 16 bytes, zeros past the data): the up scales of one block,
+// every chunk (kMaxD / 128 chunks x 128 B), then the down scales of up to 12
+// block pairs (2 blocks x 64 B each, 1.5 KB in two loads).
+constexpr int kScUp = (kMaxD / 128 * 128 + 1023) / 1024 * 1024;
+constexpr int kScW = kScUp + (12 * 2 * 64 + 1023) / 1024 * 1024;
+constexpr int kOob = 0x40000000;               // a buffer offset past every extent: the load reads nothing
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from a buffer straight into LDS: lane l writes dst + 16 l
+// (dst the same for the whole wavefront).
+__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint8_t *dst, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)dst, 16, voffset, 0, 0, 0);
+}
 
 struct StepArgs {
   DecodeLayerProblem lp;
@@ -99,6 +113,7 @@ struct StepArgs {
   int sgroups;   // reducer: groups of kSumGroup slices (of the wider expert)
   int x_stride;  // elements of one token's x in LDS (dch * 128, zero-padded)
   int x_lds;     // LDS bytes of x
+  int sc_off;    // LDS byte offset of the wavefronts' scale regions (kScW each)
 };
 
 // Workgroup barrier for LDS only: unlike __syncthreads it does not wait for
@@ -218,6 +233,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
   int32_t *flags = lp.sync + 2;
   uint8_t *s_xb = (uint8_t *)s_dyn;    // x
   uint8_t *s_scr = s_xb + a.x_lds;     // phase scratch
+  uint8_t *my_sc = (uint8_t *)s_dyn + a.sc_off + wave * kScW;  // this wavefront's scales of the unit
   const int n = lp.n_tokens, d = lp.d, E = lp.n_experts, K = lp.top_k, P = n * K, NE = n * E;
   const int n_units_max = a.ns + lp.max_slots * a.nr;
 
@@ -251,6 +267,8 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
   //      register for all pieces, the rest a scalar offset.
   constexpr int TPC = 4 * NB;  // up tiles per chunk
   constexpr int SU = CU * TPC, S = SU + DP;
+  static_assert(CU * 1024 <= kScUp && (DP * 8 + 63) / 64 * 1024 <= kScW - kScUp,
+                "a wavefront's scale loads stay inside its LDS region");
   const int my_t = wave % TPC;  // this wavefront's up tile
   const int nq = lane >> 4, nn = lane & 15;                        // up: k-quarter, row
   const int dq = lane & 1, dr = (lane & 31) >> 1, dh = lane >> 5;  // down: slice half, row, block of the pair
@@ -275,20 +293,22 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
                       (uint32_t)((size_t)a.dblk * q.dnch * 128));
     return q;
   };
-  // piece i (a compile-time index) of the unit: 16 bytes of codes and the two
-  // scales of those 32 k (the low byte for the first 16)
+  // piece i (a compile-time index) of the unit: 16 bytes of codes.  Its two
+  // scales (the low byte for the first 16 k) are read from the wavefront's
+  // LDS copy of the unit's scales, which start_unit requests with a few
+  // buffer-to-LDS loads (a 2-byte load per piece cost about a sixth of the
+  // stream's time: a request per piece for 128 bytes).
   struct Piece {
     u32x4_t w;
-    uint32_t sc;
   };
-  const int up_ls = (nq >> 1) * 64 + nn * 4 + (nq & 1) * 2;
+  const int up_ls = (nq >> 1) * 64 + nn * 4 + (nq & 1) * 2;   // a lane's scales in a block-chunk
+  const int dn_ls = dh * 64 + dr * 4 + dq * 2;                 // ... in a block pair's down scales
   auto load_piece = [&](const UnitSrc &q, int i) -> Piece {
     Piece p;
     if (i < SU) {
       const int c = min((wave + kWaves * i) / TPC, a.dch - 1), blk = min(4 * q.s + (my_t & 3), q.nb_out - 1);
       const int piece = ((my_t >> 2) * q.nb_out + blk) * a.dch + c;
       p.w = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(q.uc, up_lc, piece * 1024, 0));
-      p.sc = __builtin_amdgcn_raw_buffer_load_b16(q.us, up_ls, piece * 128, 0);
       return p;
     }
     const int jj = i - SU;
@@ -296,11 +316,9 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
     // block 2 pr + dh (the first block of a half-used last pair), row dr, half dq
     const bool whole = 2 * pr + 1 < a.dblk;
     const int lc = (whole ? dh * q.dnch * 1024 : 0) + dr * 32 + dq * 16;
-    const int ls = (whole ? dh * q.dnch * 128 : 0) + dr * 4 + dq * 2;
     const int piece = 2 * pr * q.dnch + (q.s >> 1);
     p.w = __builtin_bit_cast(u32x4_t,
                              __builtin_amdgcn_raw_buffer_load_b128(q.dc, lc, piece * 1024 + (q.s & 1) * 512, 0));
-    p.sc = __builtin_amdgcn_raw_buffer_load_b16(q.dsc, ls, piece * 128 + (q.s & 1) * 64, 0);
     return p;
   };
 
@@ -527,7 +545,6 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
       // pieces' decode and LDS reads, and runs out of registers
       __builtin_amdgcn_sched_barrier(0);
       const u32x4_t w = ring[i % kWin].w;
-      const uint32_t psc = ring[i % kWin].sc;
       if (i + kWin < S) ring[i % kWin] = load_piece(q, i + kWin);
       if (i < SU) {  // ---- up piece: chunk c, tile my_t
         const int c = (wave + kWaves * i) / TPC;
@@ -546,7 +563,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
             }
           }
           float s0, s1;
-          e4m3x2_to_f32(psc, s0, s1);
+          e4m3x2_to_f32(*(const uint16_t *)(my_sc + c * 128 + up_ls), s0, s1);
 #pragma unroll
           for (int r = 0; r < NR; ++r) {
             if (r >= R) break;  // uniform
@@ -596,7 +613,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
         const int jj = i - SU, pr = wave + kWaves * jj, blk = 2 * pr + dh;
         if (2 * pr < a.dblk) {  // uniform
           float s0, s1;
-          e4m3x2_to_f32(psc, s0, s1);
+          e4m3x2_to_f32(*(const uint16_t *)(my_sc + kScUp + jj * 128 + dn_ls), s0, s1);
 #pragma unroll
           for (int r = 0; r < NR; ++r) {
             if (r >= R) break;  // uniform
@@ -620,6 +637,26 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
   Piece ring[kWin];
   auto start_unit = [&](const UnitRef &u, UnitSrc &q) {
     q = unit_src(u);
+    // this wavefront's scales, into its LDS region: the up tile's block for
+    // every chunk (dch x 128 contiguous bytes), then its block pairs' down
+    // scales (the unit's 64-wide half of one chunk: 64 bytes per block)
+    {
+      const int blk = min(4 * q.s + (my_t & 3), q.nb_out - 1);
+      const int base = ((my_t >> 2) * q.nb_out + blk) * a.dch * 128, nbytes = a.dch * 128;
+#pragma unroll
+      for (int k = 0; k < CU; ++k) {  // dch <= 8 CU chunks: CU x 1 KB
+        const int off = (k * 64 + lane) * 16;
+        load16_to_lds(q.us, my_sc + k * 1024, off < nbytes ? base + off : kOob);
+      }
+#pragma unroll
+      for (int k = 0; k < (DP * 8 + 63) / 64; ++k) {  // DP pairs x 2 blocks x 4 lanes of 16 bytes
+        const int g = k * 64 + lane, jj = g >> 3, hb = (g >> 2) & 1;
+        const int pr = min(wave + kWaves * jj, (a.dblk - 1) >> 1);
+        const int b = 2 * pr + (2 * pr + 1 < a.dblk ? hb : 0);  // the first block of a half-used last pair
+        const int off = (b * q.dnch + (q.s >> 1)) * 128 + (q.s & 1) * 64 + (g & 3) * 16;
+        load16_to_lds(q.dsc, my_sc + kScUp + k * 1024, g < DP * 8 ? off : kOob);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < kWin; ++i) ring[i] = load_piece(q, i);
   };
@@ -925,7 +962,9 @@ hipError_t launch_decode_layer(const DecodeLayerProblem &lp, hipStream_t stream)
   a.x_lds = (int)((size_t)n * a.x_stride * (lp.x_f32 ? 4 : 2));
   const size_t reduce = (size_t)kMaxRows * (1 + MOE_MAX_TOPK) * (kRedCols / 2) * a.sgroups * 8 +
                         (size_t)kMaxRows * (1 + MOE_MAX_TOPK) * kRedCols * 4;
-  const size_t lds = (size_t)a.x_lds + std::max(scratch_bytes(swiglu ? 2 : 1), reduce);
+  a.sc_off = (int)((size_t)a.x_lds + std::max(scratch_bytes(swiglu ? 2 : 1), reduce));
+  a.sc_off = (a.sc_off + 15) / 16 * 16;
+  const size_t lds = (size_t)a.sc_off + (size_t)kWaves * kScW;
   int cus = 0, dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidValue;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
