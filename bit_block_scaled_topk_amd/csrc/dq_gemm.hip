@@ -9,6 +9,8 @@
 // expert_offsets, so the host never reads routing results.  The weights are
 // decoded in registers straight into MFMA operands (no bf16 copy in LDS or
 // HBM); only the activation tile is staged through LDS.
+#include <type_traits>
+
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
@@ -281,12 +283,42 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // chunks the roles swap; the explicit vmcnt(0) and barrier at the top of
   // each chunk order those accesses.  The activation resource is built here
   // from a restrict pointer so that the loads carry their own alias scope.
-  auto chunk = [&](const uint8_t *__restrict__ cur, uint8_t *__restrict__ nxt, const void *__restrict__ a_src, int k0) {
+  // The expert's global, requested before the first chunk's operands (its
+  // wait then comes with theirs).
+  const float gl_v = p.global[e];
+  // f32 outputs whose 16-byte row pieces are aligned, with no combine, are
+  // stored during the last chunk: each fragment's 16 rows as soon as its last
+  // MFMAs are issued, so the stores drain under the chunk's remaining MFMAs
+  // instead of after them (a wavefront ends only once its stores complete).
+  // The resource ends at the tile's last row (rows past it are dropped);
+  // columns past n_out take an offset past every extent.
+  const bool early = EPI == EPI_F32 && !batch.cmb.on && ((uintptr_t)p.out_f32 & 15) == 0 && p.ldo % 4 == 0 &&
+                     p.n_out % 4 == 0 && (size_t)BM * p.ldo * 4 < (1u << 31);
+  const __amdgpu_buffer_rsrc_t st_rsrc =
+      make_rsrc(early ? p.out_f32 + (size_t)r0 * p.ldo : nullptr, early ? (uint32_t)(mrows * p.ldo * 4) : 0u);
+  auto store_frag = [&](int i, float g) {
+    if constexpr (EPI == EPI_F32) {
+      if (!early) return;
+      const int c0 = nt * BN + wave * 64;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = c0 + 16 * j + 4 * q;
+        const uint32_t voff = (uint32_t)(16 * i + nl) * (uint32_t)(p.ldo * 4) + (col < p.n_out ? 4u * col : OOB);
+        const f32x4_t v = {g * acc[i][j][0], g * acc[i][j][1], g * acc[i][j][2], g * acc[i][j][3]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), st_rsrc, voff, 0, 0);
+      }
+    }
+  };
+
+  auto chunk = [&](auto last, const uint8_t *__restrict__ cur, uint8_t *__restrict__ nxt,
+                   const void *__restrict__ a_src, int k0) {
+    constexpr bool LAST = decltype(last)::value;
     // SP: the chunk's place in its pair; the pair's scales (loaded with the
     // pair's first chunk's codes) stay in rs32 through both of its chunks, and
     // the next pair's are requested only after this copy
     const int par = (k0 / BK) & 1;
     loads_done_barrier();
+    const float gs = LAST ? __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, gl_v))) : 0.f;
     u32x4_t cc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -336,24 +368,32 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int j = 0; j < 4; ++j) bw[j] = bn[j];
       }
+      if constexpr (LAST)
+        if (st == 3 && i > 0) store_frag(i - 1, gs);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (LAST) store_frag(7, gs);
   };
 
   load(0, sA, make_rsrc(p.a, p.a_bytes), true);
-  for (int k0 = 0, buf = 0; k0 < K; k0 += BK, buf ^= 1) chunk(sA + buf * A_BYTES, sA + (buf ^ 1) * A_BYTES, p.a, k0);
+  int k0 = 0, buf = 0;
+  for (; k0 + BK < K; k0 += BK, buf ^= 1)
+    chunk(std::false_type{}, sA + buf * A_BYTES, sA + (buf ^ 1) * A_BYTES, p.a, k0);
+  chunk(std::true_type{}, sA + buf * A_BYTES, sA + (buf ^ 1) * A_BYTES, p.a, k0);
+  if (early) return;
 
   // Epilogue.  f32 outputs (transposed product): lane holds D[m = 16 i + nl]
   // [column 16 j + 4 q + r of the wavefront], r = 0..3, written with one
   // 16-byte store per (i, j); four 4-byte element stores per lane, as the
-  // other order gives, cost the down projection about 9 % of its time.
+  // other order gives, cost the down projection about 9 % of its time.  The
+  // aligned case without the combine has stored them during the last chunk.
   // Other outputs: lane holds D[m = 16 i + 4 q + r][column 16 j + nl of the
   // wavefront].  A bf16 h tile is staged in LDS (the activation buffers are
   // free now) and written back as whole rows with 16-byte stores: 2-byte
   // element stores of 16-column row pieces cost the up projection about a
   // quarter of its time.  Both take 16-byte aligned rows whose width n_out is
   // a whole number of 16-byte chunks; other outputs get element stores.
-  const float gl = p.global[e];
+  const float gl = gl_v;
   auto value = [&](int i, int j, int r) -> float {  // the output of accumulator (i, j, r)
     if (EPI == EPI_F32) return gl * acc[i][j][r];
     if (EPI == EPI_SWIGLU) {
