@@ -78,6 +78,12 @@ constexpr int kSyncWords = 2 + kMaxGrid;
 constexpr int kMaxD = 3072;            // d_model the register tiles cover
 constexpr int kLogitsPerThread = kMaxRows * MOE_MAX_EXPERTS / kThreads;
 constexpr int kXLoads = kMaxRows * kMaxD * 4 / 16 / kThreads;  // 16-byte pieces of x per thread (fp32 x)
+// Floats of a unit's up partial sums in LDS: per row, wavefront and lane
+// (one tile per wavefront), or, when the up pieces go chunk-fastest, per tile,
+// wavefront, row and column (4 NB tiles).
+constexpr int up_part_floats(int NB) {
+  return kMaxRows * kThreads > 4 * NB * kWaves * kMaxRows * 16 ? kMaxRows * kThreads : 4 * NB * kWaves * kMaxRows * 16;
+}
 constexpr int kSumGroup = 8;           // slices one reducer thread adds
 constexpr int kRedCols = 16;           // output columns one reducer block combines
 constexpr int kWin = 8;                // weight loads in flight per wavefront
@@ -217,7 +223,7 @@ struct UnitRef {
   int tok[kMaxRows];     // token of each row
 };
 
-template <int NB, int NR, bool XF, int CU, int DP>
+template <int NB, int NR, bool XF, int CU, int DP, bool CF>
 __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
   extern __shared__ u32x4_t s_dyn[];  // x | phase scratch
   __shared__ int s_id[kMaxPicks], s_prow[kMaxPicks], s_pslot[kMaxPicks];  // per pick t*K + j
@@ -270,6 +276,14 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
   static_assert(CU * 1024 <= kScUp && (DP * 8 + 63) / 64 * 1024 <= kScW - kScUp,
                 "a wavefront's scale loads stay inside its LDS region");
   const int my_t = wave % TPC;  // this wavefront's up tile
+  // CF (chunk-fastest; dch = 8 CU): up piece i of every wavefront is tile
+  // i / CU, chunk wave + 8 (i % CU), so that in each round the wavefronts
+  // read 8 adjacent chunks of one 16-row block and a workgroup's loads in
+  // flight cover one contiguous stretch of its unit's blocks; each wavefront
+  // then holds a partial sum of every tile.  Otherwise piece i is tile my_t,
+  // chunk (wave + 8 i) / TPC (past the chunks: absent).
+  auto up_tile = [&](int i) { return CF ? i / CU : my_t; };
+  auto up_chunk = [&](int i) { return CF ? wave + kWaves * (i % CU) : (wave + kWaves * i) / TPC; };
   const int nq = lane >> 4, nn = lane & 15;                        // up: k-quarter, row
   const int dq = lane & 1, dr = (lane & 31) >> 1, dh = lane >> 5;  // down: slice half, row, block of the pair
   const int up_lc = (nq >> 1) * 512 + nn * 32 + (nq & 1) * 16;
@@ -306,8 +320,8 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
   auto load_piece = [&](const UnitSrc &q, int i) -> Piece {
     Piece p;
     if (i < SU) {
-      const int c = min((wave + kWaves * i) / TPC, a.dch - 1), blk = min(4 * q.s + (my_t & 3), q.nb_out - 1);
-      const int piece = ((my_t >> 2) * q.nb_out + blk) * a.dch + c;
+      const int tt = up_tile(i), c = min(up_chunk(i), a.dch - 1), blk = min(4 * q.s + (tt & 3), q.nb_out - 1);
+      const int piece = ((tt >> 2) * q.nb_out + blk) * a.dch + c;
       p.w = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(q.uc, up_lc, piece * 1024, 0));
       return p;
     }
@@ -529,15 +543,15 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
     const int nout = up.n_out;
     const float gl_up = up.global[u.e];
     const int R = u.rows;
-    float acc[NR];  // tile my_t, per row
+    float acc[NR];  // tile up_tile(i), per row
 #pragma unroll
     for (int r = 0; r < NR; ++r) acc[r] = 0.f;
     u32x4_t x4[NR][4];
     f32x4_t x8[NR][8];
     f32x4_t hq[NR][8];
     uint64_t *part = (uint64_t *)lp.part + (size_t)(u.shared ? u.s : a.ns + u.slot * a.nr + u.s) * kMaxRows * d;
-    float *s_up = (float *)s_scr;                         // [kMaxRows][8 waves][64 lanes]
-    float *s_usum = s_up + kMaxRows * kThreads;           // [4 NB][kMaxRows][16]
+    float *s_up = (float *)s_scr;                         // up_part_floats(NB): the partial sums
+    float *s_usum = s_up + up_part_floats(NB);            // [4 NB][kMaxRows][16]
     float *s_h = s_usum + 4 * NB * kMaxRows * 16;         // [kMaxRows][64]
 #pragma unroll
     for (int i = 0; i < S; ++i) {
@@ -546,9 +560,9 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       const u32x4_t w = ring[i % kWin].w;
       if (i + kWin < S) ring[i % kWin] = load_piece(q, i + kWin);
-      if (i < SU) {  // ---- up piece: chunk c, tile my_t
-        const int c = (wave + kWaves * i) / TPC;
-        if (c < a.dch) {  // uniform
+      if (i < SU) {  // ---- up piece: chunk c of tile up_tile(i)
+        const int c = up_chunk(i);
+        if (c < a.dch) {  // uniform (always with CF)
           const int k0 = 128 * c + 32 * nq;
 #pragma unroll
           for (int r = 0; r < NR; ++r) {  // this chunk's x, all rows
@@ -563,7 +577,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
             }
           }
           float s0, s1;
-          e4m3x2_to_f32(*(const uint16_t *)(my_sc + c * 128 + up_ls), s0, s1);
+          e4m3x2_to_f32(*(const uint16_t *)(my_sc + (CF ? i : c) * 128 + up_ls), s0, s1);
 #pragma unroll
           for (int r = 0; r < NR; ++r) {
             if (r >= R) break;  // uniform
@@ -576,19 +590,39 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
             }
           }
         }
+        if constexpr (CF) {
+          if (i % CU == CU - 1) {  // the wavefront's last piece of tile i / CU: its sums over the k-quarters
+            const int tt = i / CU;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+              float v = acc[r];
+              v += __shfl_xor(v, 16);
+              v += __shfl_xor(v, 32);
+              if (nq == 0) s_up[((tt * kWaves + wave) * kMaxRows + r) * 16 + nn] = v;
+              acc[r] = 0.f;
+            }
+          }
+        }
       }
       if (i == SU - 1) {  // ---- the up sums of the wavefronts and k-quarters of a tile, in a fixed order -> h
+        if constexpr (!CF) {
 #pragma unroll
-        for (int r = 0; r < kMaxRows; ++r) s_up[(r * kWaves + wave) * 64 + lane] = r < NR ? acc[r < NR ? r : 0] : 0.f;
+          for (int r = 0; r < kMaxRows; ++r) s_up[(r * kWaves + wave) * 64 + lane] = r < NR ? acc[r < NR ? r : 0] : 0.f;
+        }
         lds_barrier();
         if (tid < TPC * kMaxRows * 16) {  // (tile t, row r, column n): tid = (t kMaxRows + r) 16 + n
           const int tr = tid >> 4, t = tr / kMaxRows, r = tr - t * kMaxRows;
-          const float *pp = s_up + r * kThreads + (tid & 15);
           float sum = 0.f;
+          if constexpr (CF) {  // rows past NR are never read
 #pragma unroll
-          for (int wv = t; wv < kWaves; wv += TPC)
+            for (int wv = 0; wv < kWaves; ++wv) sum += s_up[((t * kWaves + wv) * kMaxRows + r) * 16 + (tid & 15)];
+          } else {
+            const float *pp = s_up + r * kThreads + (tid & 15);
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) sum += pp[wv * 64 + qq * 16];
+            for (int wv = t; wv < kWaves; wv += TPC)
+#pragma unroll
+              for (int qq = 0; qq < 4; ++qq) sum += pp[wv * 64 + qq * 16];
+          }
           s_usum[tid] = sum;
         }
         lds_barrier();
@@ -640,7 +674,14 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
     // this wavefront's scales, into its LDS region: the up tile's block for
     // every chunk (dch x 128 contiguous bytes), then its block pairs' down
     // scales (the unit's 64-wide half of one chunk: 64 bytes per block)
-    {
+    if constexpr (CF) {  // the block-chunk (128 bytes) of each of its SU = 8 CU pieces: CU x 1 KB
+#pragma unroll
+      for (int k = 0; k < CU; ++k) {
+        const int pi = 8 * k + (lane >> 3), tt = pi / CU, c = wave + kWaves * (pi % CU);
+        const int blk = min(4 * q.s + (tt & 3), q.nb_out - 1);
+        load16_to_lds(q.us, my_sc + k * 1024, (((tt >> 2) * q.nb_out + blk) * a.dch + c) * 128 + (lane & 7) * 16);
+      }
+    } else {
       const int blk = min(4 * q.s + (my_t & 3), q.nb_out - 1);
       const int base = ((my_t >> 2) * q.nb_out + blk) * a.dch * 128, nbytes = a.dch * 128;
 #pragma unroll
@@ -648,6 +689,8 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
         const int off = (k * 64 + lane) * 16;
         load16_to_lds(q.us, my_sc + k * 1024, off < nbytes ? base + off : kOob);
       }
+    }
+    {
 #pragma unroll
       for (int k = 0; k < (DP * 8 + 63) / 64; ++k) {  // DP pairs x 2 blocks x 4 lanes of 16 bytes
         const int g = k * 64 + lane, jj = g >> 3, hb = (g >> 2) & 1;
@@ -815,24 +858,24 @@ __global__ void k_zero_words_long(int32_t *w, long n) {
 // unit's up sums and h slice.
 size_t scratch_bytes(int NB) {
   const size_t route = (size_t)kMaxRows * kKeyRow * 16 + (size_t)kMaxRows * MOE_MAX_EXPERTS * 4 + (size_t)kMaxPicks * 8;
-  const size_t up = ((size_t)kMaxRows * kThreads + (size_t)4 * NB * kMaxRows * 16 + (size_t)kMaxRows * kSlice) * 4;
+  const size_t up = ((size_t)up_part_floats(NB) + (size_t)4 * NB * kMaxRows * 16 + (size_t)kMaxRows * kSlice) * 4;
   return std::max(route, up);
 }
 
-template <int NB, int NR, bool XF, int CU, int DP>
+template <int NB, int NR, bool XF, int CU, int DP, bool CF>
 hipError_t launch_one(StepArgs &a, size_t lds, hipStream_t stream) {
   static int occ = -1;  // same code object on every device
   static size_t occ_lds = 0, static_lds = 0;
   if (occ < 0) {
     hipFuncAttributes attr;
-    if (hipFuncGetAttributes(&attr, (const void *)k_decode_step<NB, NR, XF, CU, DP>) != hipSuccess)
+    if (hipFuncGetAttributes(&attr, (const void *)k_decode_step<NB, NR, XF, CU, DP, CF>) != hipSuccess)
       return hipErrorInvalidValue;
     static_lds = attr.sharedSizeBytes;
   }
   if (lds + static_lds > (size_t)kLdsLimit) return hipErrorNotSupported;
   if (occ < 0 || occ_lds != lds) {
     int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, k_decode_step<NB, NR, XF, CU, DP>, kThreads, lds) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, k_decode_step<NB, NR, XF, CU, DP, CF>, kThreads, lds) !=
         hipSuccess)
       return hipErrorInvalidValue;
     occ = o;
@@ -844,21 +887,30 @@ hipError_t launch_one(StepArgs &a, size_t lds, hipStream_t stream) {
     return hipErrorInvalidValue;
   // every workgroup must be resident at once
   if ((long)occ * cus < a.grid) return hipErrorNotSupported;
-  hipLaunchKernelGGL((k_decode_step<NB, NR, XF, CU, DP>), dim3(a.grid), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL((k_decode_step<NB, NR, XF, CU, DP, CF>), dim3(a.grid), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 
 // Register tiles by d_model class: up chunk iterations CU = ceil(d / 1024),
 // down block-pair iterations DP = 4 CU (8 wavefronts); fp32 x for d_model <=
 // 1024 only (its x tiles take twice the registers).
+template <int NB, int NR, bool XF, int CU, int DP>
+hipError_t launch_cf(StepArgs &a, size_t lds, hipStream_t stream) {
+  // SwiGLU units whose up chunks fill the wavefronts' rounds exactly (dch = 8 CU)
+  // take their up pieces chunk-fastest
+  if constexpr (NB == 2)
+    if (a.dch == 8 * CU) return launch_one<NB, NR, XF, CU, DP, true>(a, lds, stream);
+  return launch_one<NB, NR, XF, CU, DP, false>(a, lds, stream);
+}
+
 template <int NB, int NR>
 hipError_t launch_class(StepArgs &a, size_t lds, hipStream_t stream) {
   const int cls = (a.lp.d + 1023) / 1024;
-  if (a.lp.x_f32) return cls <= 1 ? launch_one<NB, NR, true, 1, 4>(a, lds, stream) : hipErrorNotSupported;
-  if (cls <= 1) return launch_one<NB, NR, false, 1, 4>(a, lds, stream);
-  if (cls <= 2) return launch_one<NB, NR, false, 2, 8>(a, lds, stream);
+  if (a.lp.x_f32) return cls <= 1 ? launch_cf<NB, NR, true, 1, 4>(a, lds, stream) : hipErrorNotSupported;
+  if (cls <= 1) return launch_cf<NB, NR, false, 1, 4>(a, lds, stream);
+  if (cls <= 2) return launch_cf<NB, NR, false, 2, 8>(a, lds, stream);
   if constexpr (NB == 1) {
-    if (cls <= 3) return launch_one<NB, NR, false, 3, 12>(a, lds, stream);
+    if (cls <= 3) return launch_cf<NB, NR, false, 3, 12>(a, lds, stream);
   }
   return hipErrorNotSupported;
 }

@@ -678,6 +678,11 @@ SINGLE_LAUNCH_CASES = [
     ("gated2", dict(n=1, seed=17), True),
     ("tiny16", dict(n=2, act="swiglu", fs=0, seed=19), True),
     ("tiny16", dict(n=1, act="swiglu", fs=0, d=160, f=96, seed=20), True),
+    # gated units whose up pieces go chunk-fastest (d_model a multiple of 1024
+    # or just under): shared experts and a half-filled last unit; fp32 x with a
+    # ragged last chunk
+    ("gated2", dict(n=2, E=8, K=4, f=992, seed=21), True),
+    ("tiny16", dict(n=2, act="swiglu", fs=0, d=960, f=96, seed=22), True),
     ("decode1", dict(n=7, E=32, fs=0, seed=18), False),
 ]
 
