@@ -146,10 +146,12 @@ __global__ void __launch_bounds__(64 * WAVES) k_dq_gemv(GemvBatch batch) {
   }
 
   const int nl = lane & 15, q = lane >> 4;
+  // The wavefronts take the k-groups round-robin, an iteration (kNI chunks of
+  // 4 groups) each, so that the WAVES wavefronts' loads of a round cover
+  // adjacent chunks of each 16-row block: with a contiguous quarter of k per
+  // wavefront, a round read 4 x CT separate runs of the weights.
   const int G = p.k >> 5;
-  const int gpw = (G + WAVES - 1) / WAVES;
-  const int gb = wave * gpw;
-  const int ge = min(G, gb + gpw);
+  constexpr int kIt = 4 * kNI;  // k-groups of one iteration
 
   const size_t crow = (size_t)(p.k >> 1), srow = (size_t)(p.k >> 4);
   // this lane's weight row of tile ct: column (tile0 + ct) * 16 + nl (clamped)
@@ -182,13 +184,13 @@ __global__ void __launch_bounds__(64 * WAVES) k_dq_gemv(GemvBatch batch) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) acc[ct][mt][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int g0 = gb; g0 < ge; g0 += 4 * kNI) {
+  for (int g0 = wave * kIt; g0 < G; g0 += WAVES * kIt) {
     u32x4_t wq[CT][NB][kNI];
     uint32_t sc[CT][NB][kNI];
 #pragma unroll
     for (int i = 0; i < kNI; ++i) {
       const int g = g0 + 4 * i + q;
-      const int gc = min(g, ge - 1);
+      const int gc = min(g, G - 1);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -198,18 +200,18 @@ __global__ void __launch_bounds__(64 * WAVES) k_dq_gemv(GemvBatch batch) {
             const size_t bc = slot >> 4, rr = slot & 15, hf = (gc >> 1) & 1, qt = gc & 1;
             wq[ct][b][i] = *(const u32x4_t *)(p.codes_packed + bc * 1024 + hf * 512 + rr * 32 + qt * 16);
             const uint32_t s2 = *(const uint16_t *)(p.scales_packed + bc * 128 + hf * 64 + rr * 4 + qt * 2);
-            sc[ct][b][i] = (g < ge) ? s2 : 0u;  // a zero scale neutralises a clamped group
+            sc[ct][b][i] = (g < G) ? s2 : 0u;  // a zero scale neutralises a clamped group
             continue;
           }
           wq[ct][b][i] = *(const u32x4_t *)(wrow_of(ct, b, p.codes, crow) + (size_t)gc * 16);
           const uint32_t s2 = *(const uint16_t *)(wrow_of(ct, b, p.scales, srow) + (size_t)gc * 2);
-          sc[ct][b][i] = (g < ge) ? s2 : 0u;  // a zero scale neutralises a clamped group
+          sc[ct][b][i] = (g < G) ? s2 : 0u;  // a zero scale neutralises a clamped group
         }
     }
 #pragma unroll
     for (int i = 0; i < kNI; ++i) {
-      if (g0 + 4 * i >= ge) break;  // uniform: no group of this iteration is in range
-      const int gc = min(g0 + 4 * i + q, ge - 1);
+      if (g0 + 4 * i >= G) break;  // uniform: no group of this iteration is in range
+      const int gc = min(g0 + 4 * i + q, G - 1);
       u32x4_t a[MT][NT][4];  // loaded once, used for every tile
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
