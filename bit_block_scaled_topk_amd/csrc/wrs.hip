@@ -12,7 +12,10 @@ namespace moe {
 
 namespace {
 
-template <bool ACCUM>
+// KM > 0 (top_k <= KM): the K row indices and weights are loaded first, then
+// all K rows, before the sums, so a thread waits for two round trips instead
+// of two per row; the sums run in the same j order either way.
+template <bool ACCUM, int KM>
 __global__ void __launch_bounds__(256)
 k_wrs_vec4(float *__restrict__ dst, const float *__restrict__ src, int n_src,
            const int32_t *__restrict__ rows, const float *__restrict__ w, int n, int K, int d4, int32_t *err) {
@@ -21,18 +24,45 @@ k_wrs_vec4(float *__restrict__ dst, const float *__restrict__ src, int n_src,
   int i = (int)(idx / d4);
   int c4 = (int)(idx - (long)i * d4);
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < K; ++j) {
-    int r = rows[(size_t)i * K + j];
-    float wt = w[(size_t)i * K + j];
-    if (r < 0 || r >= n_src) {
-      if (err && c4 == 0) atomicOr(err, MOE_DEVERR_ROW);
-      continue;
+  if constexpr (KM > 0) {
+    int r[KM];
+    float wt[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < K) {
+        r[j] = rows[(size_t)i * K + j];
+        wt[j] = w[(size_t)i * K + j];
+      }
+    f32x4_t sv[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < K && r[j] >= 0 && r[j] < n_src) sv[j] = ((const f32x4_t *)src)[(size_t)r[j] * d4 + c4];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (j >= K) break;
+      if (r[j] < 0 || r[j] >= n_src) {
+        if (err && c4 == 0) atomicOr(err, MOE_DEVERR_ROW);
+        continue;
+      }
+      acc.x = fmaf(wt[j], sv[j].x, acc.x);
+      acc.y = fmaf(wt[j], sv[j].y, acc.y);
+      acc.z = fmaf(wt[j], sv[j].z, acc.z);
+      acc.w = fmaf(wt[j], sv[j].w, acc.w);
     }
-    f32x4_t s = ((const f32x4_t *)src)[(size_t)r * d4 + c4];
-    acc.x = fmaf(wt, s.x, acc.x);
-    acc.y = fmaf(wt, s.y, acc.y);
-    acc.z = fmaf(wt, s.z, acc.z);
-    acc.w = fmaf(wt, s.w, acc.w);
+  } else {
+    for (int j = 0; j < K; ++j) {
+      int r = rows[(size_t)i * K + j];
+      float wt = w[(size_t)i * K + j];
+      if (r < 0 || r >= n_src) {
+        if (err && c4 == 0) atomicOr(err, MOE_DEVERR_ROW);
+        continue;
+      }
+      f32x4_t s = ((const f32x4_t *)src)[(size_t)r * d4 + c4];
+      acc.x = fmaf(wt, s.x, acc.x);
+      acc.y = fmaf(wt, s.y, acc.y);
+      acc.z = fmaf(wt, s.z, acc.z);
+      acc.w = fmaf(wt, s.w, acc.w);
+    }
   }
   if (ACCUM) {
     f32x4_t o = ((f32x4_t *)dst)[idx];
@@ -78,11 +108,18 @@ hipError_t launch_weighted_row_sum(float *dst, const float *src, int n_src_rows,
   long elems = (long)n_tokens * (vec ? d_model / 4 : d_model);
   long blocks = (elems + 255) / 256;
   dim3 grid((unsigned)blocks), block(256);
-  if (vec && accumulate)
-    hipLaunchKernelGGL(k_wrs_vec4<true>, grid, block, 0, stream, dst, src, n_src_rows, rows, weights, n_tokens,
+  const bool few = top_k <= 8;
+  if (vec && accumulate && few)
+    hipLaunchKernelGGL((k_wrs_vec4<true, 8>), grid, block, 0, stream, dst, src, n_src_rows, rows, weights, n_tokens,
+                       top_k, d_model / 4, error_word);
+  else if (vec && accumulate)
+    hipLaunchKernelGGL((k_wrs_vec4<true, 0>), grid, block, 0, stream, dst, src, n_src_rows, rows, weights, n_tokens,
+                       top_k, d_model / 4, error_word);
+  else if (vec && few)
+    hipLaunchKernelGGL((k_wrs_vec4<false, 8>), grid, block, 0, stream, dst, src, n_src_rows, rows, weights, n_tokens,
                        top_k, d_model / 4, error_word);
   else if (vec)
-    hipLaunchKernelGGL(k_wrs_vec4<false>, grid, block, 0, stream, dst, src, n_src_rows, rows, weights, n_tokens,
+    hipLaunchKernelGGL((k_wrs_vec4<false, 0>), grid, block, 0, stream, dst, src, n_src_rows, rows, weights, n_tokens,
                        top_k, d_model / 4, error_word);
   else if (accumulate)
     hipLaunchKernelGGL(k_wrs_scalar<true>, grid, block, 0, stream, dst, src, n_src_rows, rows, weights,
