@@ -27,6 +27,7 @@ constexpr int kSmallPicks = 2048;
 constexpr long kSmallCopyBytes = 1L << 21;
 constexpr int kChunkTokens = 256;  // tokens per chunk on the multi-workgroup path
 constexpr int kChunkWords = kChunkTokens / 32;
+constexpr int kIdBatch = 8;        // picks per thread loaded together on the multi-workgroup path
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
@@ -268,13 +269,26 @@ k_gather_bits(const int32_t *__restrict__ ids, int n, int K, int E, int W, uint3
   const int t1 = min(n, t0 + kChunkTokens);
   for (int i = tid; i < E * kChunkWords; i += blockDim.x) s_bits[i] = 0u;
   __syncthreads();
-  for (long p = (long)t0 * K + tid; p < (long)t1 * K; p += blockDim.x) {
-    int e = ids[p];
-    int t = (int)(p / K) - t0;
-    if (e >= 0 && e < E)
-      atomicOr(&s_bits[e * kChunkWords + (t >> 5)], 1u << (t & 31));
-    else if (err)
-      atomicOr(err, MOE_DEVERR_EXPERT_ID);
+  // the chunk's picks, kIdBatch per thread loaded before any is used (these
+  // workgroups are few, one per 256 tokens: each serial round trip shows)
+  const long p_end = (long)t1 * K;
+  for (long p0 = (long)t0 * K + tid; p0 < p_end; p0 += (long)kIdBatch * blockDim.x) {
+    int ev[kIdBatch];
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) {
+      const long p = p0 + (long)u * blockDim.x;
+      ev[u] = p < p_end ? ids[p] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) {
+      const long p = p0 + (long)u * blockDim.x;
+      if (p >= p_end) break;
+      const int e = ev[u], t = (int)(p / K) - t0;
+      if (e >= 0 && e < E)
+        atomicOr(&s_bits[e * kChunkWords + (t >> 5)], 1u << (t & 31));
+      else if (err)
+        atomicOr(err, MOE_DEVERR_EXPERT_ID);
+    }
   }
   __syncthreads();
   const int w0 = c * kChunkWords;
@@ -307,6 +321,9 @@ k_gather_place(const int32_t *__restrict__ ids, int n, int K, int E, int W,
   for (int e = tid; e < E; e += blockDim.x) {
     const int32_t *row = chunk_count + (size_t)e * n_chunks;
     int pre = 0, tot = 0;
+    // unrolled, so that the count loads go out in batches (these workgroups
+    // are few, one per 256 tokens: each serial round trip shows)
+#pragma unroll 8
     for (int cc = 0; cc < n_chunks; ++cc) {
       int v = row[cc];
       tot += v;
@@ -343,20 +360,31 @@ k_gather_place(const int32_t *__restrict__ ids, int n, int K, int E, int W,
   }
   if (c == 0 && tid == 0) offsets[E] = run;
   __syncthreads();
-  for (long p = (long)t0 * K + tid; p < (long)t1 * K; p += blockDim.x) {
-    int e = ids[p];
-    int t = (int)(p / K);
-    int32_t r = -1;
-    if (e >= 0 && e < E) {
-      int tl = t - t0;
-      int wl = tl >> 5;
-      int below = 0;
-      for (int ww = 0; ww < wl; ++ww) below += __popc(s_bits[e * kChunkWords + ww]);
-      below += __popc(s_bits[e * kChunkWords + wl] & ((1u << (tl & 31)) - 1u));
-      r = s_base[e] + below;
-      row_token[r] = t;
+  const long p_end = (long)t1 * K;
+  for (long p0 = (long)t0 * K + tid; p0 < p_end; p0 += (long)kIdBatch * blockDim.x) {
+    int ev[kIdBatch];
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) {
+      const long p = p0 + (long)u * blockDim.x;
+      ev[u] = p < p_end ? ids[p] : 0;
     }
-    rows[p] = r;
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) {
+      const long p = p0 + (long)u * blockDim.x;
+      if (p >= p_end) break;
+      const int e = ev[u], t = (int)(p / K);
+      int32_t r = -1;
+      if (e >= 0 && e < E) {
+        int tl = t - t0;
+        int wl = tl >> 5;
+        int below = 0;
+        for (int ww = 0; ww < wl; ++ww) below += __popc(s_bits[e * kChunkWords + ww]);
+        below += __popc(s_bits[e * kChunkWords + wl] & ((1u << (tl & 31)) - 1u));
+        r = s_base[e] + below;
+        row_token[r] = t;
+      }
+      rows[p] = r;
+    }
   }
   // rows past the valid picks (only when ids were dropped)
   const long picks = (long)n * K;
