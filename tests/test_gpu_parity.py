@@ -236,15 +236,17 @@ def _wrs_bound(dst, src, rows, w):
     return (K + 1) * 2.0 ** -24 * mag
 
 
+@pytest.mark.parametrize("K", [6, 12])
 @pytest.mark.parametrize("d", [100, 33])
-def test_weighted_row_sum(ops, d):
+def test_weighted_row_sum(ops, d, K):
     """Bit for bit equal to the oracle's binary32 WeightedRowSum (a fixed-order
     fmaf chain over j, then one add onto dst), with repeated source rows and a
     pre-filled dst; within the rigorous bound of the exact sum; deterministic.
-    d = 100 takes the 16-byte kernel, d = 33 the element kernel.  Row 1 is the
-    case where an unfused multiply-add or the other j order gives other bits."""
-    rng = np.random.default_rng(d)
-    n, K, ns = 37, 6, 50
+    d = 100 takes the 16-byte kernel (K = 6 its all-rows-first form, K = 12 the
+    per-row loop), d = 33 the element kernel.  Row 1 is the case where an
+    unfused multiply-add or the other j order gives other bits."""
+    rng = np.random.default_rng(d + K)
+    n, ns = 37, 50
     src = rng.standard_normal((ns, d)).astype(np.float32)
     rows = rng.integers(0, ns, size=(n, K)).astype(np.int32)
     rows[0] = rows[0, 0]                       # repeated source rows
