@@ -790,6 +790,10 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
           break;
         }
         __builtin_amdgcn_s_sleep(2);
+        // a compiler barrier: nothing in this loop writes memory, so without
+        // one the repeated loads of the same addresses may be merged with the
+        // first ones, and the loop would test the same stale values
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int i = 0; i < kSumGroup; ++i)
           v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(pr, off[i], 0, kSc1));
