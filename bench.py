@@ -50,6 +50,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 N_COPIES = 16
+SETTLE_STEPS = 20  # untimed steps before the warmup steps (see bench_main)
 METRIC = "MoE-layer tokens/s; decode HBM GB/s & prefill TFLOPS as % of MI355X peak"
 
 
@@ -232,9 +233,13 @@ def bench_main(args, ops, synth):
     stream = torch.cuda.Stream()
     E8 = ops.PROFILE_EVENTS
     torch.cuda.synchronize()
-    log(f"{inp.name}: inputs in {gen_s:.1f} s; warmup {args.warmup} steps")
+    # Settle steps before the warmup: after the set-up the GPU's first
+    # launches run slow (the prefill GEMM launches take up to 40 % longer over
+    # the first ~15 steps, as the clocks come up), so that few warmup steps
+    # would leave part of that ramp inside the timed region.
+    log(f"{inp.name}: inputs in {gen_s:.1f} s; {SETTLE_STEPS} settle + {args.warmup} warmup steps")
     with torch.cuda.stream(stream):
-        for _ in range(max(1, args.warmup)):
+        for _ in range(SETTLE_STEPS + max(1, args.warmup)):
             layer.forward_fused(x, logits, stream=stream, check=False)
     torch.cuda.synchronize()
 
@@ -459,6 +464,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "settle_steps": SETTLE_STEPS,
         "ms_per_step": round(elapsed / K * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
