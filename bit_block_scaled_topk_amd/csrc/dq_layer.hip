@@ -86,7 +86,7 @@ constexpr int up_part_floats(int NB) {
 }
 constexpr int kSumGroup = 8;           // slices one reducer thread adds
 constexpr int kRedCols = 16;           // output columns one reducer block combines
-constexpr int kWin = 8;                // weight loads in flight per wavefront
+constexpr int kWin = 6;                // weight loads in flight per wavefront
 constexpr int kKeyRow = 2 * MOE_MAX_EXPERTS;  // routing keys of one token, padded
 // LDS of a wavefront's scale copies, in whole 1 KB buffer-to-LDS loads (every
 // lane writes its 16 bytes, zeros past the data): the up scales of one block,
