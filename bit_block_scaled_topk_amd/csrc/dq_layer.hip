@@ -671,9 +671,10 @@ __global__ void __launch_bounds__(kThreads) k_decode_step(StepArgs a) {
   Piece ring[kWin];
   auto start_unit = [&](const UnitRef &u, UnitSrc &q) {
     q = unit_src(u);
-    // this wavefront's scales, into its LDS region: the up tile's block for
-    // every chunk (dch x 128 contiguous bytes), then its block pairs' down
-    // scales (the unit's 64-wide half of one chunk: 64 bytes per block)
+    // this wavefront's scales, into its LDS region: the up scales its pieces
+    // read (CF: the block-chunk of each piece; else its tile's block for every
+    // chunk, dch x 128 contiguous bytes), then its block pairs' down scales
+    // (the unit's 64-wide half of one chunk: 64 bytes per block)
     if constexpr (CF) {  // the block-chunk (128 bytes) of each of its SU = 8 CU pieces: CU x 1 KB
 #pragma unroll
       for (int k = 0; k < CU; ++k) {
