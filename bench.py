@@ -431,8 +431,8 @@ def bench_router(ops, synth, reps=10, per_graph=20):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1 (the sharded "
-                                   "design is described in DESIGN.md, not built)"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1 (sharding the "
+                                   "layer across GPUs is not built)"}))
         sys.exit(2)
     if args.copy_probe_mb > 0:
         copy_probe(args.copy_probe_mb)
