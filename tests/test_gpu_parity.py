@@ -869,7 +869,9 @@ def _router_case(ops, x, x_dtype, wr, K, min_separated=0.5):
     assert np.array_equal(host(ids2), host(ids)) and np.array_equal(host(w2), host(w))
     oid, ow, _ = oracle.router_topk(x, x_dtype, wr, K)
     srt = -np.sort(-exact, axis=1)[:, :min(K + 1, E)]
-    gaps = -np.diff(srt, axis=1).min(axis=1) if srt.shape[1] > 1 else np.full(n, np.inf)
+    # the smallest gap between neighbours of the exact top K + 1 (the minus sign
+    # goes on the differences, before the min)
+    gaps = (-np.diff(srt, axis=1)).min(axis=1) if srt.shape[1] > 1 else np.full(n, np.inf)
     sep = gaps > 2 * bound.max(axis=1)
     assert sep.mean() >= min_separated, f"only {sep.mean():.2f} of the tokens are separated"
     assert np.array_equal(host(ids)[sep], oid[sep])
@@ -892,7 +894,9 @@ def test_router_topk_workloads(ops, name):
 def test_router_topk_edge_cases(ops):
     """Ragged token tiles and expert groups (37 tokens, 77 experts), the largest
     E and K (1024, 32), one expert, ties (a zero router: experts 0..K-1 with
-    weight 1/K), a long fp32 row, and no tokens."""
+    weight 1/K), a long fp32 row, each workgroup shape of the large batches
+    (16 and 32 tokens, routed in place or through the counters), and no
+    tokens."""
     rng = np.random.default_rng(95)
 
     def bf(a):
@@ -906,13 +910,23 @@ def test_router_topk_edge_cases(ops):
     ids, _ = _router_case(ops, x, "bf16", np.zeros((12, 64), dtype=np.uint16), 4, min_separated=0.0)
     assert np.array_equal(ids, np.tile(np.arange(4, dtype=np.int32), (9, 1)))
     xf = rng.standard_normal((20, 4096)).astype(np.float32)
-    _router_case(ops, xf, "f32", bf(rng.standard_normal((64, 4096)) * 0.02), 6)
+    # at d = 4096 the worst-case accumulation bound (about 0.013 here) is a fair
+    # part of the gaps between neighbouring logits: fewer rows are separated
+    _router_case(ops, xf, "f32", bf(rng.standard_normal((64, 4096)) * 0.02), 6, min_separated=0.3)
     # many token tiles: 128-expert groups per workgroup, routed in place (up to
     # 128 experts, bf16 and fp32 x) or through the counters (256 experts)
-    _router_case(ops, bf(rng.standard_normal((600, 256))), "bf16", bf(rng.standard_normal((128, 256)) * 0.06), 6)
+    _router_case(ops, bf(rng.standard_normal((1500, 256))), "bf16", bf(rng.standard_normal((128, 256)) * 0.06), 6)
     _router_case(ops, bf(rng.standard_normal((700, 128))), "bf16", bf(rng.standard_normal((256, 128)) * 0.09), 8)
     xf = rng.standard_normal((2100, 96)).astype(np.float32)
     _router_case(ops, xf, "f32", bf(rng.standard_normal((64, 96)) * 0.1), 4)
+    # more 16-token tiles (times expert groups) than a 256-CU device has CUs:
+    # 32-token workgroups, ragged in tokens and experts, routed in place or
+    # through the counters (200 experts: two groups)
+    _router_case(ops, bf(rng.standard_normal((4130, 64))), "bf16", bf(rng.standard_normal((96, 64)) * 0.12), 6)
+    _router_case(ops, bf(rng.standard_normal((2100, 64))), "bf16", bf(rng.standard_normal((200, 64)) * 0.12), 7)
+    xf = rng.standard_normal((4130, 64)).astype(np.float32)
+    _router_case(ops, xf, "f32", bf(rng.standard_normal((96, 64)) * 0.12), 6)
+    _router_case(ops, xf[:2100], "f32", bf(rng.standard_normal((200, 64)) * 0.12), 7)
     ws = router_ws(ops, 0, 8)
     ids, w, _ = ops.moe_router_topk(torch.empty((0, 64), dtype=torch.int16, device=DEV),
                                     dev(np.zeros((8, 64), dtype=np.uint16)), 2, ws)
