@@ -685,6 +685,9 @@ SINGLE_LAUNCH_CASES = [
     # ragged last chunk
     ("gated2", dict(n=2, E=8, K=4, f=992, seed=21), True),
     ("tiny16", dict(n=2, act="swiglu", fs=0, d=960, f=96, seed=22), True),
+    # more than 128 experts (two ranking passes), and more than 8 picks
+    ("tiny16", dict(n=2, E=200, K=6, seed=23), True),
+    ("tiny16", dict(n=1, E=48, K=12, seed=24), True),
     ("decode1", dict(n=7, E=32, fs=0, seed=18), False),
 ]
 
