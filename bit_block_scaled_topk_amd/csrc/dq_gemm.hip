@@ -357,10 +357,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     // block's word); sched_barriers keep that order, so LDS latency and the
     // decode hide under the MFMAs.
     u32x4_t bw[4], bn[4], af[3];
-    // f32 outputs: a wavefront computing a chunk issues ahead of the CU's
-    // others (loading, at the barrier, storing); measured 3-5 % faster for
-    // these launches and slower for the others, which keep the default
-    if constexpr (EPI == EPI_F32) __builtin_amdgcn_s_setprio(1);
+    // A wavefront computing a chunk issues ahead of the CU's others (at the
+    // barrier, issuing requests).  It keeps that priority through its tile's
+    // end: the f32 outputs are stored inside the last chunk's loop; the bf16
+    // outputs after it, which at the default priority lost to the other
+    // workgroup's MFMAs (measured: down 3.5-5.5 %, up 2.5 % faster)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) bw[j] = dq8_bf16(cc[j][0], s0[j]);
     af[0] = *(const u32x4_t *)(cur + fa[0]);
@@ -387,7 +389,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         if (st == 3 && i > 0) store_frag(i - 1, gs);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (EPI == EPI_F32) __builtin_amdgcn_s_setprio(0);
+    if constexpr (EPI == EPI_F32 || !LAST) __builtin_amdgcn_s_setprio(0);
     if constexpr (LAST) store_frag(7, gs);
   };
 
